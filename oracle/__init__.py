@@ -1,0 +1,29 @@
+"""CPU oracle for the int4 group-quantized MoE SwitchGLU layer — TEST INFRASTRUCTURE ONLY.
+
+This package is the plain, slow, obviously-correct reference that the HIP path is checked
+against.  Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+it; the product path (the C-ABI library and its Python binding) never does, and the two
+share no code: no kernels, headers, helpers, tables or constant generators.  The only
+thing both sides use is the seeded input generator module ``synth``, which holds no
+arithmetic of the method.
+
+Precision policy
+----------------
+* Matmuls, LoRA deltas, activations and routing weights are evaluated in float64 from the
+  exact dequantized weights (``scale * q + bias`` is exact in float64 for fp16 scale/bias
+  and integer codes), so the oracle is the definition of the layer up to float64 rounding.
+* Where a floating-point value *decides an integer* (a quantized code, a scale that later
+  decides codes), the oracle takes that decision in float32, the precision of the kernel,
+  with every operation spelled out in IEEE float32 (numpy float32 arrays, no contraction).
+* Outputs that the method stores in fp16 are rounded once, round-to-nearest-even.
+
+Modules
+-------
+``affine``      group-wise affine quantize / pack / unpack / dequantize (4- and 8-bit).
+``moe``         quantized linear, LoRA delta, router + top-K, experts, shared expert, layer,
+                layer stack.
+``supergroup``  mixed ternary / 4-bit super-group quantizer, packing and weight-only GEMM.
+
+Functions with no independent pin are marked "parity unpinned" in their docstrings.
+"""
+from . import affine, moe, supergroup  # noqa: F401

@@ -1,0 +1,102 @@
+"""Pins for the oracle's mixed ternary / 4-bit super-group quantizer and GEMM (CPU only)."""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import supergroup as sg
+
+W = synth.Workload.TEST
+
+
+def test_channel_allocation_one_four_bit_per_block():
+    """rho = 1/4: in every block of 4 consecutive channels exactly one (the first) is 4-bit;
+    period 1 is the all-4-bit limit (rho = 1)."""
+    flags = [sg.is_four_bit(n, 4) for n in range(64)]
+    for b in range(16):
+        assert flags[4 * b:4 * b + 4] == [True, False, False, False]
+    assert all(sg.is_four_bit(n, 1) for n in range(17))
+
+
+def test_hand_example_scales_and_codes():
+    """Worked by hand from the quantizer formulas of the EdgeRazor page (section 2.1):
+    4-bit channel [0.7, -0.35, 0.05, 0, ...]: s = max|w|/7 = 0.1 -> fp16 0.0999755859375,
+    codes rint(w/s) = [7, -4 (-3.5009 rounds to -4), 1 (0.50012 rounds to 1), 0 ...].
+    Ternary channel with |w| summing to 1.6 over 16 inputs: mean 0.1, s = 0.2 ->
+    fp16 0.199951171875; w = 0.1 -> 0.50012 -> 1; w = -0.09 -> -0.45 -> 0; 0.6 -> 3 -> 1."""
+    w4 = np.zeros(16, np.float32)
+    w4[:3] = [0.7, -0.35, 0.05]
+    q4, s4 = sg.quantize_channel(w4, True)
+    assert float(s4) == 0.0999755859375
+    assert q4[:4].tolist() == [7, -4, 1, 0]
+    wt = np.zeros(16, np.float32)
+    wt[:4] = [0.1, -0.09, 0.6, -0.81]
+    assert abs(np.abs(wt.astype(np.float64)).sum() - 1.6) < 1e-7
+    qt, st = sg.quantize_channel(wt, False)
+    assert float(st) == 0.199951171875
+    assert qt[:4].tolist() == [1, 0, 1, -1]
+
+
+def test_epsilon_floor():
+    q, s = sg.quantize_channel(np.zeros(32, np.float32), False)
+    assert float(s) == float(np.float16(1e-5)) and np.all(q == 0)
+    q, s = sg.quantize_channel(np.full(32, 1e-7, np.float32), True)
+    assert float(s) == float(np.float16(1e-5)) and np.all(q == 0)
+
+
+@pytest.mark.parametrize("four_bit", [True, False])
+def test_codes_are_nearest_clipped_level_brute_force(four_bit):
+    qmax = 7 if four_bit else 1
+    g = np.random.default_rng(9)
+    for trial in range(40):
+        w = (g.standard_normal(256) * 0.02).astype(np.float32)
+        q, s = sg.quantize_channel(w, four_bit)
+        S = Fraction(float(s))
+        for i in range(256):
+            Wv = Fraction(float(w[i]))
+            dist = [abs(Wv - S * k) for k in range(-qmax, qmax + 1)]
+            best = min(dist)
+            cands = [k - qmax for k in range(2 * qmax + 1) if dist[k] == best]
+            if int(q[i]) not in cands:
+                frac = abs(Wv / S) - int(abs(Wv / S))
+                assert abs(float(frac) - 0.5) < 1e-5
+
+
+def test_pack_round_trip_and_layout():
+    w = synth.normal_f32((64, 128), 0.02, W, 0, synth.Role.SUPERGROUP)
+    Wq, codes = sg.quantize(w, 4)
+    assert Wq.p4.shape == (16, 16) and Wq.p2.shape == (48, 8)
+    assert np.array_equal(sg.codes_of(Wq), codes)
+    # channel 0 is the first 4-bit row; channel 1 the first ternary row
+    assert (int(Wq.p4[0, 0]) & 0xF) == int(codes[0, 0]) + 8
+    assert (int(Wq.p2[0, 0]) & 0x3) == int(codes[1, 0]) + 1
+    assert ((int(Wq.p2[0, 0]) >> 2) & 0x3) == int(codes[1, 1]) + 1
+    assert (int(Wq.p2[1, 0]) & 0x3) == int(codes[2, 0]) + 1
+
+
+def test_storage_of_the_benchmark_matrix():
+    """3072 x 1024 at rho = 1/4: 768 x 128 nibble words + 2304 x 64 two-bit words +
+    3072 fp16 scales = 989,184 bytes (about 2.19 bits per weight plus scales)."""
+    w = np.zeros((3072, 1024), np.float32)
+    Wq, _ = sg.quantize(w[:3072], 4)
+    assert Wq.p4.nbytes + Wq.p2.nbytes + Wq.scales.nbytes == 989184
+
+
+def test_gemm_factorization_equals_dequantized_matmul():
+    """s * sum(q x) (scale applied once per channel) equals sum((s q) x) on the dequantized
+    weights — the scale/integer decomposition of the EdgeRazor page."""
+    w = synth.normal_f32((32, 256), 0.02, W, 1, synth.Role.SUPERGROUP)
+    Wq, codes = sg.quantize(w, 4)
+    x = synth.activations(5, 256, W)
+    deq = codes.astype(np.float64) * Wq.scales.astype(np.float64)[:, None]
+    np.testing.assert_allclose(sg.gemm(x, Wq), x.astype(np.float64) @ deq.T, rtol=1e-12, atol=1e-15)
+
+
+def test_gemm_integer_case_exact():
+    w = synth.normal_f32((16, 64), 0.02, W, 2, synth.Role.SUPERGROUP)
+    Wq, codes = sg.quantize(w, 4)
+    Wq.scales[:] = np.float16(1.0)
+    x = np.random.default_rng(3).integers(-4, 5, size=(3, 64)).astype(np.float16)
+    ref = x.astype(np.int64) @ codes.astype(np.int64).T
+    assert np.array_equal(sg.gemm(x, Wq), ref.astype(np.float64))
