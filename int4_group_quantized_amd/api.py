@@ -1,0 +1,302 @@
+"""Python entry points of libqmoe (argument marshalling only).
+
+Every function takes torch tensors that already live on a ROCm device, checks dtype /
+shape / contiguity, passes raw device pointers to the C ABI of include/qmoe.h and enqueues
+on the current stream of the tensor's device.  All arithmetic happens in the HIP kernels;
+there is no CPU path.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+import torch
+
+from ._lib import LoraC, MoELayerC, QWeightC, check, lib
+
+
+def _stream(t: torch.Tensor) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dev(t: torch.Tensor, dtype: torch.dtype, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+# ------------------------------------------------------------------------------ data types
+
+@dataclass
+class QWeight:
+    """Group-affine quantized matrix (or expert stack) on the device.
+
+    packed int32 [n_experts*rows, cols*bits/32] (uint32 words), scales / biases fp16
+    [n_experts*rows, cols/group]."""
+
+    packed: torch.Tensor
+    scales: torch.Tensor
+    biases: torch.Tensor
+    bits: int
+    rows: int
+    cols: int
+    n_experts: int = 1
+    group: int = 64
+
+    def c(self) -> QWeightC:
+        return QWeightC(self.packed.data_ptr(), self.scales.data_ptr(), self.biases.data_ptr(),
+                        self.rows, self.cols, self.bits, self.group, self.n_experts)
+
+    @classmethod
+    def from_arrays(cls, packed: np.ndarray, scales: np.ndarray, biases: np.ndarray, bits: int,
+                    device="cuda") -> "QWeight":
+        """From host arrays (uint32 words, fp16 scales and biases), optionally stacked
+        along a leading expert axis."""
+        n_experts = packed.shape[0] if packed.ndim == 3 else 1
+        rows, cols = scales.shape[-2], scales.shape[-1] * 64
+        p = torch.from_numpy(np.ascontiguousarray(packed).view(np.int32).reshape(n_experts * rows, -1))
+        s = torch.from_numpy(np.ascontiguousarray(scales).reshape(n_experts * rows, -1))
+        b = torch.from_numpy(np.ascontiguousarray(biases).reshape(n_experts * rows, -1))
+        return cls(p.to(device), s.to(device), b.to(device), bits, rows, cols, n_experts)
+
+    def expert(self, e: int) -> "QWeight":
+        r = self.rows
+        return QWeight(self.packed[e * r:(e + 1) * r], self.scales[e * r:(e + 1) * r],
+                       self.biases[e * r:(e + 1) * r], self.bits, self.rows, self.cols, 1)
+
+
+@dataclass
+class Lora:
+    """LoRA adapter set(s): A fp16 [n_adapters, rank, in_dim], B fp16 [n_adapters, out_dim,
+    rank], scale = alpha / rank."""
+
+    A: torch.Tensor
+    B: torch.Tensor
+    scale: float
+
+    def c(self) -> LoraC:
+        n, r, i = self.A.shape
+        return LoraC(self.A.data_ptr(), self.B.data_ptr(), r, n, i, self.B.shape[1],
+                     float(self.scale))
+
+
+@dataclass
+class MoELayer:
+    hidden: int
+    inter: int
+    shared_inter: int
+    n_experts: int
+    top_k: int
+    router: QWeight
+    shared_gate: QWeight
+    exp_gate: QWeight
+    exp_up: QWeight
+    exp_down: QWeight
+    sh_gate: QWeight
+    sh_up: QWeight
+    sh_down: QWeight
+    lora_gate: Optional[Lora] = None
+    lora_up: Optional[Lora] = None
+    lora_down: Optional[Lora] = None
+    router_bias: Optional[torch.Tensor] = None
+    add_residual: bool = False
+    _keep: list = field(default_factory=list, repr=False)
+
+    def c(self) -> MoELayerC:
+        loras = []
+        for l in (self.lora_gate, self.lora_up, self.lora_down):
+            if l is None:
+                loras.append(ctypes.POINTER(LoraC)())
+            else:
+                lc = l.c()
+                self._keep.append(lc)
+                loras.append(ctypes.pointer(lc))
+        if self.router_bias is not None:
+            _dev(self.router_bias, torch.float32, "router_bias")
+        return MoELayerC(self.hidden, self.inter, self.shared_inter, self.n_experts, self.top_k,
+                         int(self.add_residual), self.router.c(), self.shared_gate.c(),
+                         self.exp_gate.c(), self.exp_up.c(), self.exp_down.c(), self.sh_gate.c(),
+                         self.sh_up.c(), self.sh_down.c(), loras[0], loras[1], loras[2],
+                         _ptr(self.router_bias))
+
+
+@dataclass
+class SuperGroupWeight:
+    p4: torch.Tensor       # int32 [rows/period, cols/8]
+    p2: torch.Tensor       # int32 [rows - rows/period, cols/16]
+    scales: torch.Tensor   # fp16 [rows]
+    period: int
+    rows: int
+    cols: int
+
+
+# ------------------------------------------------------------------------------ entry points
+
+def quantize_affine(w: torch.Tensor, bits: int = 4, group: int = 64) -> QWeight:
+    _dev(w, torch.float32, "w")
+    rows, cols = w.shape
+    packed = torch.empty((rows, cols * bits // 32), dtype=torch.int32, device=w.device)
+    scales = torch.empty((rows, cols // group), dtype=torch.float16, device=w.device)
+    biases = torch.empty_like(scales)
+    check(lib.qmoe_quantize_affine(w.data_ptr(), rows, cols, bits, group, packed.data_ptr(),
+                                   scales.data_ptr(), biases.data_ptr(), _stream(w)),
+          "qmoe_quantize_affine")
+    return QWeight(packed, scales, biases, bits, rows, cols)
+
+
+def unpack(qw: QWeight) -> torch.Tensor:
+    rows = qw.rows * qw.n_experts
+    q = torch.empty((rows, qw.cols), dtype=torch.uint8, device=qw.packed.device)
+    check(lib.qmoe_unpack(qw.packed.data_ptr(), rows, qw.cols, qw.bits, q.data_ptr(),
+                          _stream(q)), "qmoe_unpack")
+    return q
+
+
+def dequantize(qw: QWeight) -> torch.Tensor:
+    out = torch.empty((qw.rows * qw.n_experts, qw.cols), dtype=torch.float32,
+                      device=qw.packed.device)
+    c = qw.c()
+    check(lib.qmoe_dequantize(ctypes.byref(c), out.data_ptr(), _stream(out)), "qmoe_dequantize")
+    return out
+
+
+def qlinear_int4(x: torch.Tensor, qw: QWeight, lora: Optional[Lora] = None,
+                 adapter_idx: Optional[torch.Tensor] = None,
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    _dev(x, torch.float16, "x")
+    m = x.shape[0]
+    y = out if out is not None else torch.empty((m, qw.rows), dtype=torch.float16, device=x.device)
+    _dev(y, torch.float16, "out")
+    if adapter_idx is not None:
+        _dev(adapter_idx, torch.int32, "adapter_idx")
+    c = qw.c()
+    lc = lora.c() if lora is not None else None
+    check(lib.qlinear_int4(x.data_ptr(), m, ctypes.byref(c),
+                           ctypes.byref(lc) if lc is not None else None, _ptr(adapter_idx),
+                           y.data_ptr(), _stream(x)), "qlinear_int4")
+    return y
+
+
+def router_topk(logits: torch.Tensor, k: int, bias: Optional[torch.Tensor] = None):
+    _dev(logits, torch.float32, "logits")
+    t, e = logits.shape
+    if bias is not None:
+        _dev(bias, torch.float32, "bias")
+    idx = torch.empty((t, k), dtype=torch.int32, device=logits.device)
+    w = torch.empty((t, k), dtype=torch.float32, device=logits.device)
+    check(lib.router_topk(logits.data_ptr(), t, e, k, _ptr(bias), idx.data_ptr(), w.data_ptr(),
+                          _stream(logits)), "router_topk")
+    return idx, w
+
+
+def lora_apply(x: torch.Tensor, lora: Lora, y_acc: torch.Tensor,
+               adapter_idx: Optional[torch.Tensor] = None) -> torch.Tensor:
+    _dev(x, torch.float16, "x")
+    _dev(y_acc, torch.float32, "y_acc")
+    if adapter_idx is not None:
+        _dev(adapter_idx, torch.int32, "adapter_idx")
+    lc = lora.c()
+    check(lib.lora_apply(x.data_ptr(), x.shape[0], ctypes.byref(lc), _ptr(adapter_idx),
+                         y_acc.data_ptr(), _stream(x)), "lora_apply")
+    return y_acc
+
+
+def moe_workspace_bytes(layer: MoELayer, max_tokens: int) -> int:
+    c = layer.c()
+    n = lib.moe_switchglu_int4_workspace_bytes(ctypes.byref(c), max_tokens)
+    if n == 0:
+        raise ValueError("invalid layer description or token count")
+    return n
+
+
+def moe_workspace(layer: MoELayer, max_tokens: int, device="cuda") -> torch.Tensor:
+    """A workspace tensor for up to max_tokens tokens (uint8, 256-byte aligned)."""
+    return torch.empty(moe_workspace_bytes(layer, max_tokens), dtype=torch.uint8, device=device)
+
+
+def moe_switchglu_int4(layer: MoELayer, x: torch.Tensor,
+                       adapter_idx: Optional[torch.Tensor] = None,
+                       ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                       return_routing: bool = False):
+    _dev(x, torch.float16, "x")
+    t = x.shape[0]
+    if ws is None:
+        ws = moe_workspace(layer, t, x.device)
+    _dev(ws, torch.uint8, "ws")
+    y = out if out is not None else torch.empty_like(x)
+    _dev(y, torch.float16, "out")
+    if adapter_idx is not None:
+        _dev(adapter_idx, torch.int32, "adapter_idx")
+    idx = w = None
+    if return_routing:
+        idx = torch.empty((t, layer.top_k), dtype=torch.int32, device=x.device)
+        w = torch.empty((t, layer.top_k), dtype=torch.float32, device=x.device)
+    c = layer.c()
+    check(lib.moe_switchglu_int4(ctypes.byref(c), x.data_ptr(), t, _ptr(adapter_idx),
+                                 y.data_ptr(), _ptr(idx), _ptr(w), ws.data_ptr(), ws.numel(),
+                                 _stream(x)), "moe_switchglu_int4")
+    return (y, idx, w) if return_routing else y
+
+
+STAGE_ALL, STAGE_ROUTE, STAGE_GATE_UP, STAGE_DOWN = 0, 1, 2, 3
+
+
+class MoECall:
+    """A prepared moe_switchglu_int4 call: the C layer struct and every pointer are built
+    once, so repeated launches (a decode loop, graph capture) cost one C call each."""
+
+    def __init__(self, layer: MoELayer, x: torch.Tensor, y: torch.Tensor, ws: torch.Tensor,
+                 adapter_idx: Optional[torch.Tensor] = None,
+                 idx_out: Optional[torch.Tensor] = None, w_out: Optional[torch.Tensor] = None):
+        _dev(x, torch.float16, "x")
+        _dev(y, torch.float16, "y")
+        _dev(ws, torch.uint8, "ws")
+        self.layer, self.x, self.y, self.ws = layer, x, y, ws
+        self.adapter_idx, self.idx_out, self.w_out = adapter_idx, idx_out, w_out
+        self.c = layer.c()
+        self.t = x.shape[0]
+
+    def __call__(self, stage: int = STAGE_ALL, stream: Optional[int] = None) -> None:
+        s = ctypes.c_void_p(stream if stream is not None
+                            else torch.cuda.current_stream(self.x.device).cuda_stream)
+        check(lib.moe_switchglu_int4_stage(ctypes.byref(self.c), stage, self.x.data_ptr(), self.t,
+                                           _ptr(self.adapter_idx), self.y.data_ptr(),
+                                           _ptr(self.idx_out), _ptr(self.w_out),
+                                           self.ws.data_ptr(), self.ws.numel(), s),
+              "moe_switchglu_int4_stage")
+
+
+def quantize_supergroup(w: torch.Tensor, period: int = 4) -> SuperGroupWeight:
+    _dev(w, torch.float32, "w")
+    rows, cols = w.shape
+    n4 = rows // period
+    p4 = torch.empty((n4, cols // 8), dtype=torch.int32, device=w.device)
+    p2 = torch.empty((rows - n4, cols // 16), dtype=torch.int32, device=w.device)
+    scales = torch.empty(rows, dtype=torch.float16, device=w.device)
+    check(lib.qmoe_quantize_supergroup(w.data_ptr(), rows, cols, period, p4.data_ptr(),
+                                       p2.data_ptr() if p2.numel() else None, scales.data_ptr(),
+                                       _stream(w)), "qmoe_quantize_supergroup")
+    return SuperGroupWeight(p4, p2, scales, period, rows, cols)
+
+
+def qlinear_supergroup(x: torch.Tensor, W: SuperGroupWeight,
+                       out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    _dev(x, torch.float16, "x")
+    b = x.shape[0]
+    y = out if out is not None else torch.empty((b, W.rows), dtype=torch.float16, device=x.device)
+    _dev(y, torch.float16, "out")
+    check(lib.qlinear_supergroup(x.data_ptr(), b, W.p4.data_ptr(),
+                                 W.p2.data_ptr() if W.p2.numel() else None, W.scales.data_ptr(),
+                                 W.rows, W.cols, W.period, y.data_ptr(), _stream(x)),
+          "qlinear_supergroup")
+    return y

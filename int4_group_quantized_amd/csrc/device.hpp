@@ -1,0 +1,100 @@
+// Device-side helpers shared by the gfx950 kernels of libqmoe.
+//
+// Code unpacking uses exact fp16 construction: a 4-bit code q placed in the four top
+// mantissa bits of 1.0 gives the fp16 value 1 + q/16 exactly (8-bit: 1 + q/256).  A dot
+// product against x then yields sum(x) + sum(q x)/16, from which the affine group term
+// s*sum(q x) + b*sum(x) = 16 s * dot + (b - 16 s) * sum(x) follows with fp32 arithmetic.
+// Keeping the constant 1 (not 1024, as with the usual exponent trick) makes the constant
+// part of the dot the same size as the code part, so fp32 accumulation loses nothing.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmoe {
+
+typedef _Float16 f16;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float h2f(uint16_t b) { return (float)__builtin_bit_cast(f16, b); }
+// fp32 -> fp16, round to nearest even (v_cvt_f16_f32 in the default rounding mode)
+__device__ __forceinline__ uint16_t f2h(float v) { return __builtin_bit_cast(uint16_t, (f16)v); }
+
+__device__ __forceinline__ f16x2 as_h2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
+__device__ __forceinline__ uint32_t as_u32(f16x2 h) { return __builtin_bit_cast(uint32_t, h); }
+
+// 4-bit word w holds codes q0..q7 (q_j in bits [4j, 4j+4)).  Pair j in 0..3 returns the
+// fp16 pair (1 + q_j/16, 1 + q_{j+4}/16): nibble j moved to mantissa bits 6..9 of the low
+// half, nibble j+4 to bits 6..9 of the high half, exponent of 1.0 ORed in.
+template <int J>
+__device__ __forceinline__ uint32_t nib_pair(uint32_t w) {
+    uint32_t s;
+    if constexpr (J == 0) s = w << 6;
+    else if constexpr (J == 1) s = w << 2;
+    else if constexpr (J == 2) s = w >> 2;
+    else s = w >> 6;
+    return (s & 0x03C003C0u) | 0x3C003C00u;
+}
+
+// 8-bit word w holds codes b0..b3 (byte j).  Pair 0 = (1 + b0/256, 1 + b2/256),
+// pair 1 = (1 + b1/256, 1 + b3/256).
+template <int J>
+__device__ __forceinline__ uint32_t byte_pair(uint32_t w) {
+    uint32_t s = (J == 0) ? (w << 2) : (w >> 6);
+    return (s & 0x03FC03FCu) | 0x3C003C00u;
+}
+
+// Dot of one packed word against its x values, x given as the matching pairs.
+__device__ __forceinline__ float dot_word4(uint32_t w, const f16x2* xp, float acc) {
+    acc = __builtin_amdgcn_fdot2(as_h2(nib_pair<0>(w)), xp[0], acc, false);
+    acc = __builtin_amdgcn_fdot2(as_h2(nib_pair<1>(w)), xp[1], acc, false);
+    acc = __builtin_amdgcn_fdot2(as_h2(nib_pair<2>(w)), xp[2], acc, false);
+    acc = __builtin_amdgcn_fdot2(as_h2(nib_pair<3>(w)), xp[3], acc, false);
+    return acc;
+}
+__device__ __forceinline__ float dot_word8(uint32_t w, const f16x2* xp, float acc) {
+    acc = __builtin_amdgcn_fdot2(as_h2(byte_pair<0>(w)), xp[0], acc, false);
+    acc = __builtin_amdgcn_fdot2(as_h2(byte_pair<1>(w)), xp[1], acc, false);
+    return acc;
+}
+
+// The code scale 16 (4-bit) or 256 (8-bit) of the 1 + q/C construction.
+template <int BITS>
+__device__ __forceinline__ constexpr float code_div() { return BITS == 4 ? 16.0f : 256.0f; }
+
+// Permute 8 consecutive x values (x0..x7, one 4-bit word's worth) into the pair order of
+// nib_pair: (x0,x4) (x1,x5) (x2,x6) (x3,x7).
+__device__ __forceinline__ void pair_perm8(const f16* x, f16x2* out) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[j] = f16x2{x[j], x[j + 4]};
+}
+// 4 consecutive x values (one 8-bit word) into (x0,x2) (x1,x3).
+__device__ __forceinline__ void pair_perm4(const f16* x, f16x2* out) {
+    out[0] = f16x2{x[0], x[2]};
+    out[1] = f16x2{x[1], x[3]};
+}
+
+// Butterfly sum over `width` consecutive lanes (width a power of two <= 64); every lane of
+// the segment ends with the same total, in the same order on every run.
+template <int WIDTH>
+__device__ __forceinline__ float seg_sum(float v) {
+#pragma unroll
+    for (int off = WIDTH / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// Adapter of token t: adapter_idx[t] clamped into [0, n) (0 when no index array), so an
+// out-of-range index can never address memory outside the adapter stack.
+__device__ __forceinline__ int adapter_of(const int32_t* adapter_idx, int t, int n) {
+    if (!adapter_idx) return 0;
+    const int a = adapter_idx[t];
+    return a < 0 ? 0 : (a >= n ? n - 1 : a);
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+__device__ __forceinline__ float sigmoid(float z) { return 1.0f / (1.0f + __expf(-z)); }
+
+}  // namespace qmoe

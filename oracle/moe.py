@@ -136,6 +136,16 @@ def topk(logits: np.ndarray, k: int):
     return idx, w
 
 
+def topk_f32(logits32: np.ndarray, k: int, bias32: Optional[np.ndarray] = None):
+    """Top-K on float32 logits plus an optional float32 per-expert bias, the sum rounded to
+    float32 before any comparison (the precision in which the device takes the decision).
+    Weights as in :func:`topk`."""
+    ell = np.asarray(logits32, dtype=np.float32)
+    if bias32 is not None:
+        ell = ell + np.asarray(bias32, dtype=np.float32)[None, :]
+    return topk(ell.astype(np.float64), k)
+
+
 def topk_gap(logits: np.ndarray, k: int) -> np.ndarray:
     """Per token, the K-th largest logit minus the (K+1)-th (inf when K == E)."""
     s = -np.sort(-np.asarray(logits, dtype=np.float64), axis=1)

@@ -1,0 +1,150 @@
+"""The C-ABI library loads, exports every entry point its header declares, agrees with the
+binding on struct layout, and rejects bad arguments before touching the GPU (CPU only:
+every call here fails validation, so nothing is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import int4_group_quantized_amd as q
+from int4_group_quantized_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "qmoe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for n in ("qlinear_int4", "moe_switchglu_int4", "lora_apply", "router_topk"):
+        assert n in names
+
+
+def test_every_declared_function_is_exported():
+    lib = ctypes.CDLL(q.LIB_PATH)
+    names = declared_functions()
+    assert len(names) == 15
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.EXPORTED)
+
+
+def test_version_status_and_struct_layout():
+    assert q.lib.qmoe_abi_version() == 1
+    assert q.lib.qmoe_status_string(0) == b"ok"
+    assert q.lib.qmoe_status_string(-4) == b"workspace missing or too small"
+    assert q.lib.qmoe_abi_struct_size(0) == ctypes.sizeof(_lib.QWeightC)
+    assert q.lib.qmoe_abi_struct_size(1) == ctypes.sizeof(_lib.LoraC)
+    assert q.lib.qmoe_abi_struct_size(2) == ctypes.sizeof(_lib.MoELayerC)
+    assert q.lib.qmoe_abi_struct_size(7) == 0
+
+
+FAKE = 0x100000  # a 16-byte aligned fake device address; never dereferenced (validation fails first)
+
+
+def qw(rows=512, cols=2048, bits=4, n_experts=1, packed=FAKE):
+    return _lib.QWeightC(packed, FAKE, FAKE, rows, cols, bits, 64, n_experts)
+
+
+def test_quantize_rejects_bad_arguments():
+    f = q.lib.qmoe_quantize_affine
+    assert f(None, 4, 64, 4, 64, FAKE, FAKE, FAKE, None) == _lib.QMOE_ERR_INVALID_ARG
+    assert f(FAKE, 0, 64, 4, 64, FAKE, FAKE, FAKE, None) == _lib.QMOE_ERR_INVALID_ARG
+    assert f(FAKE, 4, 64, 3, 64, FAKE, FAKE, FAKE, None) == _lib.QMOE_ERR_UNSUPPORTED
+    assert f(FAKE, 4, 64, 4, 32, FAKE, FAKE, FAKE, None) == _lib.QMOE_ERR_UNSUPPORTED
+    assert f(FAKE, 4, 96, 4, 64, FAKE, FAKE, FAKE, None) == _lib.QMOE_ERR_UNSUPPORTED
+    assert f(FAKE + 4, 4, 64, 4, 64, FAKE, FAKE, FAKE, None) == _lib.QMOE_ERR_MISALIGNED
+
+
+def test_qlinear_rejects_bad_arguments():
+    f = q.lib.qlinear_int4
+    w = qw()
+    assert f(None, 1, ctypes.byref(w), None, None, FAKE, None) == _lib.QMOE_ERR_INVALID_ARG
+    assert f(FAKE, 0, ctypes.byref(w), None, None, FAKE, None) == _lib.QMOE_ERR_INVALID_ARG
+    assert f(FAKE, 5000, ctypes.byref(w), None, None, FAKE, None) == _lib.QMOE_ERR_UNSUPPORTED
+    bad = qw(cols=1000)
+    assert f(FAKE, 1, ctypes.byref(bad), None, None, FAKE, None) == _lib.QMOE_ERR_UNSUPPORTED
+    bad = qw(bits=2)
+    assert f(FAKE, 1, ctypes.byref(bad), None, None, FAKE, None) == _lib.QMOE_ERR_UNSUPPORTED
+    bad = qw(packed=FAKE + 8)
+    assert f(FAKE, 1, ctypes.byref(bad), None, None, FAKE, None) == _lib.QMOE_ERR_MISALIGNED
+    assert f(FAKE, 1, ctypes.byref(w), None, None, FAKE + 2, None) == _lib.QMOE_ERR_MISALIGNED
+    lo = _lib.LoraC(FAKE, FAKE, 65, 1, 2048, 512, 2.0)
+    assert f(FAKE, 1, ctypes.byref(w), ctypes.byref(lo), None, FAKE * 8, None) == _lib.QMOE_ERR_UNSUPPORTED
+    lo = _lib.LoraC(FAKE, FAKE, 16, 1, 1024, 512, 2.0)
+    assert f(FAKE, 1, ctypes.byref(w), ctypes.byref(lo), None, FAKE * 8, None) == _lib.QMOE_ERR_INVALID_ARG
+    # output overlapping the input
+    assert f(FAKE, 1, ctypes.byref(w), None, None, FAKE + 16, None) == _lib.QMOE_ERR_INVALID_ARG
+
+
+def test_router_topk_rejects_bad_arguments():
+    f = q.lib.router_topk
+    assert f(None, 1, 256, 4, None, FAKE, FAKE, None) == _lib.QMOE_ERR_INVALID_ARG
+    assert f(FAKE, 1, 256, 0, None, FAKE, FAKE, None) == _lib.QMOE_ERR_INVALID_ARG
+    assert f(FAKE, 1, 256, 33, None, FAKE, FAKE, None) == _lib.QMOE_ERR_UNSUPPORTED
+    assert f(FAKE, 1, 2048, 4, None, FAKE, FAKE, None) == _lib.QMOE_ERR_UNSUPPORTED
+    assert f(FAKE, 1, 4, 5, None, FAKE, FAKE, None) == _lib.QMOE_ERR_UNSUPPORTED
+
+
+def test_lora_apply_rejects_bad_arguments():
+    f = q.lib.lora_apply
+    lo = _lib.LoraC(FAKE, FAKE, 16, 1, 2048, 512, 2.0)
+    assert f(None, 1, ctypes.byref(lo), None, FAKE, None) == _lib.QMOE_ERR_INVALID_ARG
+    bad = _lib.LoraC(FAKE, FAKE, 0, 1, 2048, 512, 2.0)
+    assert f(FAKE, 1, ctypes.byref(bad), None, FAKE, None) == _lib.QMOE_ERR_INVALID_ARG
+    bad = _lib.LoraC(FAKE, FAKE, 16, 1, 1000, 512, 2.0)
+    assert f(FAKE, 1, ctypes.byref(bad), None, FAKE, None) == _lib.QMOE_ERR_UNSUPPORTED
+
+
+def layer_c(**kw):
+    H, I, E = 2048, 512, 256
+    d = dict(hidden=H, inter=I, shared_inter=512, n_experts=E, top_k=4, add_residual=0,
+             router=qw(E, H, 8), shared_gate=qw(1, H, 8), exp_gate=qw(I, H, 4, E),
+             exp_up=qw(I, H, 4, E), exp_down=qw(H, I, 4, E), sh_gate=qw(512, H), sh_up=qw(512, H),
+             sh_down=qw(H, 512))
+    d.update(kw)
+    return _lib.MoELayerC(**d)
+
+
+def test_moe_workspace_and_validation():
+    L = layer_c()
+    ws1 = q.lib.moe_switchglu_int4_workspace_bytes(ctypes.byref(L), 1)
+    ws512 = q.lib.moe_switchglu_int4_workspace_bytes(ctypes.byref(L), 512)
+    assert 0 < ws1 < ws512
+    assert q.lib.moe_switchglu_int4_workspace_bytes(ctypes.byref(L), 0) == 0
+    f = q.lib.moe_switchglu_int4
+    X, Y = FAKE, FAKE * 16
+    assert f(ctypes.byref(L), X, 1, None, Y, None, None, None, 0, None) == _lib.QMOE_ERR_WORKSPACE
+    assert f(ctypes.byref(L), X, 1, None, Y, None, None, FAKE * 64, ws1 - 1, None) == _lib.QMOE_ERR_WORKSPACE
+    assert f(ctypes.byref(L), X, 1, None, Y, None, None, FAKE * 64 + 16, ws1, None) == _lib.QMOE_ERR_MISALIGNED
+    assert f(ctypes.byref(L), X, 1, None, X, None, None, FAKE * 64, ws1, None) == _lib.QMOE_ERR_INVALID_ARG
+    for bad in (layer_c(top_k=0), layer_c(top_k=300), layer_c(hidden=1000),
+                layer_c(router=qw(256, 2048, 4)), layer_c(exp_down=qw(512, 2048, 4, 256)),
+                layer_c(n_experts=2000)):
+        st = f(ctypes.byref(bad), X, 1, None, Y, None, None, FAKE * 64, 1 << 30, None)
+        assert st in (_lib.QMOE_ERR_INVALID_ARG, _lib.QMOE_ERR_UNSUPPORTED), st
+    lo = _lib.LoraC(FAKE, FAKE, 16, 4, 2048, 1024, 2.0)  # wrong out_dim for the shared gate
+    bad = layer_c(lora_gate=ctypes.pointer(lo))
+    assert f(ctypes.byref(bad), X, 1, None, Y, None, None, FAKE * 64, 1 << 30, None) == _lib.QMOE_ERR_INVALID_ARG
+
+
+def test_supergroup_rejects_bad_arguments():
+    f = q.lib.qlinear_supergroup
+    assert f(FAKE, 1, FAKE, FAKE, FAKE, 3070, 1024, 4, FAKE * 4, None) == _lib.QMOE_ERR_UNSUPPORTED
+    assert f(FAKE, 1, FAKE, None, FAKE, 3072, 1024, 4, FAKE * 4, None) == _lib.QMOE_ERR_INVALID_ARG
+    assert f(FAKE, 1, FAKE, FAKE, FAKE, 3072, 1000, 4, FAKE * 4, None) == _lib.QMOE_ERR_UNSUPPORTED
+    g = q.lib.qmoe_quantize_supergroup
+    assert g(FAKE, 3072, 1024, 0, FAKE, FAKE, FAKE, None) == _lib.QMOE_ERR_INVALID_ARG
+    assert g(FAKE, 3072, 1024, 5, FAKE, FAKE, FAKE, None) == _lib.QMOE_ERR_UNSUPPORTED
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    with pytest.raises(TypeError):
+        q.quantize_affine(torch.zeros(4, 64))

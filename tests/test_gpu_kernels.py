@@ -1,0 +1,231 @@
+"""GPU parity of the building blocks against the oracle, through the C ABI.
+
+Bit-exact: quantized words, scales, biases, unpacked codes, fp32 dequantized weights,
+top-K indices on given logits, super-group codes and scales.  Floating point: max abs
+2e-2 and relative L2 1e-3 against the float64 oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import affine, moe, supergroup
+from layers import assert_close
+
+pytestmark = pytest.mark.gpu
+W = synth.Workload.TEST
+DEV = "cuda"
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+@pytest.fixture(scope="module")
+def q():
+    import int4_group_quantized_amd as q
+    assert torch.cuda.is_available()
+    return q
+
+
+def ulp_distance(a, b):
+    """Largest distance in fp16 steps between two fp16 arrays (ordered-integer view)."""
+    def ordered(v):
+        i = np.asarray(v, np.float16).view(np.int16).astype(np.int32)
+        return np.where(i < 0, -32768 - i, i)
+    return int(np.max(np.abs(ordered(a) - ordered(b))))
+
+
+def special_matrix(rows, cols, seed):
+    """N(0, 0.02) with planted degenerate groups, outliers and on-grid groups."""
+    g = np.random.default_rng(seed)
+    w = (g.standard_normal((rows, cols)) * 0.02).astype(np.float32)
+    w[0, :64] = 0.5                      # constant group: scale 0
+    w[1, 64:128] = 0.0
+    w[2, 5] = 3.0                        # outlier
+    w[3, :64] = (np.arange(64) % 16 * 0.25 - 1).astype(np.float32)   # on an int4 grid
+    return w
+
+
+# ------------------------------------------------------------------------------ quantize
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("shape", [(512, 2048), (7, 64), (33, 192), (256, 2048), (2048, 512)])
+def test_quantize_bit_exact(q, bits, shape):
+    print(f"quantize bits={bits} shape={shape}", flush=True)
+    w = special_matrix(*shape, seed=shape[0] * 31 + bits)
+    ref = affine.quantize(w, bits)
+    got = q.quantize_affine(dev(w), bits)
+    assert np.array_equal(host(got.packed).view(np.uint32), ref.packed)
+    assert np.array_equal(host(got.scales).view(np.uint16), ref.scales.view(np.uint16))
+    assert np.array_equal(host(got.biases).view(np.uint16), ref.biases.view(np.uint16))
+
+
+def test_quantize_full_expert_stack_slice(q):
+    """A config-sized matrix from the seeded generator (gate_proj of expert 0)."""
+    w = synth.normal_f32((512, 2048), 0.02, synth.Workload.MOE_DECODE, 0, synth.Role.EXP_GATE, 0)
+    ref = affine.quantize(w, 4)
+    got = q.quantize_affine(dev(w), 4)
+    assert np.array_equal(host(got.packed).view(np.uint32), ref.packed)
+    assert np.array_equal(host(got.scales).view(np.uint16), ref.scales.view(np.uint16))
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_unpack_and_dequantize_bit_exact(q, bits):
+    words = synth.random_words((96, 2048 * bits // 32), W, 1, synth.Role.WORDS, bits)
+    sc = synth.uniform_f16((96, 32), -0.05, 0.05, W, 1, synth.Role.SCALES, bits)
+    bi = synth.uniform_f16((96, 32), -1.0, 1.0, W, 1, synth.Role.BIASES, bits)
+    qw = affine.QWeight(words, sc, bi, bits, 64)
+    g = q.QWeight.from_arrays(words, sc, bi, bits, DEV)
+    assert np.array_equal(host(q.unpack(g)), affine.unpack(words, bits))
+    assert np.array_equal(host(q.dequantize(g)).view(np.uint32), affine.dequantize_f32(qw).view(np.uint32))
+
+
+def test_dequantize_expert_stack(q):
+    E = 3
+    words = synth.random_words((E, 64, 64), W, 2, synth.Role.WORDS)
+    sc = synth.uniform_f16((E, 64, 8), 0.0, 0.02, W, 2, synth.Role.SCALES)
+    bi = synth.uniform_f16((E, 64, 8), -0.1, 0.0, W, 2, synth.Role.BIASES)
+    g = q.QWeight.from_arrays(words, sc, bi, 4, DEV)
+    out = host(q.dequantize(g)).reshape(E, 64, 512)
+    for e in range(E):
+        ref = affine.dequantize_f32(affine.QWeight(words[e], sc[e], bi[e], 4, 64))
+        assert np.array_equal(out[e].view(np.uint32), ref.view(np.uint32))
+
+
+# ------------------------------------------------------------------------------ qlinear
+
+def _qw(rows, cols, bits, idx):
+    w = synth.normal_f32((rows, cols), 0.02, W, 3, synth.Role.DENSE, idx)
+    return affine.quantize(w, bits)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("m,rows,cols", [(1, 512, 2048), (1, 2048, 512), (3, 96, 1024),
+                                         (8, 40, 1536), (13, 64, 2048), (1, 1, 512),
+                                         (2, 130, 4096)])
+def test_qlinear_matches_oracle(q, bits, m, rows, cols):
+    print(f"qlinear bits={bits} m={m} rows={rows} cols={cols}", flush=True)
+    ref_w = _qw(rows, cols, bits, rows + cols + m)
+    x = synth.activations(m, cols, W, 3, m)
+    y = host(q.qlinear_int4(dev(x), q.QWeight.from_arrays(ref_w.packed, ref_w.scales, ref_w.biases, bits, DEV)))
+    assert_close(y, moe.qlinear(x, ref_w), what="qlinear")
+
+
+def test_qlinear_decode_workload_with_seeded_generator(q):
+    """The decode GEMV workload: x [1 x 2048] ~ N(0,1), W [512 x 2048] ~ N(0, 0.02)."""
+    w = synth.normal_f32((512, 2048), 0.02, synth.Workload.GEMV, 0, synth.Role.DENSE)
+    x = synth.activations(1, 2048, synth.Workload.GEMV)
+    ref_w = affine.quantize(w, 4)
+    gw = q.quantize_affine(dev(w), 4)       # the device quantizer feeds the device GEMV
+    assert np.array_equal(host(gw.packed).view(np.uint32), ref_w.packed)
+    y = host(q.qlinear_int4(dev(x), gw))
+    ref = moe.qlinear(x, ref_w)
+    assert_close(y, ref, what="gemv workload")
+    assert ulp_distance(y, moe.to_f16(ref)) <= 1   # within one fp16 step of exact rounding
+
+
+def test_qlinear_integer_case_exact(q):
+    """scale 1, bias 0, integer x: every partial sum is an integer below 2^24, so the
+    device result is exact."""
+    g = np.random.default_rng(5)
+    N, K, T = 64, 2048, 2
+    codes = g.integers(0, 16, size=(N, K)).astype(np.uint8)
+    qw = affine.QWeight(affine.pack(codes, 4), np.ones((N, 32), np.float16),
+                        np.zeros((N, 32), np.float16), 4, 64)
+    x = g.integers(-2, 3, size=(T, K)).astype(np.float16)
+    y = host(q.qlinear_int4(dev(x), q.QWeight.from_arrays(qw.packed, qw.scales, qw.biases, 4, DEV)))
+    ref = (x.astype(np.int64) @ codes.astype(np.int64).T).astype(np.float16)
+    assert np.array_equal(y, ref)
+
+
+def test_qlinear_with_lora_and_adapters(q):
+    rows, cols, T, n_ad, r = 512, 2048, 8, 4, 16
+    ref_w = _qw(rows, cols, 4, 77)
+    A = synth.normal_f16((n_ad, r, cols), 0.01, W, 4, synth.Role.LORA_A_GATE)
+    B = synth.normal_f16((n_ad, rows, r), 0.01, W, 4, synth.Role.LORA_B_GATE)
+    L = moe.Lora(A, B, 2.0)
+    ad = synth.adapter_index(T, 2)
+    x = synth.activations(T, cols, W, 4)
+    gw = q.QWeight.from_arrays(ref_w.packed, ref_w.scales, ref_w.biases, 4, DEV)
+    y = host(q.qlinear_int4(dev(x), gw, q.Lora(dev(A), dev(B), 2.0), dev(ad)))
+    assert_close(y, moe.qlinear(x, ref_w, L, ad), what="qlinear+lora")
+
+
+# ------------------------------------------------------------------------------ router
+
+@pytest.mark.parametrize("t,e,k", [(1, 256, 4), (16, 256, 8), (512, 256, 4), (5, 1024, 32),
+                                   (3, 7, 7), (2, 64, 1)])
+def test_router_topk_bit_exact_on_given_logits(q, t, e, k):
+    g = np.random.default_rng(t * 1000 + e + k)
+    logits = g.standard_normal((t, e)).astype(np.float32)
+    bias = np.zeros(e, np.float32)
+    bias[:min(16, e)] = 2.0
+    for b in (None, bias):
+        idx, w = q.router_topk(dev(logits), k, None if b is None else dev(b))
+        ridx, rw = moe.topk_f32(logits, k, b)
+        assert np.array_equal(host(idx), ridx)
+        np.testing.assert_allclose(host(w), rw, rtol=0, atol=1e-6)
+
+
+def test_router_topk_exact_ties(q):
+    logits = np.zeros((4, 256), np.float32)
+    logits[0, [200, 3, 77, 150]] = 1.0
+    logits[1, :] = 0.25                                  # all tied -> 0, 1, 2, 3
+    logits[2, [9, 8]] = 5.0
+    logits[2, [255, 0]] = 4.0
+    logits[3, :] = -np.arange(256, dtype=np.float32)[::-1]   # increasing: top are 255...
+    idx, w = q.router_topk(dev(logits), 4)
+    ridx, rw = moe.topk_f32(logits, 4)
+    assert np.array_equal(host(idx), ridx)
+    assert host(idx)[1].tolist() == [0, 1, 2, 3]
+    assert host(idx)[2].tolist() == [8, 9, 0, 255]
+    np.testing.assert_allclose(host(w)[1], 0.25, atol=1e-7)
+
+
+# ------------------------------------------------------------------------------ LoRA
+
+@pytest.mark.parametrize("t,in_dim,out_dim,r,n_ad", [(1, 2048, 512, 16, 1), (16, 2048, 512, 16, 4),
+                                                     (3, 512, 2048, 16, 2), (2, 1024, 300, 64, 1)])
+def test_lora_apply(q, t, in_dim, out_dim, r, n_ad):
+    A = synth.normal_f16((n_ad, r, in_dim), 0.01, W, 5, synth.Role.LORA_A_UP, r)
+    B = synth.normal_f16((n_ad, out_dim, r), 0.01, W, 5, synth.Role.LORA_B_UP, r)
+    L = moe.Lora(A, B, 32.0 / r)
+    x = synth.activations(t, in_dim, W, 5, t)
+    ad = (np.arange(t) % n_ad).astype(np.int32)
+    y0 = synth.normal_f32((t, out_dim), 1.0, W, 5, synth.Role.MISC)
+    got = host(q.lora_apply(dev(x), q.Lora(dev(A), dev(B), L.scale), dev(y0.copy()), dev(ad)))
+    ref = y0.astype(np.float64) + moe.lora_delta(x, L, ad)
+    np.testing.assert_allclose(got, ref, rtol=1e-5, atol=1e-6)
+
+
+# ------------------------------------------------------------------------------ super-group
+
+@pytest.mark.parametrize("rows,cols,period", [(3072, 1024, 4), (64, 512, 4), (48, 2048, 2),
+                                              (16, 512, 1)])
+def test_supergroup_quantize_bit_exact(q, rows, cols, period):
+    w = synth.normal_f32((rows, cols), 0.02, synth.Workload.SUPERGROUP, 0, synth.Role.SUPERGROUP, rows + period)
+    w[0, :] = 0.0                                                       # epsilon floor
+    ref, _ = supergroup.quantize(w, period)
+    got = q.quantize_supergroup(dev(w), period)
+    assert np.array_equal(host(got.scales).view(np.uint16), ref.scales.view(np.uint16))
+    assert np.array_equal(host(got.p4).view(np.uint32), ref.p4)
+    if period > 1:
+        assert np.array_equal(host(got.p2).view(np.uint32), ref.p2)
+
+
+@pytest.mark.parametrize("b", [1, 3, 64])
+def test_supergroup_gemm(q, b):
+    rows, cols = 3072, 1024
+    w = synth.normal_f32((rows, cols), 0.02, synth.Workload.SUPERGROUP, 0, synth.Role.SUPERGROUP)
+    ref, _ = supergroup.quantize(w, 4)
+    x = synth.activations(b, cols, synth.Workload.SUPERGROUP, 0, b)
+    W_ = q.SuperGroupWeight(dev(ref.p4.view(np.int32)), dev(ref.p2.view(np.int32)), dev(ref.scales),
+                            4, rows, cols)
+    y = host(q.qlinear_supergroup(dev(x), W_))
+    assert_close(y, supergroup.gemm(x, ref), what="supergroup")
