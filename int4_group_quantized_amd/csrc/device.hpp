@@ -77,12 +77,41 @@ __device__ __forceinline__ void pair_perm4(const f16* x, f16x2* out) {
     out[1] = f16x2{x[1], x[3]};
 }
 
-// Butterfly sum over `width` consecutive lanes (width a power of two <= 64); every lane of
-// the segment ends with the same total, in the same order on every run.
+// ---- cross-lane sums without LDS round trips -------------------------------------------
+// DPP controls (gfx9): quad_perm [1,0,3,2] and [2,3,0,1], row_half_mirror (lane i <-> 7-i
+// in each 8), row_mirror (i <-> 15-i in each 16).  After the first two steps the four lanes
+// of a quad hold equal values, so each mirror step pairs every lane with a lane of the
+// neighbouring quad / half-row: the result is the segment total in every lane, the same
+// bits in every lane (fp add is commutative), and the same order on every run.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL,
+                                                              0xF, 0xF, true));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
+}
+constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140;
+
+// Sum over aligned segments of WIDTH lanes (a power of two <= 64), total in every lane.
+// Segments of 32 and 64 lanes combine their 16-lane rows through scalar readlanes in a
+// fixed order.
 template <int WIDTH>
 __device__ __forceinline__ float seg_sum(float v) {
-#pragma unroll
-    for (int off = WIDTH / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    if constexpr (WIDTH >= 2) v += dpp<DPP_XOR1>(v);
+    if constexpr (WIDTH >= 4) v += dpp<DPP_XOR2>(v);
+    if constexpr (WIDTH >= 8) v += dpp<DPP_HALF_MIRROR>(v);
+    if constexpr (WIDTH >= 16) v += dpp<DPP_MIRROR>(v);
+    if constexpr (WIDTH >= 32) {
+        const int bits = __builtin_bit_cast(int, v);
+        const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(bits, 0));
+        const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(bits, 16));
+        const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(bits, 32));
+        const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(bits, 48));
+        if constexpr (WIDTH == 32) v = (threadIdx.x & 32) ? r2 + r3 : r0 + r1;
+        else v = (r0 + r1) + (r2 + r3);
+    }
     return v;
 }
 

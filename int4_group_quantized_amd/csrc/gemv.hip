@@ -101,6 +101,40 @@ __global__ void __launch_bounds__(256) k_qgemv(const uint16_t* __restrict__ x, i
     }
 }
 
+// Fast path (no LoRA, m <= 8, at most two 32-input chunks per lane): each lane segment's
+// weight loads are issued first, then x is staged, so the two memory round trips overlap.
+template <int BITS>
+__global__ void __launch_bounds__(256) k_qgemv_fast(const uint16_t* __restrict__ x, int m, int K,
+                                                    int N, const uint32_t* __restrict__ packed,
+                                                    const uint16_t* __restrict__ scales,
+                                                    const uint16_t* __restrict__ biases,
+                                                    uint16_t* __restrict__ y) {
+    extern __shared__ __align__(16) char smem[];
+    asm volatile("" ::"s"(x), "s"(packed), "s"(scales), "s"(biases));   // args in one batch
+    asm volatile("" ::"s"(y), "s"(m), "s"(K), "s"(N));
+    f16x2* xs = reinterpret_cast<f16x2*>(smem);                        // [m][K/2]
+    float* xsum = reinterpret_cast<float*>(smem + XS_BYTES);            // [m][K/32]
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lpr = lanes_per_row(K), rpw = 64 / lpr, seg = lane / lpr, sl = lane % lpr;
+    const int row = (blockIdx.x * 4 + wave) * rpw + seg;
+    RowRegs<BITS, 2> rr;
+    rr.load(packed, scales, biases, K, row < N ? row : 0, lpr, sl, row < N);
+    const uint4* x4 = reinterpret_cast<const uint4*>(x);
+    stage_rows<BITS, 8>([=](int i) { return x4 + (long)i * (K / 8); }, m, K, xs, xsum);
+    __syncthreads();
+    float acc[GEMV_MT];
+#pragma unroll
+    for (int t = 0; t < GEMV_MT; ++t) acc[t] = 0.0f;
+    rr.dot(K, lpr, sl, xs, xsum, m, acc);
+#pragma unroll
+    for (int t = 0; t < GEMV_MT; ++t) {
+        if (t < m) {
+            const float v = segment_sum(acc[t], lpr);
+            if (sl == 0 && row < N) y[(long)t * N + row] = f2h(v);
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_qlinear_gemv(const uint16_t* x, int m, const qmoe_qweight& w,
@@ -112,6 +146,13 @@ hipError_t launch_qlinear_gemv(const uint16_t* x, int m, const qmoe_qweight& w,
     const size_t smem = (size_t)XS_BYTES + (size_t)GEMV_MT * (K / 32) * 4 + (size_t)GEMV_MT * MAX_RANK * 4;
     const int wave_rows = (N + rpw - 1) / rpw;
     const unsigned blocks = (unsigned)std::max(1, std::min((wave_rows + 3) / 4, 2048));
+    const int cpl = (K / 32) / lanes_per_row(K);
+    if (!lora && m <= mt_max && cpl <= 2 && m * (K / 8) <= 256 * 8) {
+        const unsigned fb = (unsigned)((N + 4 * rpw - 1) / (4 * rpw));
+        if (w.bits == 4) k_qgemv_fast<4><<<fb, 256, smem, s>>>(x, m, K, N, w.packed, w.scales, w.biases, y);
+        else k_qgemv_fast<8><<<fb, 256, smem, s>>>(x, m, K, N, w.packed, w.scales, w.biases, y);
+        return hipGetLastError();
+    }
     const uint16_t* A = lora ? lora->A : nullptr;
     const uint16_t* B = lora ? lora->B : nullptr;
     const int rank = lora ? lora->rank : 0;

@@ -28,42 +28,14 @@
 
 #include "gemv_core.hpp"
 #include "launch.hpp"
+#include "moe_common.hpp"
 
 namespace qmoe {
 
 namespace {
 
-constexpr int MAX_RANK = 64;
 constexpr int MT = GEMV_MT;
-constexpr int MAX_K = 32;
 constexpr int ROUTE_THREADS = 1024;
-
-struct QW {
-    const uint32_t* p;
-    const uint16_t* s;
-    const uint16_t* b;
-};
-
-struct MoeArgs {
-    int T, H, I, SI, E, K, add_residual, max_slots;
-    const uint16_t* x;
-    uint16_t* y;
-    const int32_t* adapter;
-    QW router, sgate, eg, eu, ed, shg, shu, shd;
-    const uint16_t *Ag, *Bg, *Au, *Bu, *Ad, *Bd;
-    int rg, ru, rd;
-    int nag, nau, nad;  // adapters per projection
-    float lsg, lsu, lsd;
-    const float* rbias;
-    // workspace
-    float *logits, *gate, *zg, *zu, *gs, *us;
-    int32_t *idx, *offs, *perm, *uniq, *nuniq;
-    float* wts;
-    uint16_t *h, *hs;
-    float *o, *os;
-    int32_t* idx_out;
-    float* w_out;
-};
 
 struct Layout {
     size_t logits, gate, zg, zu, gs, us, idx, wts, offs, perm, uniq, nuniq, h, hs, o, os, total;
@@ -76,7 +48,7 @@ Layout layout_of(const qmoe_moe_layer& L, int T) {
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t r = off; off = up256(off + bytes); return r; };
     const size_t TK = (size_t)T * L.top_k;
-    l.logits = take((size_t)T * L.n_experts * 4);
+    l.logits = take((size_t)T * ((L.n_experts + 63) / 64 * 64) * 4);
     l.gate = take((size_t)T * 4);
     l.zg = take((size_t)T * MAX_RANK * 4);
     l.zu = take((size_t)T * MAX_RANK * 4);
@@ -96,95 +68,7 @@ Layout layout_of(const qmoe_moe_layer& L, int T) {
     return l;
 }
 
-// ------------------------------------------------------------------------------ helpers
-
-// One wave: the K largest of v + bias over e entries (ties to the lower index) and the
-// softmax over them.  Results are valid in every lane.
-__device__ void topk_wave(const float* __restrict__ v, const float* __restrict__ bias, int e,
-                          int k, int* si, float* sw) {
-    const int lane = threadIdx.x & 63;
-    constexpr int PER = 16;  // e <= 1024
-    float val[PER];
-    uint32_t live = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const int ei = lane + 64 * i;
-        val[i] = 0.0f;
-        if (ei < e) {
-            val[i] = v[ei] + (bias ? bias[ei] : 0.0f);
-            live |= 1u << i;
-        }
-    }
-    for (int r = 0; r < k; ++r) {
-        float bv = 0.0f;
-        int bi = -1;
-#pragma unroll
-        for (int i = 0; i < PER; ++i)
-            if (((live >> i) & 1u) && (bi < 0 || val[i] > bv)) { bv = val[i]; bi = lane + 64 * i; }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const float ov = __shfl_xor(bv, off, 64);
-            const int oi = __shfl_xor(bi, off, 64);
-            if (oi >= 0 && (bi < 0 || ov > bv || (ov == bv && oi < bi))) { bv = ov; bi = oi; }
-        }
-        if ((bi & 63) == lane) live &= ~(1u << (bi >> 6));
-        si[r] = bi;
-        sw[r] = bv;
-    }
-    const float m = sw[0];
-    float sum = 0.0f;
-    for (int r = 0; r < k; ++r) { sw[r] = expf(sw[r] - m); sum += sw[r]; }
-    for (int r = 0; r < k; ++r) sw[r] = sw[r] / sum;
-}
-
-// LoRA z for tokens rows[0..mt): z[i][r] = A[a][r] . src[rows[i]] (K inputs), one wave per
-// (i, r).  Written to LDS zl[i * MAX_RANK + r].
-__device__ void lora_z_lds(const uint16_t* __restrict__ src, const int* rows, const int* toks,
-                           int mt, int K, const uint16_t* __restrict__ A, int rank,
-                           const int32_t* __restrict__ adapter, int n_ad, float* zl) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    for (int p = wave; p < mt * rank; p += nw) {
-        const int i = p / rank, r = p % rank;
-        const int a = adapter_of(adapter, toks[i], n_ad);
-        const uint16_t* arow = A + ((long)a * rank + r) * K;
-        const uint16_t* xrow = src + (long)rows[i] * K;
-        float acc = 0.0f;
-        for (int k = lane * 8; k < K; k += 512) {
-            const uint4 av = *reinterpret_cast<const uint4*>(arow + k);
-            const uint4 xv = *reinterpret_cast<const uint4*>(xrow + k);
-            const f16x2* ah = reinterpret_cast<const f16x2*>(&av);
-            const f16x2* xh = reinterpret_cast<const f16x2*>(&xv);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_fdot2(ah[j], xh[j], acc, false);
-        }
-        acc = seg_sum<64>(acc);
-        if (lane == 0) zl[i * MAX_RANK + r] = acc;
-    }
-}
-
-__device__ __forceinline__ float lora_b_dot(const uint16_t* __restrict__ B, int a, int out_dim,
-                                            int n, int rank, const float* z) {
-    const uint16_t* brow = B + ((long)a * out_dim + n) * rank;
-    float d = 0.0f;
-    for (int r = 0; r < rank; ++r) d = fmaf(h2f(brow[r]), z[r], d);
-    return d;
-}
-
 // ------------------------------------------------------------------------------ 1. x-side
-
-struct XsideGrid {
-    int nb_router, nb_gate, nb_shared, nb_z;
-};
-
-__host__ __device__ inline XsideGrid xside_grid(int T, int H, int E, int SI, int zjobs) {
-    XsideGrid g;
-    const int r8 = 4 * (64 / lanes_per_row(H));  // rows per block, 8-bit and 4-bit alike
-    g.nb_router = (E + r8 - 1) / r8;
-    g.nb_gate = 1;
-    g.nb_shared = (2 * SI + r8 - 1) / r8;
-    g.nb_z = (zjobs + 3) / 4;
-    return g;
-}
 
 __global__ void __launch_bounds__(256) k_moe_xside(MoeArgs a) {
     __shared__ __align__(16) f16x2 xs[8192];  // 32 KB: tokens per pass = 8192 / (K/2)
@@ -198,27 +82,7 @@ __global__ void __launch_bounds__(256) k_moe_xside(MoeArgs a) {
     int b = blockIdx.x;
 
     if (b >= g.nb_router + g.nb_gate + g.nb_shared) {  // LoRA z jobs: one wave per dot
-        const int j = (b - g.nb_router - g.nb_gate - g.nb_shared) * 4 + wave;
-        if (j >= zjobs) return;
-        const int ng = a.Ag ? a.T * a.rg : 0;
-        const bool isg = j < ng;
-        const int jj = isg ? j : j - ng;
-        const int rank = isg ? a.rg : a.ru;
-        const int t = jj / rank, r = jj % rank;
-        const int ad = adapter_of(a.adapter, t, isg ? a.nag : a.nau);
-        const uint16_t* arow = (isg ? a.Ag : a.Au) + ((long)ad * rank + r) * H;
-        const uint16_t* xrow = a.x + (long)t * H;
-        float acc = 0.0f;
-        for (int k = lane * 8; k < H; k += 512) {
-            const uint4 av = *reinterpret_cast<const uint4*>(arow + k);
-            const uint4 xv = *reinterpret_cast<const uint4*>(xrow + k);
-            const f16x2* ah = reinterpret_cast<const f16x2*>(&av);
-            const f16x2* xh = reinterpret_cast<const f16x2*>(&xv);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_fdot2(ah[i], xh[i], acc, false);
-        }
-        acc = seg_sum<64>(acc);
-        if (lane == 0) (isg ? a.zg : a.zu)[t * MAX_RANK + r] = acc;
+        xside_lora_z(a, (b - g.nb_router - g.nb_gate - g.nb_shared) * 4 + wave, zjobs);
         return;
     }
 
@@ -242,7 +106,7 @@ __global__ void __launch_bounds__(256) k_moe_xside(MoeArgs a) {
             row = (b * 4 + wave) * rpw + seg;
             if (row < a.E) qdot_row<8>(a.router.p, a.router.s, a.router.b, H, row, lpr, sl, xs, xsum, mt, acc);
             out = a.logits + row;
-            ostride = a.E;
+            ostride = a.Ep;
             if (row >= a.E) row = -1;
         } else if (b < g.nb_router + g.nb_gate) {
             row = (wave == 0 && seg == 0) ? 0 : -1;
@@ -279,19 +143,19 @@ __global__ void __launch_bounds__(ROUTE_THREADS) k_moe_route(MoeArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = ROUTE_THREADS / 64;
     const int K = a.K, E = a.E, TK = a.T * a.K;
 
+    __shared__ int wsel[ROUTE_THREADS / 64][MAX_K];
+    __shared__ float wsw[ROUTE_THREADS / 64][MAX_K];
     for (int t = wave; t < a.T; t += nw) {
-        int si[MAX_K];
-        float sw[MAX_K];
-        topk_wave(a.logits + (long)t * E, a.rbias, E, K, si, sw);
-        if (lane < K) {
-            int sel = 0;
-            float wv = 0.0f;
-            for (int r = 0; r < K; ++r)
-                if (r == lane) { sel = si[r]; wv = sw[r]; }
-            a.idx[(long)t * K + lane] = sel;
-            a.wts[(long)t * K + lane] = wv;
-            if (a.idx_out) a.idx_out[(long)t * K + lane] = sel;
-            if (a.w_out) a.w_out[(long)t * K + lane] = wv;
+        wave_topk(a.logits + (long)t * a.Ep, a.rbias, E, K, wsel[wave], wsw[wave]);
+        if (lane == 0) {
+            for (int r = 0; r < K; ++r) {
+                const int sel = wsel[wave][r];
+                const float wv = wsw[wave][r];
+                a.idx[(long)t * K + r] = sel;
+                a.wts[(long)t * K + r] = wv;
+                if (a.idx_out) a.idx_out[(long)t * K + r] = sel;
+                if (a.w_out) a.w_out[(long)t * K + r] = wv;
+            }
         }
     }
     for (int e = tid; e < 1024; e += ROUTE_THREADS) { cnt[e] = 0; fill[e] = 0; }
@@ -505,6 +369,7 @@ hipError_t launch_moe(const qmoe_moe_layer& L, int stage, const uint16_t* x, int
     MoeArgs a{};
     a.T = T; a.H = L.hidden; a.I = L.inter; a.SI = L.shared_inter; a.E = L.n_experts;
     a.K = L.top_k; a.add_residual = L.add_residual;
+    a.Ep = (L.n_experts + 63) / 64 * 64;
     a.max_slots = std::min(T * L.top_k, L.n_experts);
     a.x = x; a.y = y; a.adapter = adapter_idx;
     auto qw = [](const qmoe_qweight& w) { return QW{w.packed, w.scales, w.biases}; };
@@ -533,6 +398,7 @@ hipError_t launch_moe(const qmoe_moe_layer& L, int stage, const uint16_t* x, int
     a.os = reinterpret_cast<float*>(base + lo.os);
     a.idx_out = idx_out;
     a.w_out = w_out;
+    if (decode_path_fits(L, T)) return launch_moe_decode(a, stage, s);
 
     const int zjobs = (a.Ag ? T * a.rg : 0) + (a.Au ? T * a.ru : 0);
     const XsideGrid g = xside_grid(T, a.H, a.E, a.SI, zjobs);

@@ -1,0 +1,198 @@
+// Shared pieces of the two MoE layer paths (moe.hip: sorted, any token count; moe_decode.hip:
+// a few tokens): kernel arguments, the x-side job grid, top-K of one token in one wave, and
+// LoRA helpers.
+#pragma once
+
+#include "gemv_core.hpp"
+#include "qmoe.h"
+#include "topk.hpp"
+
+namespace qmoe {
+
+constexpr int MAX_RANK = 64;
+constexpr int MAX_K = 32;
+constexpr int MAX_DEC_T = 32;  // the decode path serves up to this many tokens per call
+constexpr int MAX_DEC_K = 8;   // ... and up to this many experts per token
+
+struct QW {
+    const uint32_t* p;
+    const uint16_t* s;
+    const uint16_t* b;
+};
+
+struct MoeArgs {
+    int T, H, I, SI, E, K, add_residual, max_slots;
+    int Ep;  // logits row stride: E rounded up to a multiple of 64
+    const uint16_t* x;
+    uint16_t* y;
+    const int32_t* adapter;
+    QW router, sgate, eg, eu, ed, shg, shu, shd;
+    const uint16_t *Ag, *Bg, *Au, *Bu, *Ad, *Bd;
+    int rg, ru, rd;
+    int nag, nau, nad;  // adapters per projection
+    float lsg, lsu, lsd;
+    const float* rbias;
+    // workspace
+    float *logits, *gate, *zg, *zu, *gs, *us;
+    int32_t *idx, *offs, *perm, *uniq, *nuniq;
+    float* wts;
+    uint16_t *h, *hs;
+    float *o, *os;
+    int32_t* idx_out;
+    float* w_out;
+};
+
+
+struct XsideGrid {
+    int nb_router, nb_gate, nb_shared, nb_z;
+};
+
+__host__ __device__ inline XsideGrid xside_grid(int T, int H, int E, int SI, int zjobs) {
+    XsideGrid g;
+    const int r8 = 4 * (64 / lanes_per_row(H));  // rows per block, 8-bit and 4-bit alike
+    g.nb_router = (E + r8 - 1) / r8;
+    g.nb_gate = 1;
+    g.nb_shared = (2 * SI + r8 - 1) / r8;
+    g.nb_z = (zjobs + 3) / 4;
+    return g;
+}
+
+
+// Kernel arguments live in per-launch memory that no cache holds yet, so every scalar load
+// batch of argument fields is a full memory round trip.  Consuming the fields a kernel
+// needs in one empty asm at entry makes the compiler issue all those loads together (one
+// round trip) instead of in dependent batches spread over the kernel.
+#define QMOE_SGPR_USE2(x, y) asm volatile("" ::"s"(x), "s"(y))
+#define QMOE_SGPR_USE4(x, y, z, w) asm volatile("" ::"s"(x), "s"(y), "s"(z), "s"(w))
+
+namespace {
+
+// LoRA z for tokens rows[0..mt): z[i][r] = A[a][r] . src[rows[i]] (K inputs), one wave per
+// (i, r).  Written to LDS zl[i * MAX_RANK + r].
+__device__ void lora_z_lds(const uint16_t* __restrict__ src, const int* rows, const int* toks,
+                           int mt, int K, const uint16_t* __restrict__ A, int rank,
+                           const int32_t* __restrict__ adapter, int n_ad, float* zl) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    for (int p = wave; p < mt * rank; p += nw) {
+        const int i = p / rank, r = p % rank;
+        const int a = adapter_of(adapter, toks[i], n_ad);
+        const uint16_t* arow = A + ((long)a * rank + r) * K;
+        const uint16_t* xrow = src + (long)rows[i] * K;
+        float acc = 0.0f;
+        for (int k = lane * 8; k < K; k += 512) {
+            const uint4 av = *reinterpret_cast<const uint4*>(arow + k);
+            const uint4 xv = *reinterpret_cast<const uint4*>(xrow + k);
+            const f16x2* ah = reinterpret_cast<const f16x2*>(&av);
+            const f16x2* xh = reinterpret_cast<const f16x2*>(&xv);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_fdot2(ah[j], xh[j], acc, false);
+        }
+        acc = seg_sum<64>(acc);
+        if (lane == 0) zl[i * MAX_RANK + r] = acc;
+    }
+}
+
+// scale-free LoRA up-projection of one output: sum_r B[a][n][r] * z[r].  Rank rows of a
+// multiple of 8 are read with 16-byte loads, all issued before the sum.
+__device__ __forceinline__ float lora_b_dot(const uint16_t* __restrict__ B, int a, int out_dim,
+                                            int n, int rank, const float* z) {
+    const uint16_t* brow = B + ((long)a * out_dim + n) * rank;
+    float d = 0.0f;
+    if ((rank & 7) == 0) {
+        uint4 v[MAX_RANK / 8];
+#pragma unroll
+        for (int i = 0; i < MAX_RANK / 8; ++i)
+            if (i < rank / 8) v[i] = *reinterpret_cast<const uint4*>(brow + i * 8);
+#pragma unroll
+        for (int i = 0; i < MAX_RANK / 8; ++i) {
+            if (i < rank / 8) {
+                const f16* h = reinterpret_cast<const f16*>(&v[i]);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) d = fmaf((float)h[j], z[i * 8 + j], d);
+            }
+        }
+        return d;
+    }
+    for (int r = 0; r < rank; ++r) d = fmaf(h2f(brow[r]), z[r], d);
+    return d;
+}
+
+
+// z[r] = A[r] . v for r < rank (A fp16 [rank][K] row-major, v fp16 [K]), whole block: one
+// 16-lane DPP row per rank row, each lane a K/16 slice (K a multiple of 128), so all loads
+// of the block are in flight together.  Writes z (LDS); the caller synchronises.
+__device__ inline void lora_rows16(const uint16_t* __restrict__ A, int rank,
+                                   const uint16_t* __restrict__ v, int K, float* z) {
+    const int lane16 = threadIdx.x & 15, row0 = threadIdx.x >> 4, nrows = blockDim.x >> 4;
+    const int per = K / 16;                 // inputs per lane (a multiple of 8)
+    constexpr int MAXI = 16;                // K <= 2048
+    for (int r = row0; r < rank; r += nrows) {
+        const uint16_t* arow = A + (long)r * K + lane16 * per;
+        const uint16_t* vrow = v + lane16 * per;
+        uint4 av[MAXI], xv[MAXI];
+#pragma unroll
+        for (int i = 0; i < MAXI; ++i) {
+            if (i * 8 < per) {
+                av[i] = *reinterpret_cast<const uint4*>(arow + i * 8);
+                xv[i] = *reinterpret_cast<const uint4*>(vrow + i * 8);
+            }
+        }
+        float acc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < MAXI; ++i) {
+            if (i * 8 < per) {
+                const f16x2* ah = reinterpret_cast<const f16x2*>(&av[i]);
+                const f16x2* xh = reinterpret_cast<const f16x2*>(&xv[i]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_fdot2(ah[q], xh[q], acc, false);
+            }
+        }
+        acc = seg_sum<16>(acc);
+        if (lane16 == 0) z[r] = acc;
+    }
+}
+
+// One LoRA down-projection dot of the x-side kernels: job j = (projection, token, rank row).
+__device__ inline void xside_lora_z(const MoeArgs& a, int j, int zjobs) {
+    const int lane = threadIdx.x & 63;
+    if (j >= zjobs) return;
+    const int H = a.H;
+    const int ng = a.Ag ? a.T * a.rg : 0;
+    const bool isg = j < ng;
+    const int jj = isg ? j : j - ng;
+    const int rank = isg ? a.rg : a.ru;
+    const int t = jj / rank, r = jj % rank;
+    const int ad = adapter_of(a.adapter, t, isg ? a.nag : a.nau);
+    const uint16_t* arow = (isg ? a.Ag : a.Au) + ((long)ad * rank + r) * H;
+    const uint16_t* xrow = a.x + (long)t * H;
+    constexpr int MAXI = 8;                       // hidden <= 4096: 8 x 512 inputs
+    uint4 av[MAXI], xv[MAXI];
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) {
+        const int k = lane * 8 + i * 512;
+        if (k < H) {
+            av[i] = *reinterpret_cast<const uint4*>(arow + k);
+            xv[i] = *reinterpret_cast<const uint4*>(xrow + k);
+        }
+    }
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) {
+        if (lane * 8 + i * 512 < H) {
+            const f16x2* ah = reinterpret_cast<const f16x2*>(&av[i]);
+            const f16x2* xh = reinterpret_cast<const f16x2*>(&xv[i]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_fdot2(ah[q], xh[q], acc, false);
+        }
+    }
+    acc = seg_sum<64>(acc);
+    if (lane == 0) (isg ? a.zg : a.zu)[t * MAX_RANK + r] = acc;
+}
+
+}  // namespace
+
+// moe_decode.hip
+bool decode_path_fits(const qmoe_moe_layer& L, int T);
+hipError_t launch_moe_decode(const MoeArgs& a, int stage, hipStream_t s);
+
+}  // namespace qmoe

@@ -8,59 +8,29 @@
 // highlight 2).
 #include "device.hpp"
 #include "launch.hpp"
+#include "topk.hpp"
 
 namespace qmoe {
 
 namespace {
 
-constexpr int MAX_PER_LANE = 16;  // e <= 1024
 constexpr int MAX_K = 32;
 
-// One wave per token.  Lane l holds logits l, l+64, ...; K rounds of a wave-wide argmax
-// (ties to the lower index), each removing the winner.
+// One wave per token; lane 0 writes the selection.
 __global__ void __launch_bounds__(256) k_router_topk(const float* __restrict__ logits, int t, int e,
                                                      int k, const float* __restrict__ bias,
                                                      int32_t* __restrict__ idx,
                                                      float* __restrict__ wout) {
-    const int lane = threadIdx.x & 63;
-    const int tok = blockIdx.x * 4 + (threadIdx.x >> 6);
+    __shared__ int sel[4][MAX_K];
+    __shared__ float sw[4][MAX_K];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tok = blockIdx.x * 4 + wave;
     if (tok >= t) return;
-    float v[MAX_PER_LANE];
-    uint32_t live = 0;
-#pragma unroll
-    for (int i = 0; i < MAX_PER_LANE; ++i) {
-        const int ei = lane + 64 * i;
-        v[i] = 0.0f;
-        if (ei < e) {
-            v[i] = logits[(long)tok * e + ei] + (bias ? bias[ei] : 0.0f);
-            live |= 1u << i;
-        }
-    }
-    float sv[MAX_K];
-    int si[MAX_K];
-    for (int r = 0; r < k; ++r) {
-        float bv = 0.0f;
-        int bi = -1;
-#pragma unroll
-        for (int i = 0; i < MAX_PER_LANE; ++i)
-            if (((live >> i) & 1u) && (bi < 0 || v[i] > bv)) { bv = v[i]; bi = lane + 64 * i; }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const float ov = __shfl_xor(bv, off, 64);
-            const int oi = __shfl_xor(bi, off, 64);
-            if (oi >= 0 && (bi < 0 || ov > bv || (ov == bv && oi < bi))) { bv = ov; bi = oi; }
-        }
-        if ((bi & 63) == lane) live &= ~(1u << (bi >> 6));
-        sv[r] = bv;
-        si[r] = bi;
-    }
+    wave_topk(logits + (long)tok * e, bias, e, k, sel[wave], sw[wave]);
     if (lane == 0) {
-        const float m = sv[0];
-        float sum = 0.0f;
-        for (int r = 0; r < k; ++r) { sv[r] = expf(sv[r] - m); sum += sv[r]; }
         for (int r = 0; r < k; ++r) {
-            idx[(long)tok * k + r] = si[r];
-            wout[(long)tok * k + r] = sv[r] / sum;
+            idx[(long)tok * k + r] = sel[wave][r];
+            wout[(long)tok * k + r] = sw[wave][r];
         }
     }
 }
