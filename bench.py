@@ -209,6 +209,109 @@ def bench_moe_decode(args, q, torch):
     return res, cpu_baseline_moe_decode
 
 
+def cpu_baseline_moe_prefill(n_tokens=64, budget_s=20.0):
+    """The oracle (float64 numpy) on a bounded sample: batches of 16 prefill tokens through
+    one seeded layer of the same shapes (every expert the sample reaches is quantized)."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import synth
+    from layers import Shape, build_layer, routed_experts
+    from oracle import moe
+    from threadpoolctl import threadpool_info
+
+    S = Shape(top_k=4)
+    wl = synth.Workload.MOE_PREFILL
+    xs = synth.activations(n_tokens, H, wl, 0, 99)
+    L = build_layer(wl, 0, S, only_experts=routed_experts(xs, wl, 0, S, margin=0))
+    t0 = time.perf_counter()
+    done = 0
+    for i in range(0, n_tokens, 16):
+        moe.moe_layer(xs[i:i + 16], L)
+        done += 16
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    blas = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+    cores = max(blas) if blas else 1
+    return {"value": done / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} prefill tokens in batches of 16 through one layer (hidden 2048, "
+                      f"256 experts, top-4, shared expert, LoRA r16), float64 numpy, {dt:.1f} s"}
+
+
+def bench_moe_prefill(args, q, torch):
+    """512 tokens per step through one layer; 8 seeded layers rotated (3.6 GB of experts)."""
+    T, NL, NX = 512, 8, 8
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4321)
+    t0 = time.perf_counter()
+    layers = [make_layer(q, torch, gen, skew=args.skew) for _ in range(NL)]
+    xs = torch.randn((NX, T, H), generator=gen, device="cuda").half()
+    ys = torch.empty_like(xs)
+    ws_bytes = q.moe_workspace_bytes(layers[0], T)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    log(f"built {NL} layers in {time.perf_counter() - t0:.1f} s; workspace {ws_bytes / 2**20:.1f} MiB")
+    K, W = args.steps, args.warmup
+    calls = [q.MoECall(layers[i % NL], xs[i % NX], ys[i % NX], ws) for i in range(K + W)]
+
+    def run(lo, hi):
+        def f():
+            for i in range(lo, hi):
+                calls[i]()
+        return f
+    if W:
+        graph_of(torch, run(K, K + W)).replay()
+    g_main = graph_of(torch, run(0, K))
+    ms_total = time_graph(torch, g_main)
+    ms_step = ms_total / K
+    log(f"main: {K} steps in {ms_total:.3f} ms")
+
+    # stages over NL routed workspaces (one per layer, distinct inputs)
+    wss = torch.empty((NL, ws_bytes), dtype=torch.uint8, device="cuda")
+    idx = torch.empty((NL, T, 4), dtype=torch.int32, device="cuda")
+    scalls = [q.MoECall(layers[i], xs[i % NX], ys[i % NX], wss[i], idx_out=idx[i]) for i in range(NL)]
+    for c in scalls:
+        c(q.STAGE_ROUTE)
+    torch.cuda.synchronize()
+    stage_us = {}
+    for name, st in (("route", q.STAGE_ROUTE), ("gate_up", q.STAGE_GATE_UP), ("down", q.STAGE_DOWN)):
+        def f(st=st):
+            for c in scalls:
+                c(st)
+        stage_us[name] = time_graph(torch, graph_of(torch, f), reps=5) / NL * 1e3
+    ih = idx.cpu().numpy()
+    used = np.mean([len(np.unique(ih[i])) for i in range(NL)])
+    pairs = T * 4
+    gu_bytes = used * 2 * MAT_BYTES_4BIT(I, H) + T * H * 2 + pairs * I * 2
+    gu_flops = 2 * 2 * pairs * I * H
+    us = stage_us["gate_up"]
+    achieved = gu_bytes / (us * 1e-6) / 1e9
+    tflops = gu_flops / (us * 1e-6) / 1e12
+    step_bytes = (MAT_BYTES_8BIT(E, H) + MAT_BYTES_8BIT(1, H) + used * 3 * MAT_BYTES_4BIT(I, H)
+                  + 3 * MAT_BYTES_4BIT(SI, H) + 3 * RANK * (H + SI) * 2 + 2 * T * H * 2)
+    step_flops = 2 * T * (E * H + H + 3 * SI * H + 4 * 3 * I * H)
+    res = {
+        "metric": "int4 MoE layer tokens/s (prefill, 512 tokens per step)",
+        "value": T * K / (ms_total * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": W, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "moe_switchglu_int4 prefill: 512 tokens/step, hidden 2048, 256 "
+                               "experts int4 g64, top-4, shared expert + 8-bit gate, LoRA r16 "
+                               "a32, 8 independently seeded layers rotated"
+                               + (", logits +2.0 on experts 0..15" if args.skew else ""),
+                   "global_batch": T, "experts_used_per_layer": used,
+                   "step_algorithmic_bytes": step_bytes,
+                   "step_hbm_gbps": step_bytes / (ms_step * 1e-3) / 1e9,
+                   "step_mfma_tflops": step_flops / (ms_step * 1e-3) / 1e12,
+                   "stage_us": stage_us},
+        "roofline": {"kernel": "k_pf_gemm grouped gate/up (silu*up epilogue)",
+                     "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "bytes_per_launch": gu_bytes, "us_per_launch": us,
+                     "mfma_tflops": tflops, "mfma_frac": tflops / FP16_MFMA_PEAK_TFLOPS},
+    }
+    return res, cpu_baseline_moe_prefill
+
+
 def bench_gemv(args, q, torch):
     gen = torch.Generator(device="cuda")
     gen.manual_seed(1234)
@@ -247,7 +350,7 @@ def bench_gemv(args, q, torch):
     return res, None
 
 
-WORKLOADS = {"moe_decode": bench_moe_decode, "gemv": bench_gemv}
+WORKLOADS = {"moe_decode": bench_moe_decode, "moe_prefill": bench_moe_prefill, "gemv": bench_gemv}
 
 
 def main():
@@ -256,6 +359,7 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="moe_decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--skew", action="store_true", help="moe_prefill: +2.0 on experts 0..15")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:

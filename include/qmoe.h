@@ -224,8 +224,9 @@ int moe_switchglu_int4(const qmoe_moe_layer* L, const uint16_t* x, int32_t t,
  *   QMOE_STAGE_ROUTE   (1): router and shared-gate logits, the shared expert's raw gate/up
  *                           projections, LoRA down-projections of x, top-K + softmax and the
  *                           sort of (token, k) pairs by expert (writes idx_out / w_out);
- *   QMOE_STAGE_GATE_UP (2): h = silu(gate x) * (up x) for every routed pair and for the
- *                           shared expert (LoRA up-projections added);
+ *                           above 32 tokens also the shared expert's h (below);
+ *   QMOE_STAGE_GATE_UP (2): h = silu(gate x) * (up x) for every routed pair; up to 32 tokens
+ *                           also for the shared expert (LoRA up-projections added);
  *   QMOE_STAGE_DOWN    (3): down projections, LoRA down delta, routing-weighted combine and
  *                           the gated shared expert, y written.
  * Stage s reads what stages < s left in `ws` for the same x, t and adapter_idx; running the

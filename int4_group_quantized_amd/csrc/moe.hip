@@ -11,19 +11,12 @@
 // highlight 2 and MoE spec); the recovery LoRA as a parallel, never-merged delta
 // ("Recover-LoRA ..." section 2).
 //
-// Launch sequence on the caller's stream (no host synchronisation anywhere):
-//   1. x-side:   router logits (8-bit), shared-gate logit (8-bit), the shared expert's raw
-//                gate/up projections (int4) and the LoRA down-projections z = A x.
-//   2. route:    top-K + renormalized softmax per token, then a stable counting sort of
-//                the (token, k) pairs by expert: offsets, pair order, used-expert list.
-//   3. gate/up:  per used expert and row block, a gather-GEMV of the expert's gate and up
-//                rows against the tokens routed to it, h = silu(g) * u (fp16); the shared
-//                expert's h adds the LoRA up-projections B z to its raw g and u first.
-//   4. down:     per used expert and row block, o = h W_down^T (fp32); the shared expert
-//                also adds its down LoRA delta.
-//   5. combine:  y = fp16(sum_k w_k o_k + sigmoid(gate) o_shared) (+ residual).
-// Every reduction has a fixed order; there are no atomics outside the LDS counters of
-// the sort, whose totals do not depend on the order of the increments.
+// Two launch sequences on the caller's stream, neither with a host synchronisation:
+//   decode (moe_decode.hip, up to 32 tokens): three launches, top-K once per token inside
+//     the gate/up kernel;
+//   prefill (moe_prefill.hip, any count): router / shared-expert GEMMs on MFMA, top-K, a
+//     stable sort of the (token, k) pairs by expert, grouped expert GEMMs, combine.
+// This file owns the workspace layout and the choice between the two.
 #include <algorithm>
 
 #include "gemv_core.hpp"
@@ -34,11 +27,9 @@ namespace qmoe {
 
 namespace {
 
-constexpr int MT = GEMV_MT;
-constexpr int ROUTE_THREADS = 1024;
-
 struct Layout {
-    size_t logits, gate, zg, zu, gs, us, idx, wts, offs, perm, uniq, nuniq, h, hs, o, os, total;
+    size_t logits, gate, zg, zu, zd, gs, us, idx, wts, offs, perm, wrec, wpairs, h, hs, o, os,
+        total;
 };
 
 size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -52,307 +43,22 @@ Layout layout_of(const qmoe_moe_layer& L, int T) {
     l.gate = take((size_t)T * 4);
     l.zg = take((size_t)T * MAX_RANK * 4);
     l.zu = take((size_t)T * MAX_RANK * 4);
+    l.zd = take((size_t)T * MAX_RANK * 4);
     l.gs = take((size_t)T * L.shared_inter * 4);
     l.us = take((size_t)T * L.shared_inter * 4);
     l.idx = take(TK * 4);
     l.wts = take(TK * 4);
     l.offs = take((size_t)(L.n_experts + 1) * 4);
     l.perm = take(TK * 4);
-    l.uniq = take((size_t)L.n_experts * 4);
-    l.nuniq = take(4);
+    const size_t items = (size_t)prefill_max_items(L.n_experts, T, L.top_k);
+    l.wrec = take(items * 16);
+    l.wpairs = take(items * PF_ITEM * 4);
     l.h = take(TK * L.inter * 2);
     l.hs = take((size_t)T * L.shared_inter * 2);
     l.o = take(TK * L.hidden * 4);
     l.os = take((size_t)T * L.hidden * 4);
     l.total = off;
     return l;
-}
-
-// ------------------------------------------------------------------------------ 1. x-side
-
-__global__ void __launch_bounds__(256) k_moe_xside(MoeArgs a) {
-    __shared__ __align__(16) f16x2 xs[8192];  // 32 KB: tokens per pass = 8192 / (K/2)
-    __shared__ float xsum[MT * 128];
-    __shared__ int rows[MT];
-    const int H = a.H;
-    const int zjobs = (a.Ag ? a.T * a.rg : 0) + (a.Au ? a.T * a.ru : 0);
-    const XsideGrid g = xside_grid(a.T, H, a.E, a.SI, zjobs);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int lpr = lanes_per_row(H), rpw = 64 / lpr, seg = lane / lpr, sl = lane % lpr;
-    int b = blockIdx.x;
-
-    if (b >= g.nb_router + g.nb_gate + g.nb_shared) {  // LoRA z jobs: one wave per dot
-        xside_lora_z(a, (b - g.nb_router - g.nb_gate - g.nb_shared) * 4 + wave, zjobs);
-        return;
-    }
-
-    const int mt_max = min(MT, (int)(sizeof(xs) / (H * 2)));
-    const bool eight = b < g.nb_router + g.nb_gate;
-    for (int t0 = 0; t0 < a.T; t0 += mt_max) {
-        const int mt = min(mt_max, a.T - t0);
-        __syncthreads();
-        if (threadIdx.x < MT) rows[threadIdx.x] = t0 + threadIdx.x;
-        __syncthreads();
-        if (eight) stage_tokens<8>(a.x, rows, mt, H, xs, xsum);
-        else stage_tokens<4>(a.x, rows, mt, H, xs, xsum);
-        __syncthreads();
-        float acc[MT];
-#pragma unroll
-        for (int t = 0; t < MT; ++t) acc[t] = 0.0f;
-        int row;
-        float* out;
-        int ostride;
-        if (b < g.nb_router) {
-            row = (b * 4 + wave) * rpw + seg;
-            if (row < a.E) qdot_row<8>(a.router.p, a.router.s, a.router.b, H, row, lpr, sl, xs, xsum, mt, acc);
-            out = a.logits + row;
-            ostride = a.Ep;
-            if (row >= a.E) row = -1;
-        } else if (b < g.nb_router + g.nb_gate) {
-            row = (wave == 0 && seg == 0) ? 0 : -1;
-            if (row == 0) qdot_row<8>(a.sgate.p, a.sgate.s, a.sgate.b, H, 0, lpr, sl, xs, xsum, mt, acc);
-            out = a.gate;
-            ostride = 1;
-        } else {
-            const int r = ((b - g.nb_router - g.nb_gate) * 4 + wave) * rpw + seg;  // in [0, 2 SI)
-            row = r < 2 * a.SI ? r : -1;
-            const bool up = r >= a.SI;
-            const int n = up ? r - a.SI : r;
-            const QW& w = up ? a.shu : a.shg;
-            if (row >= 0) qdot_row<4>(w.p, w.s, w.b, H, n, lpr, sl, xs, xsum, mt, acc);
-            out = (up ? a.us : a.gs) + n;
-            ostride = a.SI;
-        }
-#pragma unroll
-        for (int t = 0; t < MT; ++t) {
-            if (t < mt) {
-                const float v = segment_sum(acc[t], lpr);
-                if (sl == 0 && row >= 0) out[(long)(t0 + t) * ostride] = v;
-            }
-        }
-    }
-}
-
-// ------------------------------------------------------------------------------ 2. route
-
-__global__ void __launch_bounds__(ROUTE_THREADS) k_moe_route(MoeArgs a) {
-    __shared__ int cnt[1024];
-    __shared__ int scan[1024];
-    __shared__ int fill[1024];
-    __shared__ int chunk_e[ROUTE_THREADS];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = ROUTE_THREADS / 64;
-    const int K = a.K, E = a.E, TK = a.T * a.K;
-
-    __shared__ int wsel[ROUTE_THREADS / 64][MAX_K];
-    __shared__ float wsw[ROUTE_THREADS / 64][MAX_K];
-    for (int t = wave; t < a.T; t += nw) {
-        wave_topk(a.logits + (long)t * a.Ep, a.rbias, E, K, wsel[wave], wsw[wave]);
-        if (lane == 0) {
-            for (int r = 0; r < K; ++r) {
-                const int sel = wsel[wave][r];
-                const float wv = wsw[wave][r];
-                a.idx[(long)t * K + r] = sel;
-                a.wts[(long)t * K + r] = wv;
-                if (a.idx_out) a.idx_out[(long)t * K + r] = sel;
-                if (a.w_out) a.w_out[(long)t * K + r] = wv;
-            }
-        }
-    }
-    for (int e = tid; e < 1024; e += ROUTE_THREADS) { cnt[e] = 0; fill[e] = 0; }
-    __threadfence();
-    __syncthreads();
-    for (int p = tid; p < TK; p += ROUTE_THREADS) atomicAdd(&cnt[a.idx[p]], 1);
-    __syncthreads();
-    // exclusive scan of the counts (Hillis-Steele over 1024 slots) and of the used flags
-    int c = tid < E ? cnt[tid] : 0;
-    int f = c > 0 ? 1 : 0;
-    scan[tid] = c;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-        const int v = tid >= off ? scan[tid - off] : 0;
-        __syncthreads();
-        scan[tid] += v;
-        __syncthreads();
-    }
-    const int excl = scan[tid] - c;
-    __syncthreads();
-    scan[tid] = f;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-        const int v = tid >= off ? scan[tid - off] : 0;
-        __syncthreads();
-        scan[tid] += v;
-        __syncthreads();
-    }
-    if (tid < E) {
-        a.offs[tid] = excl;
-        if (f) a.uniq[scan[tid] - 1] = tid;
-    }
-    if (tid == E - 1) { a.offs[E] = excl + c; *a.nuniq = scan[tid]; }
-    cnt[tid] = excl;  // reuse as the bucket starts
-    __syncthreads();
-    // stable scatter, one chunk of pairs at a time
-    for (int base = 0; base < TK; base += ROUTE_THREADS) {
-        const int p = base + tid;
-        const int e = p < TK ? a.idx[p] : -1;
-        chunk_e[tid] = e;
-        __syncthreads();
-        if (e >= 0) {
-            int rank = 0;
-            for (int q = 0; q < tid; ++q) rank += (chunk_e[q] == e);
-            a.perm[cnt[e] + fill[e] + rank] = p;
-        }
-        __syncthreads();
-        if (e >= 0) atomicAdd(&fill[e], 1);
-        __syncthreads();
-    }
-}
-
-// ------------------------------------------------------------------------------ 3. gate/up
-
-__global__ void __launch_bounds__(256) k_moe_gate_up(MoeArgs a) {
-    __shared__ __align__(16) f16x2 xs[8192];
-    __shared__ float xsum[MT * 128];
-    __shared__ int rows[MT], pairs[MT];
-    const int H = a.H, I = a.I;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int lpr = lanes_per_row(H), rpw = 64 / lpr, seg = lane / lpr, sl = lane % lpr;
-    const int R = 4 * rpw;  // rows per block
-    const int slot = blockIdx.y;
-
-    if (slot == a.max_slots) {  // shared expert: add the LoRA up-projections, then silu * up
-        const int n0 = blockIdx.x * R;
-        for (int it = threadIdx.x; it < R * a.T; it += blockDim.x) {
-            const int n = n0 + it % R, t = it / R;
-            if (n >= a.SI) continue;
-            float gv = a.gs[(long)t * a.SI + n];
-            float uv = a.us[(long)t * a.SI + n];
-            if (a.Bg) gv = fmaf(a.lsg, lora_b_dot(a.Bg, adapter_of(a.adapter, t, a.nag), a.SI, n, a.rg, a.zg + t * MAX_RANK), gv);
-            if (a.Bu) uv = fmaf(a.lsu, lora_b_dot(a.Bu, adapter_of(a.adapter, t, a.nau), a.SI, n, a.ru, a.zu + t * MAX_RANK), uv);
-            a.hs[(long)t * a.SI + n] = f2h(silu(gv) * uv);
-        }
-        return;
-    }
-    if (slot >= *a.nuniq) return;
-    const int e = a.uniq[slot];
-    const int p0 = a.offs[e], p1 = a.offs[e + 1];
-    const int n = (blockIdx.x * 4 + wave) * rpw + seg;
-    if (blockIdx.x * R >= I) return;
-    const long ew = (long)e * I;  // first row of expert e in the stacked matrices
-    const int mt_max = min(MT, (int)(sizeof(xs) / (H * 2)));
-    for (int q0 = p0; q0 < p1; q0 += mt_max) {
-        const int mt = min(mt_max, p1 - q0);
-        __syncthreads();
-        if (threadIdx.x < mt) {
-            const int p = a.perm[q0 + threadIdx.x];
-            pairs[threadIdx.x] = p;
-            rows[threadIdx.x] = p / a.K;
-        }
-        __syncthreads();
-        stage_tokens<4>(a.x, rows, mt, H, xs, xsum);
-        __syncthreads();
-        float ag[MT], au[MT];
-#pragma unroll
-        for (int t = 0; t < MT; ++t) { ag[t] = 0.0f; au[t] = 0.0f; }
-        if (n < I) {
-            qdot_row<4>(a.eg.p, a.eg.s, a.eg.b, H, ew + n, lpr, sl, xs, xsum, mt, ag);
-            qdot_row<4>(a.eu.p, a.eu.s, a.eu.b, H, ew + n, lpr, sl, xs, xsum, mt, au);
-        }
-#pragma unroll
-        for (int t = 0; t < MT; ++t) {
-            if (t < mt) {
-                const float gv = segment_sum(ag[t], lpr);
-                const float uv = segment_sum(au[t], lpr);
-                if (sl == 0 && n < I) a.h[(long)pairs[t] * I + n] = f2h(silu(gv) * uv);
-            }
-        }
-    }
-}
-
-// ------------------------------------------------------------------------------ 4. down
-
-__global__ void __launch_bounds__(256) k_moe_down(MoeArgs a) {
-    __shared__ __align__(16) f16x2 xs[8192];
-    __shared__ float xsum[MT * 128];
-    __shared__ float zl[MT * MAX_RANK];
-    __shared__ int rows[MT], toks[MT];
-    const int H = a.H;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int slot = blockIdx.y;
-    const bool shared = slot == a.max_slots;
-    const int Kd = shared ? a.SI : a.I;
-    const int lpr = lanes_per_row(Kd), rpw = 64 / lpr, seg = lane / lpr, sl = lane % lpr;
-    const int R = 4 * rpw;
-    const int n = blockIdx.x * R + wave * rpw + seg;
-    if (blockIdx.x * R >= H) return;
-    const int mt_max = min(MT, (int)(sizeof(xs) / (Kd * 2)));
-
-    if (shared) {
-        for (int t0 = 0; t0 < a.T; t0 += mt_max) {
-            const int mt = min(mt_max, a.T - t0);
-            __syncthreads();
-            if (threadIdx.x < mt) { rows[threadIdx.x] = t0 + threadIdx.x; toks[threadIdx.x] = t0 + threadIdx.x; }
-            __syncthreads();
-            stage_tokens<4>(a.hs, rows, mt, Kd, xs, xsum);
-            if (a.Ad) lora_z_lds(a.hs, rows, toks, mt, Kd, a.Ad, a.rd, a.adapter, a.nad, zl);
-            __syncthreads();
-            float acc[MT];
-#pragma unroll
-            for (int t = 0; t < MT; ++t) acc[t] = 0.0f;
-            if (n < H) qdot_row<4>(a.shd.p, a.shd.s, a.shd.b, Kd, n, lpr, sl, xs, xsum, mt, acc);
-#pragma unroll
-            for (int t = 0; t < MT; ++t) {
-                if (t < mt) {
-                    float v = segment_sum(acc[t], lpr);
-                    if (sl == 0 && n < H) {
-                        if (a.Bd) {
-                            const int ad = adapter_of(a.adapter, t0 + t, a.nad);
-                            v = fmaf(a.lsd, lora_b_dot(a.Bd, ad, H, n, a.rd, zl + t * MAX_RANK), v);
-                        }
-                        a.os[(long)(t0 + t) * H + n] = v;
-                    }
-                }
-            }
-        }
-        return;
-    }
-    if (slot >= *a.nuniq) return;
-    const int e = a.uniq[slot];
-    const int p0 = a.offs[e], p1 = a.offs[e + 1];
-    const long ew = (long)e * H;
-    for (int q0 = p0; q0 < p1; q0 += mt_max) {
-        const int mt = min(mt_max, p1 - q0);
-        __syncthreads();
-        if (threadIdx.x < mt) rows[threadIdx.x] = a.perm[q0 + threadIdx.x];  // pair ids index h
-        __syncthreads();
-        stage_tokens<4>(a.h, rows, mt, Kd, xs, xsum);
-        __syncthreads();
-        float acc[MT];
-#pragma unroll
-        for (int t = 0; t < MT; ++t) acc[t] = 0.0f;
-        if (n < H) qdot_row<4>(a.ed.p, a.ed.s, a.ed.b, Kd, ew + n, lpr, sl, xs, xsum, mt, acc);
-#pragma unroll
-        for (int t = 0; t < MT; ++t) {
-            if (t < mt) {
-                const float v = segment_sum(acc[t], lpr);
-                if (sl == 0 && n < H) a.o[(long)rows[t] * H + n] = v;
-            }
-        }
-    }
-}
-
-// ------------------------------------------------------------------------------ 5. combine
-
-__global__ void __launch_bounds__(256) k_moe_combine(MoeArgs a) {
-    const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= (long)a.T * a.H) return;
-    const int t = (int)(i / a.H), n = (int)(i % a.H);
-    float acc = 0.0f;
-    for (int k = 0; k < a.K; ++k) acc = fmaf(a.wts[(long)t * a.K + k], a.o[((long)t * a.K + k) * a.H + n], acc);
-    acc = fmaf(sigmoid(a.gate[t]), a.os[i], acc);
-    uint16_t out = f2h(acc);
-    if (a.add_residual) out = f2h(h2f(a.x[i]) + h2f(out));
-    a.y[i] = out;
 }
 
 }  // namespace
@@ -370,7 +76,6 @@ hipError_t launch_moe(const qmoe_moe_layer& L, int stage, const uint16_t* x, int
     a.T = T; a.H = L.hidden; a.I = L.inter; a.SI = L.shared_inter; a.E = L.n_experts;
     a.K = L.top_k; a.add_residual = L.add_residual;
     a.Ep = (L.n_experts + 63) / 64 * 64;
-    a.max_slots = std::min(T * L.top_k, L.n_experts);
     a.x = x; a.y = y; a.adapter = adapter_idx;
     auto qw = [](const qmoe_qweight& w) { return QW{w.packed, w.scales, w.biases}; };
     a.router = qw(L.router); a.sgate = qw(L.shared_gate);
@@ -384,14 +89,15 @@ hipError_t launch_moe(const qmoe_moe_layer& L, int stage, const uint16_t* x, int
     a.gate = reinterpret_cast<float*>(base + lo.gate);
     a.zg = reinterpret_cast<float*>(base + lo.zg);
     a.zu = reinterpret_cast<float*>(base + lo.zu);
+    a.zd = reinterpret_cast<float*>(base + lo.zd);
     a.gs = reinterpret_cast<float*>(base + lo.gs);
     a.us = reinterpret_cast<float*>(base + lo.us);
     a.idx = reinterpret_cast<int32_t*>(base + lo.idx);
     a.wts = reinterpret_cast<float*>(base + lo.wts);
     a.offs = reinterpret_cast<int32_t*>(base + lo.offs);
     a.perm = reinterpret_cast<int32_t*>(base + lo.perm);
-    a.uniq = reinterpret_cast<int32_t*>(base + lo.uniq);
-    a.nuniq = reinterpret_cast<int32_t*>(base + lo.nuniq);
+    a.wrec = reinterpret_cast<int32_t*>(base + lo.wrec);
+    a.wpairs = reinterpret_cast<int32_t*>(base + lo.wpairs);
     a.h = reinterpret_cast<uint16_t*>(base + lo.h);
     a.hs = reinterpret_cast<uint16_t*>(base + lo.hs);
     a.o = reinterpret_cast<float*>(base + lo.o);
@@ -399,27 +105,7 @@ hipError_t launch_moe(const qmoe_moe_layer& L, int stage, const uint16_t* x, int
     a.idx_out = idx_out;
     a.w_out = w_out;
     if (decode_path_fits(L, T)) return launch_moe_decode(a, stage, s);
-
-    const int zjobs = (a.Ag ? T * a.rg : 0) + (a.Au ? T * a.ru : 0);
-    const XsideGrid g = xside_grid(T, a.H, a.E, a.SI, zjobs);
-    if (stage == QMOE_STAGE_ALL || stage == QMOE_STAGE_ROUTE) {
-        k_moe_xside<<<g.nb_router + g.nb_gate + g.nb_shared + g.nb_z, 256, 0, s>>>(a);
-        k_moe_route<<<1, ROUTE_THREADS, 0, s>>>(a);
-    }
-    if (stage == QMOE_STAGE_ALL || stage == QMOE_STAGE_GATE_UP) {
-        const int R = 4 * (64 / lanes_per_row(a.H));
-        dim3 grid((unsigned)((std::max(a.I, a.SI) + R - 1) / R), (unsigned)(a.max_slots + 1));
-        k_moe_gate_up<<<grid, 256, 0, s>>>(a);
-    }
-    if (stage == QMOE_STAGE_ALL || stage == QMOE_STAGE_DOWN) {
-        // rows per block differ between the routed (K = inter) and shared (K = shared
-        // inter) down matrices; size the grid for the smaller, blocks past H exit
-        const int R = std::min(4 * (64 / lanes_per_row(a.I)), 4 * (64 / lanes_per_row(a.SI)));
-        dim3 grid((unsigned)((a.H + R - 1) / R), (unsigned)(a.max_slots + 1));
-        k_moe_down<<<grid, 256, 0, s>>>(a);
-        k_moe_combine<<<(unsigned)(((long)T * a.H + 255) / 256), 256, 0, s>>>(a);
-    }
-    return hipGetLastError();
+    return launch_moe_prefill(a, stage, s);
 }
 
 }  // namespace qmoe

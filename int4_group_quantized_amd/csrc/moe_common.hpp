@@ -1,6 +1,5 @@
-// Shared pieces of the two MoE layer paths (moe.hip: sorted, any token count; moe_decode.hip:
-// a few tokens): kernel arguments, the x-side job grid, top-K of one token in one wave, and
-// LoRA helpers.
+// Shared pieces of the two MoE layer paths (moe_decode.hip: a few tokens; moe_prefill.hip:
+// any token count): kernel arguments, the x-side job grid and LoRA helpers.
 #pragma once
 
 #include "gemv_core.hpp"
@@ -13,6 +12,7 @@ constexpr int MAX_RANK = 64;
 constexpr int MAX_K = 32;
 constexpr int MAX_DEC_T = 32;  // the decode path serves up to this many tokens per call
 constexpr int MAX_DEC_K = 8;   // ... and up to this many experts per token
+constexpr int PF_ITEM = 32;    // pairs per work item of the token-sorted GEMMs
 
 struct QW {
     const uint32_t* p;
@@ -21,7 +21,7 @@ struct QW {
 };
 
 struct MoeArgs {
-    int T, H, I, SI, E, K, add_residual, max_slots;
+    int T, H, I, SI, E, K, add_residual;
     int Ep;  // logits row stride: E rounded up to a multiple of 64
     const uint16_t* x;
     uint16_t* y;
@@ -33,8 +33,10 @@ struct MoeArgs {
     float lsg, lsu, lsd;
     const float* rbias;
     // workspace
-    float *logits, *gate, *zg, *zu, *gs, *us;
-    int32_t *idx, *offs, *perm, *uniq, *nuniq;
+    float *logits, *gate, *zg, *zu, *zd, *gs, *us;
+    int32_t *idx, *offs, *perm;
+    int32_t* wrec;     // per work item of the token-sorted GEMMs: (expert, tokens, 0, 0)
+    int32_t* wpairs;   // per work item: PF_ITEM pair ids, the last one repeated
     float* wts;
     uint16_t *h, *hs;
     float *o, *os;
@@ -66,31 +68,6 @@ __host__ __device__ inline XsideGrid xside_grid(int T, int H, int E, int SI, int
 #define QMOE_SGPR_USE4(x, y, z, w) asm volatile("" ::"s"(x), "s"(y), "s"(z), "s"(w))
 
 namespace {
-
-// LoRA z for tokens rows[0..mt): z[i][r] = A[a][r] . src[rows[i]] (K inputs), one wave per
-// (i, r).  Written to LDS zl[i * MAX_RANK + r].
-__device__ void lora_z_lds(const uint16_t* __restrict__ src, const int* rows, const int* toks,
-                           int mt, int K, const uint16_t* __restrict__ A, int rank,
-                           const int32_t* __restrict__ adapter, int n_ad, float* zl) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    for (int p = wave; p < mt * rank; p += nw) {
-        const int i = p / rank, r = p % rank;
-        const int a = adapter_of(adapter, toks[i], n_ad);
-        const uint16_t* arow = A + ((long)a * rank + r) * K;
-        const uint16_t* xrow = src + (long)rows[i] * K;
-        float acc = 0.0f;
-        for (int k = lane * 8; k < K; k += 512) {
-            const uint4 av = *reinterpret_cast<const uint4*>(arow + k);
-            const uint4 xv = *reinterpret_cast<const uint4*>(xrow + k);
-            const f16x2* ah = reinterpret_cast<const f16x2*>(&av);
-            const f16x2* xh = reinterpret_cast<const f16x2*>(&xv);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_fdot2(ah[j], xh[j], acc, false);
-        }
-        acc = seg_sum<64>(acc);
-        if (lane == 0) zl[i * MAX_RANK + r] = acc;
-    }
-}
 
 // scale-free LoRA up-projection of one output: sum_r B[a][n][r] * z[r].  Rank rows of a
 // multiple of 8 are read with 16-byte loads, all issued before the sum.
@@ -194,5 +171,8 @@ __device__ inline void xside_lora_z(const MoeArgs& a, int j, int zjobs) {
 // moe_decode.hip
 bool decode_path_fits(const qmoe_moe_layer& L, int T);
 hipError_t launch_moe_decode(const MoeArgs& a, int stage, hipStream_t s);
+// moe_prefill.hip
+int prefill_max_items(int E, int T, int K);
+hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s);
 
 }  // namespace qmoe

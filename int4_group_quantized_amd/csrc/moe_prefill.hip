@@ -1,0 +1,754 @@
+// Prefill path of the MoE SwitchGLU layer (many tokens per call): top-K, a stable sort of
+// the (token, k) pairs by expert, and grouped GEMMs on fp16 MFMA.
+//
+// The layer is the one of moe.hip (pages: "Edge0-35B-A3B Preview model repository guide"
+// model spec; "Recover-LoRA ..." sections 1-2; "Edge0 project review" highlights 2-3).
+// With hundreds of tokens an expert sees several of them, so each expert's weight rows
+// are read once per call and applied to all its tokens as a small GEMM on the matrix
+// cores.
+//
+// GEMM kernel (k_pf_gemm).  A block of 4 waves covers 64 output features (16 per wave) of
+// one or two quantized matrices (gate and up together) against up to 64 activation rows
+// (tokens), staged in LDS per 128-input step and double buffered.  MFMA
+// v_mfma_f32_16x16x32_f16 takes the activations as A (16 tokens x 32 inputs) and the
+// weights as B (32 inputs x 16 features): lane l supplies feature l % 16 and inputs
+// 8 (l / 16) .. +7, and ends with tokens 4 (l / 16) .. +3 of feature l % 16.
+//
+// Exactness.  The weights enter the MFMA as the exact fp16 codes C + q (C = 16 for 4-bit,
+// 256 for 8-bit: the code's bits dropped into the mantissa of C), never rounded to fp16
+// after scaling; fp16 products are exact in fp32.  Each MFMA pair covers exactly one
+// 64-input group, so the group's sum P = sum (C + q) x is formed apart, and with the
+// group's sum of inputs X (one more MFMA pair against a ones operand) the affine terms are
+// applied per group in fp32:
+//     acc += s P + (b - C s) X.
+// For that, a lane's 16-byte load of packed words (inputs 32 j .. 32 j + 31 of a 128-input
+// step, j = lane / 16, i.e. half of group j / 2) is exchanged across the wave halves with
+// v_permlane32_swap so that every register then holds words of a single group; the
+// activation side reads the matching inputs from LDS.
+#include <algorithm>
+
+#include "gemv_core.hpp"
+#include "launch.hpp"
+#include "moe_common.hpp"
+
+namespace qmoe {
+
+namespace {
+
+constexpr int PF_TOK = 64;            // tokens per block of the dense GEMMs: 4 MFMA tiles
+constexpr int PF_ROWS = 64;           // output features per block: 4 waves x 16
+constexpr int PF_KS = 128;            // inputs per k step (two groups)
+constexpr int PF_PITCH = PF_KS + 8;   // LDS row pitch in halves (272 bytes: no bank conflicts)
+
+struct PfGemm {
+    const uint32_t* p[2];
+    const uint16_t* s[2];
+    const uint16_t* b[2];
+    int N, K;                      // features per matrix (per expert), inputs
+    const uint16_t* act;           // activation rows, fp16 [*][K]
+    int T;                         // dense: token count
+    int act_div;                   // grouped: activation row = pair / act_div (1: pair itself)
+    const int32_t *wrec, *wpairs;  // grouped: work items (expert, tokens) and their pair ids
+    int nrb, items;                // row blocks, grid items (a multiple of 8)
+    float* out0; float* out1;      // fp32 outputs [row][ostride]
+    int ostride;
+    uint16_t* hout;                // fp16 silu(out0) * out1, [pair][N]
+    // one extra feature row N (dense, single matrix): read from (xp, xs, xb), written to xout[t]
+    const uint32_t* xp; const uint16_t* xs; const uint16_t* xb; float* xout;
+    // LoRA delta in the epilogue (dense, single matrix): out += lscale * B[a_t][n] . z[t]
+    const uint16_t* B; const float* z; int rank, nad; float lscale; const int32_t* adapter;
+};
+
+// GEMM flavours
+constexpr int F_GROUPED = 1;   // work items of the expert sort (else token groups of all tokens)
+constexpr int F_HOUT = 2;      // fp16 silu(out0) * out1 (else fp32 outputs)
+constexpr int F_EXTRA = 4;     // one extra feature row from a second matrix (single matrix)
+constexpr int F_LORA = 8;      // LoRA delta in the epilogue (single matrix)
+
+// LDS of one GEMM block: the activation tile (double buffer: step ks computes from ks % 2
+// while step ks + 1's tile is staged into the other), and with a compile-time step count NS
+// the block's scales and biases as (s | b << 16) dwords per (row, group), row pitch 2 NS + 4
+// dwords (16 rows read without bank conflicts).
+template <int NT, int NMAT, int NS>
+struct PfSmem {
+    f16 tile[2][16 * NT * PF_PITCH];
+    uint32_t sb[NMAT][PF_ROWS][NS ? 2 * NS + 4 : 1];
+    int arow[16 * NT], orow[16 * NT];
+};
+
+// Stage one 8-input unit of activation row r (row-major fp16) into LDS in the pair order of
+// the unpacking.
+template <int BITS>
+__device__ __forceinline__ void pf_commit(const uint4& raw, int r, int c, f16* tile) {
+    const f16* h = reinterpret_cast<const f16*>(&raw);
+    f16x2 p[4];
+    if constexpr (BITS == 4) {
+        pair_perm8(h, p);
+    } else {
+        pair_perm4(h, p);
+        pair_perm4(h + 4, p + 2);
+    }
+    *reinterpret_cast<uint4*>(tile + r * PF_PITCH + c * 8) = __builtin_bit_cast(uint4, p);
+}
+
+// fp16 codes C + q of one 8-input unit in pair order (4-bit: one word, pairs (q_j, q_j+4);
+// 8-bit: two words, pairs (b0, b2) (b1, b3)): each code shifted into mantissa bits 6..9
+// (4-bit) or 2..9 (8-bit) under the exponent of C, held in `magic` (0x4C00 = 16 or 0x5C00 =
+// 256 in both halves).  `magic` lives in a VGPR so each pair is one shift and one
+// v_and_or_b32 (gfx9 VOP3 takes no literal operand).
+template <int BITS>
+__device__ __forceinline__ f16x8 pf_codes(const uint32_t* w, uint32_t magic) {
+    uint32_t u[4];
+    if constexpr (BITS == 4) {
+        constexpr uint32_t M = 0x03C003C0u;
+        u[0] = ((w[0] << 6) & M) | magic; u[1] = ((w[0] << 2) & M) | magic;
+        u[2] = ((w[0] >> 2) & M) | magic; u[3] = ((w[0] >> 6) & M) | magic;
+    } else {
+        constexpr uint32_t M = 0x03FC03FCu;
+        u[0] = ((w[0] << 2) & M) | magic; u[1] = ((w[0] >> 6) & M) | magic;
+        u[2] = ((w[1] << 2) & M) | magic; u[3] = ((w[1] >> 6) & M) | magic;
+    }
+    return __builtin_bit_cast(f16x8, u);
+}
+
+// XCD-aware block order: blocks are handed to the 8 XCDs round-robin by linear id, so the
+// id's low 3 bits pick the XCD.  Every row block of one item (expert chunk or token group)
+// lands on the same XCD, and that XCD runs them back to back: the item's activations are
+// fetched into one L2 once.
+__device__ __forceinline__ void pf_block(int id, int nrb, int& rb, int& item) {
+    const int xcd = id & 7, q = id >> 3;
+    rb = q % nrb;
+    item = (q / nrb) * 8 + xcd;
+}
+
+// The packed words, scales and biases of one 128-input step for this lane's feature row.
+template <int NMAT, int BITS>
+struct PfSlot {
+    static constexpr int LW = BITS;   // words per lane per step: 4 (4-bit) or 8 (8-bit)
+    uint32_t w[NMAT][LW];
+    uint32_t s[NMAT], b[NMAT];        // the step's two groups as fp16 pairs
+};
+
+// One block of the GEMM: features rb*64 .. +63 (16 per wave) of item `item`, up to NT
+// tiles of 16 tokens.  Weights and activations are loaded two steps ahead: the weights into
+// two register slots (the loop unrolled by two), the activations into registers that are
+// staged into the LDS double buffer one step later, so neither wait sits on a step's
+// critical path.  The weight rows of one block share a base address (the expert's matrix)
+// held in scalar registers; a lane only keeps 32-bit offsets.
+template <int NMAT, int BITS, int NT, int FL, int NS, int SM_NMAT>
+__device__ __forceinline__ void pf_gemm_block(const PfGemm& a, int rb, int item,
+                                              PfSmem<NT, SM_NMAT, NS>& sm) {
+    static_assert(SM_NMAT >= NMAT, "LDS holds the scales of every matrix");
+    constexpr bool GROUPED = FL & F_GROUPED, HOUT = FL & F_HOUT, EXTRA = FL & F_EXTRA, LORA = FL & F_LORA;
+    constexpr int TOKB = 16 * NT;
+    int ntok, e = 0;
+    if constexpr (GROUPED) {
+        static_assert(!GROUPED || TOKB == PF_ITEM, "one work item per block");
+        // the record and the pair ids in one round trip (both indexed by the item alone)
+        const int4 rec = reinterpret_cast<const int4*>(a.wrec)[item];
+        const int pair = threadIdx.x < TOKB ? a.wpairs[(long)item * PF_ITEM + threadIdx.x] : 0;
+        if (rec.y == 0) return;   // past the last item
+        e = rec.x;
+        ntok = rec.y;
+        if (threadIdx.x < TOKB) {
+            sm.arow[threadIdx.x] = pair / a.act_div;
+            sm.orow[threadIdx.x] = pair;
+        }
+    } else {
+        const int t0 = item * TOKB;
+        if (t0 >= a.T) return;
+        ntok = min(TOKB, a.T - t0);
+        if (threadIdx.x < TOKB) {
+            sm.arow[threadIdx.x] = t0 + min((int)threadIdx.x, ntok - 1);
+            sm.orow[threadIdx.x] = t0 + threadIdx.x;
+        }
+    }
+    __syncthreads();
+    const int ntiles = (ntok + 15) >> 4;
+    // NS > 0: the step count known at compile time (K = 128 NS), the loop fully unrolled
+    const int K = NS ? NS * PF_KS : a.K, G = K / 64, nsteps = NS ? NS : K / PF_KS;   // even
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 15, j = lane >> 4;
+    const int n = rb * PF_ROWS + wave * 16 + col;              // this lane's feature
+    constexpr int WPU = BITS / 4;                              // words per 8-input unit
+    const int wpr = K * BITS / 32;
+    // uniform bases (this expert's matrices) and per-lane offsets; rows past the matrix are
+    // clamped (their results are never stored)
+    const uint32_t* wb[NMAT];
+    const uint16_t* sb[NMAT];
+    const uint16_t* bb_[NMAT];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) {
+        wb[m] = a.p[m] + (long)e * a.N * wpr;
+        sb[m] = a.s[m] + (long)e * a.N * G;
+        bb_[m] = a.b[m] + (long)e * a.N * G;
+    }
+    const uint32_t woff = (uint32_t)min(n, a.N - 1) * wpr + j * 4 * WPU;
+    const uint32_t goff = (uint32_t)min(n, a.N - 1) * G;
+    // EXTRA: lanes past the last row read row 0 of the extra matrix through per-lane pointers
+    const bool xrow = EXTRA && n >= a.N;
+    const uint32_t* xw = xrow ? a.xp + j * 4 * WPU : wb[0] + woff;
+    const uint16_t* xs = xrow ? a.xs : sb[0] + goff;
+    const uint16_t* xb = xrow ? a.xb : bb_[0] + goff;
+    // with NS known: the block's scales and biases into LDS with 16-byte loads, 8 groups a unit
+    uint4 sbr[NMAT][2][NS ? (NS * 16 + 255) / 256 : 1];
+    auto load_sb = [&] {
+        if constexpr (NS > 0) {
+            constexpr int UPR = NS / 4;   // units of 8 groups per row
+#pragma unroll
+            for (int i = 0; i < (NS * 16 + 255) / 256; ++i) {
+                const int u = min(i * 256 + (int)threadIdx.x, PF_ROWS * UPR - 1);
+                const int r = u / UPR, c8 = u % UPR, rowg = rb * PF_ROWS + r;
+#pragma unroll
+                for (int m = 0; m < NMAT; ++m) {
+                    const uint16_t* ss = sb[m] + (long)min(rowg, a.N - 1) * G;
+                    const uint16_t* bs = bb_[m] + (long)min(rowg, a.N - 1) * G;
+                    if (EXTRA && rowg >= a.N) { ss = a.xs; bs = a.xb; }
+                    sbr[m][0][i] = reinterpret_cast<const uint4*>(ss)[c8];
+                    sbr[m][1][i] = reinterpret_cast<const uint4*>(bs)[c8];
+                }
+            }
+        }
+    };
+    auto commit_sb = [&] {
+        if constexpr (NS > 0) {
+            constexpr int UPR = NS / 4;
+#pragma unroll
+            for (int i = 0; i < (NS * 16 + 255) / 256; ++i) {
+                const int u = i * 256 + (int)threadIdx.x;
+                if (u < PF_ROWS * UPR) {
+                    const int r = u / UPR, c8 = u % UPR;
+#pragma unroll
+                    for (int m = 0; m < NMAT; ++m) {
+                        const uint32_t* sv = reinterpret_cast<const uint32_t*>(&sbr[m][0][i]);
+                        const uint32_t* bv = reinterpret_cast<const uint32_t*>(&sbr[m][1][i]);
+                        uint32_t o[8];
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            o[2 * k] = __builtin_amdgcn_perm(bv[k], sv[k], 0x05040100u);       // (s, b) of group 2k
+                            o[2 * k + 1] = __builtin_amdgcn_perm(bv[k], sv[k], 0x07060302u);   // group 2k + 1
+                        }
+                        uint4* dst = reinterpret_cast<uint4*>(&sm.sb[m][r][c8 * 8]);
+                        dst[0] = uint4{o[0], o[1], o[2], o[3]};
+                        dst[1] = uint4{o[4], o[5], o[6], o[7]};
+                    }
+                }
+            }
+        }
+    };
+
+    // staging: thread handles unit (r = u / 16, c = u % 16), u = tid + 256 q, q < ntiles
+    const int sr = threadIdx.x >> 4, sc = threadIdx.x & 15;
+    // Loads are unconditional (rows past the item repeat its last row; a step past the end
+    // repeats the last step): a load inside a branch gets its wait placed right after it,
+    // which would also drain every weight load in flight.
+    uint4 xr[NT];
+    auto load_x = [&](int ks) {
+        ks = min(ks, nsteps - 1);
+#pragma unroll
+        for (int q = 0; q < NT; ++q)
+            xr[q] = reinterpret_cast<const uint4*>(a.act + (long)sm.arow[q * 16 + sr] * K + ks * PF_KS)[sc];
+    };
+    auto commit_x = [&](int buf) {
+#pragma unroll
+        for (int q = 0; q < NT; ++q)
+            if (q < ntiles) pf_commit<BITS>(xr[q], q * 16 + sr, sc, sm.tile[buf]);
+    };
+    using Slot = PfSlot<NMAT, BITS>;
+    auto load_w = [&](Slot& sl, int ks) {
+        ks = min(ks, nsteps - 1);
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) {
+            const uint4* src = EXTRA ? reinterpret_cast<const uint4*>(xw + ks * (PF_KS * BITS / 32))
+                                     : reinterpret_cast<const uint4*>(wb[m] + (woff + (uint32_t)ks * (PF_KS * BITS / 32)));
+#pragma unroll
+            for (int v = 0; v < WPU; ++v) {
+                const uint4 x = src[v];
+                sl.w[m][4 * v] = x.x; sl.w[m][4 * v + 1] = x.y; sl.w[m][4 * v + 2] = x.z; sl.w[m][4 * v + 3] = x.w;
+            }
+            if constexpr (NS > 0) {
+                // scales come from LDS
+            } else if constexpr (EXTRA) {
+                sl.s[m] = reinterpret_cast<const uint32_t*>(xs)[ks];
+                sl.b[m] = reinterpret_cast<const uint32_t*>(xb)[ks];
+            } else {
+                sl.s[m] = reinterpret_cast<const uint32_t*>(sb[m] + goff)[ks];
+                sl.b[m] = reinterpret_cast<const uint32_t*>(bb_[m] + goff)[ks];
+            }
+        }
+    };
+
+    f32x4 acc[NMAT][NT];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int c = 0; c < NT; ++c) acc[m][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    constexpr float C = code_div<BITS>();
+    uint32_t magic = BITS == 4 ? 0x4C004C00u : 0x5C005C00u;   // fp16 C in both halves
+    asm volatile("" : "+v"(magic));
+    const f16x8 ones = {(f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f};
+    // input unit (8 inputs) of the step that this lane's register slot (g, mm) holds after the
+    // exchange: unit = 8 g + 2 mm + 4 (j & 1) + (j >> 1)
+    const int ubase = 4 * (j & 1) + (j >> 1);
+
+    // One step.  Every loop-carried register (the slot, the staged activations) is consumed
+    // before its reload is issued, so old and new values never live together: the register
+    // allocator keeps them in place and the loop back-edge needs no copy of a loaded register
+    // (such a copy would wait for every load in flight).
+    auto step = [&](Slot& sl, int ks) {
+        const int buf = ks & 1;
+        // stage the activations of step ks + 1 (loaded a step ago) into the other buffer, which
+        // every wave finished reading before the barrier that ended step ks - 1
+        if (ks + 1 < nsteps) commit_x(buf ^ 1);
+        // exchange halves: afterwards units 0 and 2 of the lane hold group 0, 1 and 3 group 1
+        uint32_t cw[NMAT][Slot::LW];
+        float sv[NMAT][2], bv[NMAT][2];   // s and b - C s of the step's two groups
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                for (int v = 0; v < WPU; ++v) {
+                    const auto r = __builtin_amdgcn_permlane32_swap(sl.w[m][(2 * h) * WPU + v],
+                                                                    sl.w[m][(2 * h + 1) * WPU + v], false, false);
+                    cw[m][(2 * h) * WPU + v] = r[0];
+                    cw[m][(2 * h + 1) * WPU + v] = r[1];
+                }
+            }
+            if constexpr (NS > 0) {
+                const uint2 p = *reinterpret_cast<const uint2*>(&sm.sb[m][wave * 16 + col][2 * ks]);
+                const f16x2 g0 = as_h2(p.x), g1 = as_h2(p.y);   // (s, b) of the step's groups
+                sv[m][0] = (float)g0[0];
+                bv[m][0] = fmaf(-C, sv[m][0], (float)g0[1]);
+                sv[m][1] = (float)g1[0];
+                bv[m][1] = fmaf(-C, sv[m][1], (float)g1[1]);
+            } else {
+                const f16x2 s2 = as_h2(sl.s[m]), b2 = as_h2(sl.b[m]);
+#pragma unroll
+                for (int g = 0; g < 2; ++g) {
+                    sv[m][g] = (float)s2[g];
+                    bv[m][g] = fmaf(-C, sv[m][g], (float)b2[g]);
+                }
+            }
+        }
+        // then the loads of step ks + 2: activations first, since memory waits are in issue
+        // order and the activations are needed a step earlier than the weights
+        load_x(ks + 2);
+        load_w(sl, ks + 2);
+        const f16* tb = sm.tile[buf];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            f16x8 bw[NMAT][2];
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                for (int mm = 0; mm < 2; ++mm) bw[m][mm] = pf_codes<BITS>(&cw[m][(2 * mm + g) * WPU], magic);
+#pragma unroll
+            for (int c = 0; c < NT; ++c) {
+                if (c < ntiles) {
+                    const f16* trow = tb + (c * 16 + col) * PF_PITCH;
+                    const f16x8 a0 = *reinterpret_cast<const f16x8*>(trow + 8 * (8 * g + ubase));
+                    const f16x8 a1 = *reinterpret_cast<const f16x8*>(trow + 8 * (8 * g + 2 + ubase));
+                    f32x4 X = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, ones, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                    X = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, ones, X, 0, 0, 0);
+#pragma unroll
+                    for (int m = 0; m < NMAT; ++m) {
+                        f32x4 P = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bw[m][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                        P = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bw[m][1], P, 0, 0, 0);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            acc[m][c][r] = fmaf(sv[m][g], P[r], fmaf(bv[m][g], X[r], acc[m][c][r]));
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    };
+
+    Slot s0, s1;
+    load_sb();
+    load_x(0);
+    load_w(s0, 0);
+    commit_sb();
+    commit_x(0);
+    load_x(1);
+    load_w(s1, 1);
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < (NS ? NS : nsteps); ks += 2) {
+        step(s0, ks);
+        step(s1, ks + 1);
+    }
+
+    // epilogue: tokens 16 c + 4 j + r of feature n
+    const bool extra = EXTRA && n == a.N;
+    if (n >= a.N && !extra) return;
+#pragma unroll
+    for (int c = 0; c < NT; ++c) {
+        if (c >= ntiles) break;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = c * 16 + 4 * j + r;
+            if (t < ntok) {
+                const int orow = sm.orow[t];
+                if constexpr (HOUT) {
+                    a.hout[(long)orow * a.N + n] = f2h(silu(acc[0][c][r]) * acc[NMAT - 1][c][r]);
+                } else if (extra) {
+                    a.xout[orow] = acc[0][c][r];
+                } else {
+                    const long o = (long)orow * a.ostride + n;
+                    float v = acc[0][c][r];
+                    if (LORA && a.B)
+                        v = fmaf(a.lscale, lora_b_dot(a.B, adapter_of(a.adapter, orow, a.nad), a.N, n,
+                                                      a.rank, a.z + (long)orow * MAX_RANK), v);
+                    a.out0[o] = v;
+                    if (NMAT == 2) a.out1[o] = acc[NMAT - 1][c][r];
+                }
+            }
+        }
+    }
+}
+
+template <int NMAT, int BITS, int NT, int FL, int NS>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) k_pf_gemm(PfGemm a) {
+    __shared__ __align__(16) PfSmem<NT, NMAT, NS> sm;
+    int rb, item;
+    pf_block(blockIdx.x, a.nrb, rb, item);
+    pf_gemm_block<NMAT, BITS, NT, FL, NS, NMAT>(a, rb, item, sm);
+}
+
+// v . A-row over K inputs in one wave (fp16 x fp16 into fp32), every load of a 4096-input
+// chunk issued before its sum.
+__device__ __forceinline__ float wave_dot16(const uint16_t* __restrict__ arow,
+                                            const uint16_t* __restrict__ vrow, int K) {
+    const int lane = threadIdx.x & 63;
+    float acc = 0.0f;
+    for (int k0 = 0; k0 < K; k0 += 4096) {
+        uint4 av[8], xv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int k = k0 + lane * 8 + i * 512;
+            if (k < K) {
+                av[i] = *reinterpret_cast<const uint4*>(arow + k);
+                xv[i] = *reinterpret_cast<const uint4*>(vrow + k);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (k0 + lane * 8 + i * 512 < K) {
+                const f16x2* ah = reinterpret_cast<const f16x2*>(&av[i]);
+                const f16x2* xh = reinterpret_cast<const f16x2*>(&xv[i]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_fdot2(ah[q], xh[q], acc, false);
+            }
+        }
+    }
+    return seg_sum<64>(acc);
+}
+
+// x side of the layer in one launch: the router rows plus the shared-gate row (8-bit), the
+// shared expert's gate and up (int4), then the LoRA down-projections of x (one wave per
+// (projection, token, rank row)).
+struct XsideArgs {
+    PfGemm router, shared;
+    int nb_router, nb_shared, zjobs;
+};
+
+template <int NS>
+__global__ void __launch_bounds__(256) k_pf_xside(XsideArgs xa, MoeArgs a) {
+    __shared__ __align__(16) PfSmem<4, 2, NS> sm;
+    const int b = blockIdx.x;
+    int rb, item;
+    if (b < xa.nb_router) {
+        pf_block(b, xa.router.nrb, rb, item);
+        pf_gemm_block<1, 8, 4, F_EXTRA, NS, 2>(xa.router, rb, item, sm);
+        return;
+    }
+    if (b < xa.nb_router + xa.nb_shared) {
+        pf_block(b - xa.nb_router, xa.shared.nrb, rb, item);
+        pf_gemm_block<2, 4, 4, 0, NS, 2>(xa.shared, rb, item, sm);
+        return;
+    }
+    const int jb = (b - xa.nb_router - xa.nb_shared) * 4 + (threadIdx.x >> 6);
+    if (jb >= xa.zjobs) return;
+    const int ng = a.Ag ? a.T * a.rg : 0;
+    const bool isg = jb < ng;
+    const int jj = isg ? jb : jb - ng;
+    const int rank = isg ? a.rg : a.ru;
+    const int t = jj / rank, r = jj % rank;
+    const int ad = adapter_of(a.adapter, t, isg ? a.nag : a.nau);
+    const float v = wave_dot16((isg ? a.Ag : a.Au) + ((long)ad * rank + r) * a.H, a.x + (long)t * a.H, a.H);
+    if ((threadIdx.x & 63) == 0) (isg ? a.zg : a.zu)[(long)t * MAX_RANK + r] = v;
+}
+
+// Shared expert activation for one token per block: hs = silu(gs + LoRA_gate) * (us +
+// LoRA_up), written to HBM and kept in LDS for the down LoRA's z = A_down hs.
+__global__ void __launch_bounds__(256) k_pf_shared_h(MoeArgs a) {
+    extern __shared__ __align__(16) uint16_t hl[];
+    const int t = blockIdx.x;
+    for (int n = threadIdx.x; n < a.SI; n += 256) {
+        const long i = (long)t * a.SI + n;
+        float gv = a.gs[i], uv = a.us[i];
+        if (a.Bg) gv = fmaf(a.lsg, lora_b_dot(a.Bg, adapter_of(a.adapter, t, a.nag), a.SI, n, a.rg, a.zg + (long)t * MAX_RANK), gv);
+        if (a.Bu) uv = fmaf(a.lsu, lora_b_dot(a.Bu, adapter_of(a.adapter, t, a.nau), a.SI, n, a.ru, a.zu + (long)t * MAX_RANK), uv);
+        const uint16_t h = f2h(silu(gv) * uv);
+        a.hs[i] = h;
+        hl[n] = h;
+    }
+    if (!a.Ad) return;
+    __syncthreads();
+    const int ad = adapter_of(a.adapter, t, a.nad);
+    for (int r = threadIdx.x >> 6; r < a.rd; r += 4) {
+        const float v = wave_dot16(a.Ad + ((long)ad * a.rd + r) * a.SI, hl, a.SI);
+        if ((threadIdx.x & 63) == 0) a.zd[(long)t * MAX_RANK + r] = v;
+    }
+}
+
+// Top-K of every token, one wave per token.
+__global__ void __launch_bounds__(256) k_pf_topk(MoeArgs a) {
+    __shared__ int sel[4][MAX_K];
+    __shared__ float sw[4][MAX_K];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t = blockIdx.x * 4 + wave;
+    if (t >= a.T) return;
+    wave_topk(a.logits + (long)t * a.Ep, a.rbias, a.E, a.K, sel[wave], sw[wave]);
+    if (lane == 0) {   // the lane that wrote the selection
+        for (int r = 0; r < a.K; ++r) {
+            const long i = (long)t * a.K + r;
+            const int e = sel[wave][r];
+            const float w = sw[wave][r];
+            a.idx[i] = e;
+            a.wts[i] = w;
+            if (a.idx_out) a.idx_out[i] = e;
+            if (a.w_out) a.w_out[i] = w;
+        }
+    }
+}
+
+// Inclusive prefix sum over the wave.
+__device__ __forceinline__ int wave_scan(int v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(v, off);
+        if (lane >= off) v += t;
+    }
+    return v;
+}
+
+// Exclusive prefix sum over a block of 1024 threads; the total goes to *total.
+__device__ int block_scan_excl(int v, int* wsum, int* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int inc = wave_scan(v);
+    if (lane == 63) wsum[wave] = inc;
+    __syncthreads();
+    if (wave == 0) {
+        const int s = lane < 16 ? wsum[lane] : 0;
+        const int si = wave_scan(s);
+        if (lane < 16) wsum[16 + lane] = si - s;
+        if (lane == 15) *total = si;
+    }
+    __syncthreads();
+    const int r = inc - v + wsum[16 + wave];
+    __syncthreads();   // wsum is reused by the next scan
+    return r;
+}
+
+// Stable counting sort of the (token, k) pairs by expert (pair p = t * K + k), written as
+// GEMM work items: chunks of at most PF_ITEM pairs of one expert, each a record (expert,
+// tokens) and its pair ids (the last repeated up to PF_ITEM); records past the last item get
+// zero tokens.  One block of 1024 threads.  Ranks inside each chunk of 64 pairs come from
+// ballots on the expert index bits (lanes with the same expert); the chunks of a segment of
+// 1024 pairs are then offset per expert by a prefix over the segment's 16 chunk counts.
+__global__ void __launch_bounds__(1024) k_pf_sort(MoeArgs a, int max_items) {
+    __shared__ int cnt[1024], base[1024], eoff[1024], ewex[1024], ecnt[1024], wsum[32], tot;
+    __shared__ uint16_t tab[16][1024];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int E = a.E, TK = a.T * a.K;
+    cnt[tid] = 0;
+    __syncthreads();
+    for (int p = tid; p < TK; p += 1024) atomicAdd(&cnt[a.idx[p]], 1);
+    __syncthreads();
+    const int c = tid < E ? cnt[tid] : 0;
+    const int excl = block_scan_excl(c, wsum, &tot);
+    const int nw = (c + PF_ITEM - 1) / PF_ITEM;
+    const int wex = block_scan_excl(nw, wsum, &tot);
+    if (tid < E) {
+        a.offs[tid] = excl;
+        base[tid] = excl;
+        eoff[tid] = excl;
+        ewex[tid] = wex;
+        ecnt[tid] = c;
+        for (int w = 0; w < nw; ++w)
+            reinterpret_cast<int4*>(a.wrec)[wex + w] = int4{tid, min(PF_ITEM, c - w * PF_ITEM), 0, 0};
+    }
+    if (tid == 0) a.offs[E] = TK;
+    __syncthreads();
+    for (int it = tot + tid; it < max_items; it += 1024) reinterpret_cast<int4*>(a.wrec)[it] = int4{0, 0, 0, 0};
+    const int ebits = E > 1 ? 32 - __builtin_clz(E - 1) : 0;
+    const uint64_t lt = (1ull << lane) - 1;
+    for (int s0 = 0; s0 < TK; s0 += 1024) {
+        const int p = s0 + tid;
+        const bool valid = p < TK;
+        const int ex = valid ? a.idx[p] : 0;
+        uint64_t same = __ballot(valid);
+        for (int bt = 0; bt < ebits; ++bt) {
+            const bool bit = (ex >> bt) & 1;
+            const uint64_t bb = __ballot(bit);
+            same &= bit ? bb : ~bb;
+        }
+        const int rank = __popcll(same & lt);
+        if (tid < E)
+            for (int w = 0; w < 16; ++w) tab[w][tid] = 0;
+        __syncthreads();
+        if (valid && rank == 0) tab[wave][ex] = (uint16_t)__popcll(same);
+        __syncthreads();
+        if (tid < E) {
+            int run = 0;
+            for (int w = 0; w < 16; ++w) {
+                const int v = tab[w][tid];
+                tab[w][tid] = (uint16_t)run;
+                run += v;
+            }
+            cnt[tid] = run;
+        }
+        __syncthreads();
+        if (valid) {
+            const int pos = base[ex] + tab[wave][ex] + rank;
+            a.perm[pos] = p;
+            // the pair's slot in its work item; the item's last pair also fills the padding
+            const int r = pos - eoff[ex], it = ewex[ex] + r / PF_ITEM, i = r % PF_ITEM;
+            const int n_it = min(PF_ITEM, ecnt[ex] - (r / PF_ITEM) * PF_ITEM);
+            int32_t* dst = a.wpairs + (long)it * PF_ITEM;
+            dst[i] = p;
+            if (i == n_it - 1)
+                for (int q = i + 1; q < PF_ITEM; ++q) dst[q] = p;
+        }
+        __syncthreads();
+        if (tid < E) base[tid] += cnt[tid];
+        __syncthreads();
+    }
+}
+
+// y = fp16(sum_k w_k o_k + sigmoid(gate) os) (+ residual), k in order; os already holds the
+// LoRA down delta.  Eight outputs per thread with 16-byte loads.
+__global__ void __launch_bounds__(256) k_pf_combine(MoeArgs a) {
+    const long i8 = ((long)blockIdx.x * 256 + threadIdx.x) * 8;
+    if (i8 >= (long)a.T * a.H) return;
+    const int t = (int)(i8 / a.H), n = (int)(i8 % a.H);
+    float acc[8];
+    const float4* os = reinterpret_cast<const float4*>(a.os + i8);
+    const float4 o0 = os[0], o1 = os[1];
+    const float gm = sigmoid(a.gate[t]);
+    float ov[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+    for (int k = 0; k < a.K; ++k) {
+        const float w = a.wts[(long)t * a.K + k];
+        const float4* ok = reinterpret_cast<const float4*>(a.o + ((long)t * a.K + k) * a.H + n);
+        const float4 p0 = ok[0], p1 = ok[1];
+        const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] = fmaf(w, pv[q], acc[q]);
+    }
+    uint16_t out[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) out[q] = f2h(fmaf(gm, ov[q], acc[q]));
+    if (a.add_residual) {
+        const uint4 xr = *reinterpret_cast<const uint4*>(a.x + i8);
+        const uint16_t* xh = reinterpret_cast<const uint16_t*>(&xr);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) out[q] = f2h(h2f(xh[q]) + h2f(out[q]));
+    }
+    *reinterpret_cast<uint4*>(a.y + i8) = *reinterpret_cast<const uint4*>(out);
+}
+
+// Launch with the step loop unrolled for the common input sizes (512, 1024, 2048).
+template <int NMAT, int BITS, int NT, int FL>
+void pf_gemm(const PfGemm& p, hipStream_t s) {
+    const dim3 grid((unsigned)(p.nrb * p.items));
+    switch (p.K / PF_KS) {
+        case 4: k_pf_gemm<NMAT, BITS, NT, FL, 4><<<grid, 256, 0, s>>>(p); break;
+        case 8: k_pf_gemm<NMAT, BITS, NT, FL, 8><<<grid, 256, 0, s>>>(p); break;
+        case 16: k_pf_gemm<NMAT, BITS, NT, FL, 16><<<grid, 256, 0, s>>>(p); break;
+        default: k_pf_gemm<NMAT, BITS, NT, FL, 0><<<grid, 256, 0, s>>>(p); break;
+    }
+}
+
+// Arguments of one GEMM over `feat` feature rows (N plus an optional extra row) and `items`
+// token groups or work items.
+PfGemm gemm_args(const QW& w0, const QW* w1, int N, int K, const uint16_t* act, int feat,
+                 int items) {
+    PfGemm p{};
+    p.p[0] = w0.p; p.s[0] = w0.s; p.b[0] = w0.b;
+    if (w1) { p.p[1] = w1->p; p.s[1] = w1->s; p.b[1] = w1->b; }
+    p.N = N; p.K = K; p.act = act; p.ostride = N;
+    p.nrb = (feat + PF_ROWS - 1) / PF_ROWS;
+    p.items = (items + 7) / 8 * 8;
+    return p;
+}
+
+PfGemm grouped(const MoeArgs& a, const QW& w0, const QW* w1, int N, int K, const uint16_t* act,
+               int act_div, int items) {
+    PfGemm p = gemm_args(w0, w1, N, K, act, N, items);
+    p.act_div = act_div;
+    p.wrec = a.wrec; p.wpairs = a.wpairs;
+    return p;
+}
+
+}  // namespace
+
+// Upper bound on the work items of the sort, rounded up to the 8 XCDs of the block order:
+// sum over experts of ceil(count / PF_ITEM) <= E + T K / PF_ITEM.
+int prefill_max_items(int E, int T, int K) {
+    return (E + (T * K + PF_ITEM - 1) / PF_ITEM + 7) / 8 * 8;
+}
+
+hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s) {
+    const int items = prefill_max_items(a.E, a.T, a.K);
+    const int tgroups = (a.T + PF_TOK - 1) / PF_TOK;
+    const bool all = stage == QMOE_STAGE_ALL;
+    if (all || stage == QMOE_STAGE_ROUTE) {
+        XsideArgs xa{};
+        xa.router = gemm_args(a.router, nullptr, a.E, a.H, a.x, a.E + 1, tgroups);
+        xa.router.T = a.T;
+        xa.router.out0 = a.logits; xa.router.ostride = a.Ep;
+        xa.router.xp = a.sgate.p; xa.router.xs = a.sgate.s; xa.router.xb = a.sgate.b; xa.router.xout = a.gate;
+        xa.shared = gemm_args(a.shg, &a.shu, a.SI, a.H, a.x, a.SI, tgroups);
+        xa.shared.T = a.T;
+        xa.shared.out0 = a.gs; xa.shared.out1 = a.us;
+        xa.nb_router = xa.router.nrb * xa.router.items;
+        xa.nb_shared = xa.shared.nrb * xa.shared.items;
+        xa.zjobs = (a.Ag ? a.T * a.rg : 0) + (a.Au ? a.T * a.ru : 0);
+        const dim3 grid((unsigned)(xa.nb_router + xa.nb_shared + (xa.zjobs + 3) / 4));
+        switch (a.H / PF_KS) {
+            case 4: k_pf_xside<4><<<grid, 256, 0, s>>>(xa, a); break;
+            case 8: k_pf_xside<8><<<grid, 256, 0, s>>>(xa, a); break;
+            case 16: k_pf_xside<16><<<grid, 256, 0, s>>>(xa, a); break;
+            default: k_pf_xside<0><<<grid, 256, 0, s>>>(xa, a); break;
+        }
+        k_pf_shared_h<<<a.T, 256, (size_t)a.SI * 2, s>>>(a);
+        k_pf_topk<<<(a.T + 3) / 4, 256, 0, s>>>(a);
+        k_pf_sort<<<1, 1024, 0, s>>>(a, items);
+    }
+    if (all || stage == QMOE_STAGE_GATE_UP) {
+        PfGemm p = grouped(a, a.eg, &a.eu, a.I, a.H, a.x, a.K, items);
+        p.hout = a.h;
+        pf_gemm<2, 4, PF_ITEM / 16, F_GROUPED | F_HOUT>(p, s);
+    }
+    if (all || stage == QMOE_STAGE_DOWN) {
+        PfGemm p = grouped(a, a.ed, nullptr, a.H, a.I, a.h, 1, items);
+        p.out0 = a.o;
+        pf_gemm<1, 4, PF_ITEM / 16, F_GROUPED>(p, s);
+        PfGemm q = gemm_args(a.shd, nullptr, a.H, a.SI, a.hs, a.H, tgroups);
+        q.T = a.T;
+        q.out0 = a.os;
+        q.B = a.Bd; q.z = a.zd; q.rank = a.rd; q.nad = a.nad; q.lscale = a.lsd; q.adapter = a.adapter;
+        pf_gemm<1, 4, PF_TOK / 16, F_LORA>(q, s);
+        k_pf_combine<<<(unsigned)(((long)a.T * a.H / 8 + 255) / 256), 256, 0, s>>>(a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace qmoe

@@ -96,6 +96,30 @@ def test_wider_shapes_many_tiles(q):
     check_layer(Lc, x, ad, y, idx, w)
 
 
+@pytest.mark.parametrize("T", [33, 150])
+def test_prefill_ragged_shapes(q, T):
+    """Token-sorted path with ragged sizes: 37 experts (router rows and the logits stride
+    are not a multiple of 64), top-3, hidden 1024, a wider shared expert, 3 adapters."""
+    S = Shape(hidden=1024, inter=512, shared_inter=1024, n_experts=37, top_k=3, rank=16, n_adapters=3)
+    Lc = build_layer(synth.Workload.TEST, 14, S)
+    x = synth.activations(T, S.hidden, synth.Workload.TEST, 14, T)
+    ad = (np.arange(T) % 3).astype(np.int32)
+    y, idx, w = run_device(q, Lc, S, x, ad)
+    err, rel, n_alt = check_layer(Lc, x, ad, y, idx, w)
+    print(f"ragged T={T}: max abs {err:.2e} rel L2 {rel:.2e} alternatives {n_alt}", flush=True)
+
+
+def test_prefill_wide_inter_many_items(q):
+    """An expert with more than 64 tokens (several work items) and a 1536-wide inter."""
+    S = Shape(hidden=1024, inter=1536, shared_inter=512, n_experts=4, top_k=2, rank=16, n_adapters=2)
+    Lc = build_layer(synth.Workload.TEST, 15, S)
+    x = synth.activations(200, S.hidden, synth.Workload.TEST, 15)
+    ad = (np.arange(200) % 2).astype(np.int32)
+    y, idx, w = run_device(q, Lc, S, x, ad)
+    assert np.bincount(idx.ravel(), minlength=4).max() > 64
+    check_layer(Lc, x, ad, y, idx, w)
+
+
 def test_decode_one_token_full_shape(q):
     """The single-token decode workload: hidden 2048, 256 experts, top-4, shared expert with
     8-bit gate, LoRA rank 16 alpha 32 on the shared projections."""
@@ -144,12 +168,31 @@ def test_multi_tenant_stack_teacher_forced(q):
         x = moe.residual(x, moe.moe_layer(x, Lc, ad)["y"])
 
 
-def test_deterministic(q):
+@pytest.mark.parametrize("T", [23, 100])
+def test_deterministic(q, T):
     Lc = build_layer(synth.Workload.TEST, 13, SMALL)
     Ld = to_device(Lc, SMALL, DEV)
-    x = dev(synth.activations(23, SMALL.hidden, synth.Workload.TEST, 13))
-    ws = q.moe_workspace(Ld, 23, DEV)
+    x = dev(synth.activations(T, SMALL.hidden, synth.Workload.TEST, 13))
+    ws = q.moe_workspace(Ld, T, DEV)
     a = q.moe_switchglu_int4(Ld, x, ws=ws).clone()
     b = q.moe_switchglu_int4(Ld, x, ws=ws)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("T", [5, 100])
+def test_stages_in_order_equal_the_whole_layer(q, T):
+    """moe_switchglu_int4_stage: ROUTE, GATE_UP, DOWN in order give the bits of one call."""
+    Lc = build_layer(synth.Workload.TEST, 16, SMALL)
+    Ld = to_device(Lc, SMALL, DEV)
+    x = dev(synth.activations(T, SMALL.hidden, synth.Workload.TEST, 16))
+    ad = dev((np.arange(T) % 2).astype(np.int32))
+    ws = q.moe_workspace(Ld, T, DEV)
+    whole = q.moe_switchglu_int4(Ld, x, ad, ws=ws).clone()
+    y = torch.empty_like(x)
+    call = q.MoECall(Ld, x, y, ws, adapter_idx=ad)
+    for st in (q.STAGE_ROUTE, q.STAGE_GATE_UP, q.STAGE_DOWN):
+        call(st)
+    call(q.STAGE_DOWN)   # a stage re-run alone repeats its work on the same inputs
+    torch.cuda.synchronize()
+    assert torch.equal(whole.view(torch.int16), y.view(torch.int16))
