@@ -312,6 +312,174 @@ def bench_moe_prefill(args, q, torch):
     return res, cpu_baseline_moe_prefill
 
 
+def cpu_baseline_moe_stack(n_layers=2, budget_s=25.0):
+    """The oracle (float64 numpy) on a bounded sample: the 16 multi-tenant tokens through the
+    first layers of the stack (only the experts they reach are quantized); the rate is
+    scaled to the 40-layer step."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import synth
+    from layers import Shape, build_layer, routed_experts
+    from oracle import moe
+    from threadpoolctl import threadpool_info
+
+    S = Shape(top_k=8, n_adapters=4)
+    wl = synth.Workload.MOE_STACK
+    x = synth.activations(16, H, wl, 0)
+    ad = synth.adapter_index(16, 4)
+    spent, done = 0.0, 0
+    for layer in range(n_layers):
+        L = build_layer(wl, layer, S, only_experts=routed_experts(x, wl, layer, S, margin=0))
+        t0 = time.perf_counter()
+        out = moe.moe_layer(x, L, ad)
+        spent += time.perf_counter() - t0
+        x = moe.residual(x, out["y"])
+        done += 1
+        if spent > budget_s:
+            break
+    blas = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+    cores = max(blas) if blas else 1
+    per_step = spent / done * LAYERS
+    return {"value": 16 / per_step, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"16 tokens (4 adapters) through {done} of the 40 layers, float64 numpy, "
+                      f"{spent:.1f} s, scaled to 40 layers"}
+
+
+def bench_moe_stack(args, q, torch):
+    """40 stacked layers, 16 tokens per step (4 LoRA adapter sets x 4 tokens), top-8."""
+    T, TOPK, NAD = 16, 8, 4
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(2468)
+    t0 = time.perf_counter()
+    layers = [make_layer(q, torch, gen, top_k=TOPK, n_adapters=NAD, residual=True)
+              for _ in range(LAYERS)]
+    torch.cuda.synchronize()
+    log(f"built {LAYERS} layers in {time.perf_counter() - t0:.1f} s")
+    K, W = args.steps, args.warmup
+    ad = (torch.arange(T, device="cuda", dtype=torch.int32) // (T // NAD)).contiguous()
+    x0 = torch.randn((T, H), generator=gen, device="cuda").half()
+    acts = torch.empty((LAYERS + 1, T, H), dtype=torch.float16, device="cuda")
+    ws = torch.empty(q.moe_workspace_bytes(layers[0], T), dtype=torch.uint8, device="cuda")
+    calls = [q.MoECall(layers[l], acts[l], acts[l + 1], ws, adapter_idx=ad) for l in range(LAYERS)]
+
+    def step():
+        for c in calls:
+            c()
+    acts[0].copy_(x0)
+    if W:
+        gw = graph_of(torch, lambda: [step() for _ in range(W)])
+        gw.replay()
+    g = graph_of(torch, lambda: [step() for _ in range(K)])
+    ms = time_graph(torch, g)
+    ms_step = ms / K
+
+    # dominant kernel: gate/up of one layer over routed workspaces (one per layer)
+    wss = torch.empty((LAYERS, ws.numel()), dtype=torch.uint8, device="cuda")
+    idx = torch.empty((LAYERS, T, TOPK), dtype=torch.int32, device="cuda")
+    rcalls = [q.MoECall(layers[l], acts[l], acts[l + 1], wss[l], adapter_idx=ad, idx_out=idx[l])
+              for l in range(LAYERS)]
+    for c in rcalls:
+        c(q.STAGE_ROUTE)
+    torch.cuda.synchronize()
+    g_gu = graph_of(torch, lambda: [c(q.STAGE_GATE_UP) for c in rcalls])
+    us_gu = time_graph(torch, g_gu, reps=3) / LAYERS * 1e3
+    ih = idx.cpu().numpy()
+    used = float(np.mean([len(np.unique(ih[l])) for l in range(LAYERS)]))
+    gu_bytes = (used * 2 * MAT_BYTES_4BIT(I, H) + 2 * MAT_BYTES_4BIT(SI, H) + T * H * 2
+                + 2 * NAD * SI * RANK * 2 + (T * TOPK * I + T * SI) * 2)
+    step_bytes = LAYERS * (MAT_BYTES_8BIT(E, H) + MAT_BYTES_8BIT(1, H) + used * 3 * MAT_BYTES_4BIT(I, H)
+                           + 3 * MAT_BYTES_4BIT(SI, H) + 3 * NAD * RANK * (H + SI) * 2 + 2 * T * H * 2)
+    achieved = gu_bytes / (us_gu * 1e-6) / 1e9
+    res = {
+        "metric": "int4 MoE stack tokens/s (multi-tenant decode, 40 layers, 16 tokens per step)",
+        "value": T * K / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "moe_switchglu_int4 x 40 stacked layers with residual, 16 tokens/step, "
+                               "top-8 of 256 experts, 4 LoRA adapter sets (adapter = token // 4), "
+                               "hidden 2048, int4 g64, shared expert + 8-bit gate",
+                   "global_batch": T, "layers": LAYERS, "experts_used_per_layer": used,
+                   "step_algorithmic_bytes": step_bytes,
+                   "step_hbm_gbps": step_bytes / (ms_step * 1e-3) / 1e9},
+        "roofline": {"kernel": "k_dec_gate_up (16 tokens, top-8, routed + shared)",
+                     "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "bytes_per_launch": gu_bytes, "us_per_launch": us_gu},
+    }
+    return res, cpu_baseline_moe_stack
+
+
+def sg_bytes(rows, cols, period=4):
+    n4 = rows // period
+    return n4 * cols // 2 + (rows - n4) * cols // 4 + rows * 2
+
+
+def cpu_baseline_supergroup(batch, budget_s=15.0):
+    """The oracle on a bounded sample: the super-group GEMM of one seeded 3072 x 1024 weight
+    against `batch` inputs, repeated until the budget is spent."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import synth
+    from oracle import supergroup
+    from threadpoolctl import threadpool_info
+
+    w = synth.normal_f32((3072, 1024), synth.WEIGHT_SIGMA, synth.Workload.SUPERGROUP, 0,
+                         synth.Role.SUPERGROUP)
+    W, _ = supergroup.quantize(w, 4)
+    x = synth.activations(batch, 1024, synth.Workload.SUPERGROUP, 0)
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        supergroup.gemm(x, W)
+        n += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    blas = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+    return {"value": n * batch / dt, "unit": "tokens/s", "cores": int(max(blas) if blas else 1),
+            "kind": "oracle", "sample": f"{n} GEMMs of W[3072x1024] with {batch} inputs, {dt:.1f} s"}
+
+
+def bench_supergroup(args, q, torch):
+    """Mixed ternary/4-bit super-group GEMM, W [3072 x 1024], B inputs per call."""
+    B, N, Kc = args.batch, 3072, 1024
+    COPIES = 1024 if B == 1 else 64          # B = 1: 1 GB of weights rotated, 4x the cache
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(97)
+    mats = []
+    for _ in range(COPIES):
+        w = torch.randn((N, Kc), generator=gen, device="cuda") * 0.02
+        mats.append(q.quantize_supergroup(w, 4))
+    del w
+    K, W = args.steps, args.warmup
+    xs = torch.randn((16, B, Kc), generator=gen, device="cuda").half()
+    ys = torch.empty((16, B, N), dtype=torch.float16, device="cuda")
+
+    def run(lo, hi):
+        def f():
+            for i in range(lo, hi):
+                q.qlinear_supergroup(xs[i % 16], mats[i % COPIES], out=ys[i % 16])
+        return f
+    if W:
+        graph_of(torch, run(K, K + W)).replay()
+    g = graph_of(torch, run(0, K))
+    ms = time_graph(torch, g)
+    us = ms / K * 1e3
+    wbytes = sg_bytes(N, Kc)
+    bytes_ = wbytes + B * Kc * 2 + B * N * 2
+    flops = 2 * B * N * Kc
+    ach = bytes_ / (us * 1e-6) / 1e9
+    res = {"metric": f"super-group GEMM tokens/s (B={B})", "value": B * K / (ms * 1e-3),
+           "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": ms / K,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+           "data": "synthetic",
+           "config": {"workload": f"qlinear_supergroup W[3072x1024] (1 in 4 channels 4-bit, 3 ternary), "
+                                  f"x[{B}x1024], {COPIES} weight copies rotated", "global_batch": B,
+                      "tflops": flops / (us * 1e-6) / 1e12},
+           "roofline": {"kernel": "k_sg_gemv", "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None,
+                        "bytes_per_launch": bytes_, "us_per_launch": us}}
+    return res, (lambda: cpu_baseline_supergroup(B))
+
+
 def bench_gemv(args, q, torch):
     gen = torch.Generator(device="cuda")
     gen.manual_seed(1234)
@@ -350,7 +518,8 @@ def bench_gemv(args, q, torch):
     return res, None
 
 
-WORKLOADS = {"moe_decode": bench_moe_decode, "moe_prefill": bench_moe_prefill, "gemv": bench_gemv}
+WORKLOADS = {"moe_decode": bench_moe_decode, "moe_prefill": bench_moe_prefill,
+             "moe_stack": bench_moe_stack, "supergroup": bench_supergroup, "gemv": bench_gemv}
 
 
 def main():
@@ -360,6 +529,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="moe_decode", choices=sorted(WORKLOADS))
     ap.add_argument("--skew", action="store_true", help="moe_prefill: +2.0 on experts 0..15")
+    ap.add_argument("--batch", type=int, default=1, choices=(1, 64), help="supergroup: inputs per call")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
