@@ -46,6 +46,20 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter runs (profiles/traffic.json),
+    or None when the kernel's sources changed since the counters were taken."""
+    import hashlib
+    try:
+        entry = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))[kernel]
+        h = hashlib.sha256()
+        for src in entry["sources"]:
+            h.update(open(os.path.join(ROOT, src), "rb").read())
+    except (OSError, KeyError, ValueError):
+        return None
+    return entry["traffic_bytes_per_launch"] if h.hexdigest() == entry["source_sha256"] else None
+
+
 # ------------------------------------------------------------------------------ device data
 
 def make_layer(q, torch, gen, top_k=4, n_adapters=1, skew=False, residual=False):
@@ -201,9 +215,10 @@ def bench_moe_decode(args, q, torch):
                    "global_batch": 1, "layers_rotated": LAYERS,
                    "step_algorithmic_bytes": step_bytes,
                    "step_hbm_gbps": step_bytes / (ms_step * 1e-3) / 1e9},
-        "roofline": {"kernel": "k_moe_gate_up (routed + shared gate/up, silu*up)",
+        "roofline": {"kernel": "k_dec_gate_up (top-K, routed + shared gate/up, silu*up)",
                      "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic("k_dec_gate_up"),
                      "bytes_per_launch": gu_bytes, "us_per_launch": ms_gu * 1e3},
     }
     return res, cpu_baseline_moe_decode

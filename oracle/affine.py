@@ -14,7 +14,7 @@ Sources
   dequantized weight is the scale times the integer plus the bias (the operator between the
   two is lost in the page's text; the tensors are called *biases*, so the offset is added).
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
 * The scale is ``(max - min) / (2^bits - 1)`` and the bias is the group minimum (min-max
   affine), both computed in float32 and stored as fp16 (round-to-nearest-even).
 * The integer code uses the *stored* fp16 scale and bias:

@@ -19,7 +19,7 @@ Sources
 * "Recover-LoRA ..." (bjdmk.com.cn), section 2: frozen int4 base plus an unmerged LoRA
   added at inference; one read-only base serves many adapter sets.
 
-Readings where the pages are silent (all listed in the design doc): SiLU(z) = z / (1 + e^-z)
+Readings where the pages are silent: SiLU(z) = z / (1 + e^-z)
 applied to the gate projection and multiplied by the up projection; the shared expert is
 scaled by sigmoid of the 8-bit gate's logit; the LoRA delta is ``(alpha/r) * B (A v)`` on
 each of the shared expert's three projections, with the projection's own input ``v``; the

@@ -12,7 +12,7 @@ Source: "EDGERAZOR deep dive: how 1.58-bit quantization makes on-device models 1
   product: ``Y = sum (s_W s_X) Q(W)^T Q(X)``; weight-only here, so ``s_X = 1`` and x stays
   fp16.
 
-Readings (listed in DESIGN.md): per-channel scales (mean / max over the channel's inputs);
+Readings where the pages are silent: per-channel scales (mean / max over the channel's inputs);
 the *first* channel of every block is the 4-bit one; eps = 1e-5 for both quantizers; the
 scale is stored as fp16 and the codes are taken against the stored scale, in float32, ties
 to even; the ternary mean is summed in float64 and rounded once to float32 so that its value
