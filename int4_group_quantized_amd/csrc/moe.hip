@@ -39,13 +39,14 @@ Layout layout_of(const qmoe_moe_layer& L, int T) {
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t r = off; off = up256(off + bytes); return r; };
     const size_t TK = (size_t)T * L.top_k;
-    l.logits = take((size_t)T * ((L.n_experts + 63) / 64 * 64) * 4);
-    l.gate = take((size_t)T * 4);
+    const size_t ks = (size_t)prefill_ksplit(L.hidden);   // split-K partials of the x side
+    l.logits = take(ks * T * ((L.n_experts + 63) / 64 * 64) * 4);
+    l.gate = take(ks * T * 4);
     l.zg = take((size_t)T * MAX_RANK * 4);
     l.zu = take((size_t)T * MAX_RANK * 4);
     l.zd = take((size_t)T * MAX_RANK * 4);
-    l.gs = take((size_t)T * L.shared_inter * 4);
-    l.us = take((size_t)T * L.shared_inter * 4);
+    l.gs = take(ks * T * L.shared_inter * 4);
+    l.us = take(ks * T * L.shared_inter * 4);
     l.idx = take(TK * 4);
     l.wts = take(TK * 4);
     l.offs = take((size_t)(L.n_experts + 1) * 4);

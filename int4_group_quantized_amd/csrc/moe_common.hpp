@@ -173,6 +173,7 @@ bool decode_path_fits(const qmoe_moe_layer& L, int T);
 hipError_t launch_moe_decode(const MoeArgs& a, int stage, hipStream_t s);
 // moe_prefill.hip
 int prefill_max_items(int E, int T, int K);
+int prefill_ksplit(int hidden);
 hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s);
 
 }  // namespace qmoe

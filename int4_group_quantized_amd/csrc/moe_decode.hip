@@ -317,8 +317,11 @@ static int chunks_per_lane(int K) { return (K / 32) / lanes_per_row(K); }
 // The register and LDS budgets of the decode kernels: hidden rows of at most two 32-input
 // chunks per lane (hidden <= 4096), down rows of one chunk per lane (inter <= 2048, a power
 // of two), equal routed and shared intermediate sizes.
+// The decode path re-reads an expert for every (token, k) pair that uses it; from about 32
+// pairs on, the token-sorted path (each used expert read once, MFMA) is faster on MI355X
+// (measured at 16 x 8, 8 x 8, 8 x 4 and 4 x 8 pairs), below it its fixed route cost loses.
 bool decode_path_fits(const qmoe_moe_layer& L, int T) {
-    return T <= MAX_DEC_T && L.top_k <= MAX_DEC_K && L.inter == L.shared_inter &&
+    return T * L.top_k < 32 && T <= MAX_DEC_T && L.top_k <= MAX_DEC_K && L.inter == L.shared_inter &&
            L.hidden <= 4096 && L.inter <= 2048 && chunks_per_lane(L.hidden) <= 2 &&
            chunks_per_lane(L.inter) <= 1;
 }

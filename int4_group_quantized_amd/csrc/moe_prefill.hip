@@ -39,6 +39,7 @@ constexpr int PF_TOK = 64;            // tokens per block of the dense GEMMs: 4 
 constexpr int PF_ROWS = 64;           // output features per block: 4 waves x 16
 constexpr int PF_KS = 128;            // inputs per k step (two groups)
 constexpr int PF_PITCH = PF_KS + 8;   // LDS row pitch in halves (272 bytes: no bank conflicts)
+constexpr int PF_XS_K = 512;          // inputs per block of the split-K x-side GEMMs
 
 struct PfGemm {
     const uint32_t* p[2];
@@ -52,18 +53,18 @@ struct PfGemm {
     int nrb, items;                // row blocks, grid items (a multiple of 8)
     float* out0; float* out1;      // fp32 outputs [row][ostride]
     int ostride;
+    int ksplit;                    // dense: K split over this many blocks (partial outputs)
+    long pstride;                  // elements between the partial outputs of two splits
     uint16_t* hout;                // fp16 silu(out0) * out1, [pair][N]
-    // one extra feature row N (dense, single matrix): read from (xp, xs, xb), written to xout[t]
+    // one extra feature row N (dense, single matrix): read from (xp, xs, xb), written to
+    // xout[split][t]
     const uint32_t* xp; const uint16_t* xs; const uint16_t* xb; float* xout;
-    // LoRA delta in the epilogue (dense, single matrix): out += lscale * B[a_t][n] . z[t]
-    const uint16_t* B; const float* z; int rank, nad; float lscale; const int32_t* adapter;
 };
 
 // GEMM flavours
 constexpr int F_GROUPED = 1;   // work items of the expert sort (else token groups of all tokens)
 constexpr int F_HOUT = 2;      // fp16 silu(out0) * out1 (else fp32 outputs)
 constexpr int F_EXTRA = 4;     // one extra feature row from a second matrix (single matrix)
-constexpr int F_LORA = 8;      // LoRA delta in the epilogue (single matrix)
 
 // LDS of one GEMM block: the activation tile (double buffer: step ks computes from ks % 2
 // while step ks + 1's tile is staged into the other), and with a compile-time step count NS
@@ -139,9 +140,9 @@ template <int NMAT, int BITS, int NT, int FL, int NS, int SM_NMAT>
 __device__ __forceinline__ void pf_gemm_block(const PfGemm& a, int rb, int item,
                                               PfSmem<NT, SM_NMAT, NS>& sm) {
     static_assert(SM_NMAT >= NMAT, "LDS holds the scales of every matrix");
-    constexpr bool GROUPED = FL & F_GROUPED, HOUT = FL & F_HOUT, EXTRA = FL & F_EXTRA, LORA = FL & F_LORA;
+    constexpr bool GROUPED = FL & F_GROUPED, HOUT = FL & F_HOUT, EXTRA = FL & F_EXTRA;
     constexpr int TOKB = 16 * NT;
-    int ntok, e = 0;
+    int ntok, e = 0, split = 0;
     if constexpr (GROUPED) {
         static_assert(!GROUPED || TOKB == PF_ITEM, "one work item per block");
         // the record and the pair ids in one round trip (both indexed by the item alone)
@@ -150,12 +151,14 @@ __device__ __forceinline__ void pf_gemm_block(const PfGemm& a, int rb, int item,
         if (rec.y == 0) return;   // past the last item
         e = rec.x;
         ntok = rec.y;
-        if (threadIdx.x < TOKB) {
-            sm.arow[threadIdx.x] = pair / a.act_div;
-            sm.orow[threadIdx.x] = pair;
-        }
+        // slots past the item's pairs hold no valid pair: their activation rows repeat the
+        // last pair's (their results are never stored)
+        if (threadIdx.x < TOKB) sm.orow[threadIdx.x] = pair;
+        __syncthreads();
+        if (threadIdx.x < TOKB) sm.arow[threadIdx.x] = sm.orow[min((int)threadIdx.x, ntok - 1)] / a.act_div;
     } else {
-        const int t0 = item * TOKB;
+        const int t0 = (item / a.ksplit) * TOKB;
+        split = item % a.ksplit;
         if (t0 >= a.T) return;
         ntok = min(TOKB, a.T - t0);
         if (threadIdx.x < TOKB) {
@@ -165,8 +168,10 @@ __device__ __forceinline__ void pf_gemm_block(const PfGemm& a, int rb, int item,
     }
     __syncthreads();
     const int ntiles = (ntok + 15) >> 4;
-    // NS > 0: the step count known at compile time (K = 128 NS), the loop fully unrolled
-    const int K = NS ? NS * PF_KS : a.K, G = K / 64, nsteps = NS ? NS : K / PF_KS;   // even
+    // NS > 0: the block's step count known at compile time (the loop fully unrolled); the
+    // block covers steps kofs .. kofs + nsteps - 1 of the row (split-K for dense GEMMs)
+    const int K = a.K, G = K / 64, nsteps = NS ? NS : K / PF_KS;   // even
+    const int kofs = split * nsteps;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane & 15, j = lane >> 4;
     const int n = rb * PF_ROWS + wave * 16 + col;              // this lane's feature
@@ -204,8 +209,8 @@ __device__ __forceinline__ void pf_gemm_block(const PfGemm& a, int rb, int item,
                     const uint16_t* ss = sb[m] + (long)min(rowg, a.N - 1) * G;
                     const uint16_t* bs = bb_[m] + (long)min(rowg, a.N - 1) * G;
                     if (EXTRA && rowg >= a.N) { ss = a.xs; bs = a.xb; }
-                    sbr[m][0][i] = reinterpret_cast<const uint4*>(ss)[c8];
-                    sbr[m][1][i] = reinterpret_cast<const uint4*>(bs)[c8];
+                    sbr[m][0][i] = reinterpret_cast<const uint4*>(ss + 2 * kofs)[c8];
+                    sbr[m][1][i] = reinterpret_cast<const uint4*>(bs + 2 * kofs)[c8];
                 }
             }
         }
@@ -247,7 +252,7 @@ __device__ __forceinline__ void pf_gemm_block(const PfGemm& a, int rb, int item,
         ks = min(ks, nsteps - 1);
 #pragma unroll
         for (int q = 0; q < NT; ++q)
-            xr[q] = reinterpret_cast<const uint4*>(a.act + (long)sm.arow[q * 16 + sr] * K + ks * PF_KS)[sc];
+            xr[q] = reinterpret_cast<const uint4*>(a.act + (long)sm.arow[q * 16 + sr] * K + (kofs + ks) * PF_KS)[sc];
     };
     auto commit_x = [&](int buf) {
 #pragma unroll
@@ -259,8 +264,9 @@ __device__ __forceinline__ void pf_gemm_block(const PfGemm& a, int rb, int item,
         ks = min(ks, nsteps - 1);
 #pragma unroll
         for (int m = 0; m < NMAT; ++m) {
-            const uint4* src = EXTRA ? reinterpret_cast<const uint4*>(xw + ks * (PF_KS * BITS / 32))
-                                     : reinterpret_cast<const uint4*>(wb[m] + (woff + (uint32_t)ks * (PF_KS * BITS / 32)));
+            const int kg = kofs + ks;
+            const uint4* src = EXTRA ? reinterpret_cast<const uint4*>(xw + kg * (PF_KS * BITS / 32))
+                                     : reinterpret_cast<const uint4*>(wb[m] + (woff + (uint32_t)kg * (PF_KS * BITS / 32)));
 #pragma unroll
             for (int v = 0; v < WPU; ++v) {
                 const uint4 x = src[v];
@@ -269,11 +275,11 @@ __device__ __forceinline__ void pf_gemm_block(const PfGemm& a, int rb, int item,
             if constexpr (NS > 0) {
                 // scales come from LDS
             } else if constexpr (EXTRA) {
-                sl.s[m] = reinterpret_cast<const uint32_t*>(xs)[ks];
-                sl.b[m] = reinterpret_cast<const uint32_t*>(xb)[ks];
+                sl.s[m] = reinterpret_cast<const uint32_t*>(xs)[kg];
+                sl.b[m] = reinterpret_cast<const uint32_t*>(xb)[kg];
             } else {
-                sl.s[m] = reinterpret_cast<const uint32_t*>(sb[m] + goff)[ks];
-                sl.b[m] = reinterpret_cast<const uint32_t*>(bb_[m] + goff)[ks];
+                sl.s[m] = reinterpret_cast<const uint32_t*>(sb[m] + goff)[kg];
+                sl.b[m] = reinterpret_cast<const uint32_t*>(bb_[m] + goff)[kg];
             }
         }
     };
@@ -395,14 +401,10 @@ __device__ __forceinline__ void pf_gemm_block(const PfGemm& a, int rb, int item,
                 if constexpr (HOUT) {
                     a.hout[(long)orow * a.N + n] = f2h(silu(acc[0][c][r]) * acc[NMAT - 1][c][r]);
                 } else if (extra) {
-                    a.xout[orow] = acc[0][c][r];
+                    a.xout[(long)split * a.T + orow] = acc[0][c][r];
                 } else {
-                    const long o = (long)orow * a.ostride + n;
-                    float v = acc[0][c][r];
-                    if (LORA && a.B)
-                        v = fmaf(a.lscale, lora_b_dot(a.B, adapter_of(a.adapter, orow, a.nad), a.N, n,
-                                                      a.rank, a.z + (long)orow * MAX_RANK), v);
-                    a.out0[o] = v;
+                    const long o = (long)split * a.pstride + (long)orow * a.ostride + n;
+                    a.out0[o] = acc[0][c][r];
                     if (NMAT == 2) a.out1[o] = acc[NMAT - 1][c][r];
                 }
             }
@@ -455,8 +457,8 @@ struct XsideArgs {
     int nb_router, nb_shared, zjobs;
 };
 
-template <int NS>
 __global__ void __launch_bounds__(256) k_pf_xside(XsideArgs xa, MoeArgs a) {
+    constexpr int NS = PF_XS_K / PF_KS;
     __shared__ __align__(16) PfSmem<4, 2, NS> sm;
     const int b = blockIdx.x;
     int rb, item;
@@ -482,46 +484,90 @@ __global__ void __launch_bounds__(256) k_pf_xside(XsideArgs xa, MoeArgs a) {
     if ((threadIdx.x & 63) == 0) (isg ? a.zg : a.zu)[(long)t * MAX_RANK + r] = v;
 }
 
-// Shared expert activation for one token per block: hs = silu(gs + LoRA_gate) * (us +
-// LoRA_up), written to HBM and kept in LDS for the down LoRA's z = A_down hs.
-__global__ void __launch_bounds__(256) k_pf_shared_h(MoeArgs a) {
-    extern __shared__ __align__(16) uint16_t hl[];
-    const int t = blockIdx.x;
+// Per-token finish of the x side, one block per token: sums the split-K partials of the
+// router logits, shared-gate logit and shared gate/up in split order; wave 0 runs top-K on the
+// logits row in LDS while the others go on; hs = silu(gs + LoRA_gate) * (us + LoRA_up) (fp16,
+// to HBM and LDS); then the down LoRA's z = A_down hs, one wave per four rank rows with all
+// of a wave's loads in flight together.
+__global__ void __launch_bounds__(256) k_pf_token(MoeArgs a, int ksplit) {
+    extern __shared__ __align__(16) float tl[];          // logits row [Ep], then hs [SI] fp16
+    __shared__ int sel[MAX_K];
+    __shared__ float sw[MAX_K];
+    float* lrow = tl;
+    uint16_t* hl = reinterpret_cast<uint16_t*>(tl + a.Ep);
+    const int t = blockIdx.x, T = a.T;
+    const long plog = (long)T * a.Ep, pgu = (long)T * a.SI;
+    for (int e = threadIdx.x; e < a.E; e += 256) {
+        float v = 0.0f;
+        for (int s = 0; s < ksplit; ++s) v += a.logits[s * plog + (long)t * a.Ep + e];
+        lrow[e] = v;
+    }
+    if (threadIdx.x == 0) {
+        float v = 0.0f;
+        for (int s = 0; s < ksplit; ++s) v += a.gate[s * T + t];
+        a.gate[t] = v;   // split 0's slot holds the sum (read by the combine)
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        wave_topk(lrow, a.rbias, a.E, a.K, sel, sw);
+        if (threadIdx.x == 0) {   // the lane that wrote the selection
+            for (int r = 0; r < a.K; ++r) {
+                const long i = (long)t * a.K + r;
+                a.idx[i] = sel[r];
+                a.wts[i] = sw[r];
+                if (a.idx_out) a.idx_out[i] = sel[r];
+                if (a.w_out) a.w_out[i] = sw[r];
+            }
+        }
+    }
+    const int adg = adapter_of(a.adapter, t, a.nag), adu = adapter_of(a.adapter, t, a.nau);
     for (int n = threadIdx.x; n < a.SI; n += 256) {
-        const long i = (long)t * a.SI + n;
-        float gv = a.gs[i], uv = a.us[i];
-        if (a.Bg) gv = fmaf(a.lsg, lora_b_dot(a.Bg, adapter_of(a.adapter, t, a.nag), a.SI, n, a.rg, a.zg + (long)t * MAX_RANK), gv);
-        if (a.Bu) uv = fmaf(a.lsu, lora_b_dot(a.Bu, adapter_of(a.adapter, t, a.nau), a.SI, n, a.ru, a.zu + (long)t * MAX_RANK), uv);
+        float gv = 0.0f, uv = 0.0f;
+        for (int s = 0; s < ksplit; ++s) {
+            gv += a.gs[s * pgu + (long)t * a.SI + n];
+            uv += a.us[s * pgu + (long)t * a.SI + n];
+        }
+        if (a.Bg) gv = fmaf(a.lsg, lora_b_dot(a.Bg, adg, a.SI, n, a.rg, a.zg + (long)t * MAX_RANK), gv);
+        if (a.Bu) uv = fmaf(a.lsu, lora_b_dot(a.Bu, adu, a.SI, n, a.ru, a.zu + (long)t * MAX_RANK), uv);
         const uint16_t h = f2h(silu(gv) * uv);
-        a.hs[i] = h;
+        a.hs[(long)t * a.SI + n] = h;
         hl[n] = h;
     }
     if (!a.Ad) return;
     __syncthreads();
-    const int ad = adapter_of(a.adapter, t, a.nad);
-    for (int r = threadIdx.x >> 6; r < a.rd; r += 4) {
-        const float v = wave_dot16(a.Ad + ((long)ad * a.rd + r) * a.SI, hl, a.SI);
-        if ((threadIdx.x & 63) == 0) a.zd[(long)t * MAX_RANK + r] = v;
-    }
-}
-
-// Top-K of every token, one wave per token.
-__global__ void __launch_bounds__(256) k_pf_topk(MoeArgs a) {
-    __shared__ int sel[4][MAX_K];
-    __shared__ float sw[4][MAX_K];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int t = blockIdx.x * 4 + wave;
-    if (t >= a.T) return;
-    wave_topk(a.logits + (long)t * a.Ep, a.rbias, a.E, a.K, sel[wave], sw[wave]);
-    if (lane == 0) {   // the lane that wrote the selection
-        for (int r = 0; r < a.K; ++r) {
-            const long i = (long)t * a.K + r;
-            const int e = sel[wave][r];
-            const float w = sw[wave][r];
-            a.idx[i] = e;
-            a.wts[i] = w;
-            if (a.idx_out) a.idx_out[i] = e;
-            if (a.w_out) a.w_out[i] = w;
+    const int ad = adapter_of(a.adapter, t, a.nad), lane = threadIdx.x & 63;
+    const int SI = a.SI;
+    for (int r0 = (threadIdx.x >> 6) * 4; r0 < a.rd; r0 += 16) {
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int k0 = 0; k0 < SI; k0 += 1024) {   // 1024 inputs per pass: 2 x 8 per lane
+            uint4 av[4][2], xv[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int k = k0 + lane * 8 + i * 512;
+                const bool ok = k < SI;
+                xv[i] = ok ? *reinterpret_cast<const uint4*>(hl + k) : uint4{0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int r = min(r0 + q, a.rd - 1);
+                    av[q][i] = ok ? *reinterpret_cast<const uint4*>(a.Ad + ((long)ad * a.rd + r) * SI + k)
+                                  : uint4{0u, 0u, 0u, 0u};
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const f16x2* xh = reinterpret_cast<const f16x2*>(&xv[i]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f16x2* ah = reinterpret_cast<const f16x2*>(&av[q][i]);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) acc[q] = __builtin_amdgcn_fdot2(ah[u], xh[u], acc[q], false);
+                }
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float v = seg_sum<64>(acc[q]);
+            if (lane == 0 && r0 + q < a.rd) a.zd[(long)t * MAX_RANK + r0 + q] = v;
         }
     }
 }
@@ -557,12 +603,11 @@ __device__ int block_scan_excl(int v, int* wsum, int* total) {
 
 // Stable counting sort of the (token, k) pairs by expert (pair p = t * K + k), written as
 // GEMM work items: chunks of at most PF_ITEM pairs of one expert, each a record (expert,
-// tokens) and its pair ids (the last repeated up to PF_ITEM); records past the last item get
-// zero tokens.  One block of 1024 threads.  Ranks inside each chunk of 64 pairs come from
+// tokens) and its pair ids; records past the last item get zero tokens.  One block of 1024 threads.  Ranks inside each chunk of 64 pairs come from
 // ballots on the expert index bits (lanes with the same expert); the chunks of a segment of
 // 1024 pairs are then offset per expert by a prefix over the segment's 16 chunk counts.
 __global__ void __launch_bounds__(1024) k_pf_sort(MoeArgs a, int max_items) {
-    __shared__ int cnt[1024], base[1024], eoff[1024], ewex[1024], ecnt[1024], wsum[32], tot;
+    __shared__ int cnt[1024], base[1024], eoff[1024], ewex[1024], wsum[32], tot;
     __shared__ uint16_t tab[16][1024];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int E = a.E, TK = a.T * a.K;
@@ -579,7 +624,6 @@ __global__ void __launch_bounds__(1024) k_pf_sort(MoeArgs a, int max_items) {
         base[tid] = excl;
         eoff[tid] = excl;
         ewex[tid] = wex;
-        ecnt[tid] = c;
         for (int w = 0; w < nw; ++w)
             reinterpret_cast<int4*>(a.wrec)[wex + w] = int4{tid, min(PF_ITEM, c - w * PF_ITEM), 0, 0};
     }
@@ -618,12 +662,8 @@ __global__ void __launch_bounds__(1024) k_pf_sort(MoeArgs a, int max_items) {
             const int pos = base[ex] + tab[wave][ex] + rank;
             a.perm[pos] = p;
             // the pair's slot in its work item; the item's last pair also fills the padding
-            const int r = pos - eoff[ex], it = ewex[ex] + r / PF_ITEM, i = r % PF_ITEM;
-            const int n_it = min(PF_ITEM, ecnt[ex] - (r / PF_ITEM) * PF_ITEM);
-            int32_t* dst = a.wpairs + (long)it * PF_ITEM;
-            dst[i] = p;
-            if (i == n_it - 1)
-                for (int q = i + 1; q < PF_ITEM; ++q) dst[q] = p;
+            const int r = pos - eoff[ex];
+            a.wpairs[(long)(ewex[ex] + r / PF_ITEM) * PF_ITEM + r % PF_ITEM] = p;
         }
         __syncthreads();
         if (tid < E) base[tid] += cnt[tid];
@@ -631,17 +671,55 @@ __global__ void __launch_bounds__(1024) k_pf_sort(MoeArgs a, int max_items) {
     }
 }
 
-// y = fp16(sum_k w_k o_k + sigmoid(gate) os) (+ residual), k in order; os already holds the
-// LoRA down delta.  Eight outputs per thread with 16-byte loads.
+// y = fp16(sum_k w_k o_k + sigmoid(gate) (os + LoRA_down)) (+ residual), k in order.  Eight
+// outputs per thread with 16-byte loads; the LoRA-down delta scale * B[a_t][n..n+7] . z_d[t]
+// reads the eight B rows (contiguous) and z once.
 __global__ void __launch_bounds__(256) k_pf_combine(MoeArgs a) {
     const long i8 = ((long)blockIdx.x * 256 + threadIdx.x) * 8;
     if (i8 >= (long)a.T * a.H) return;
     const int t = (int)(i8 / a.H), n = (int)(i8 % a.H);
-    float acc[8];
     const float4* os = reinterpret_cast<const float4*>(a.os + i8);
     const float4 o0 = os[0], o1 = os[1];
-    const float gm = sigmoid(a.gate[t]);
     float ov[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+    if (a.Bd) {
+        const int ad = adapter_of(a.adapter, t, a.nad);
+        const float* z = a.zd + (long)t * MAX_RANK;
+        if ((a.rd & 7) == 0) {
+            // 8 rows of rd halves are 8 * rd contiguous halves: 16-byte loads, 16 ranks a pass
+            const uint4* b4 = reinterpret_cast<const uint4*>(a.Bd + ((long)ad * a.H + n) * a.rd);
+            const int rv = a.rd / 8;   // uint4 per row
+            float d[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            for (int r0 = 0; r0 < rv; r0 += 2) {
+                uint4 bv[8][2];
+                float4 zv[4];
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) bv[q][i] = b4[q * rv + min(r0 + i, rv - 1)];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) zv[i] = reinterpret_cast<const float4*>(z)[min(r0 * 2 + i, 2 * rv - 1)];
+                const float* zf = reinterpret_cast<const float*>(zv);
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    if (r0 + i < rv) {
+#pragma unroll
+                        for (int q = 0; q < 8; ++q) {
+                            const f16* h = reinterpret_cast<const f16*>(&bv[q][i]);
+#pragma unroll
+                            for (int u = 0; u < 8; ++u) d[q] = fmaf((float)h[u], zf[i * 8 + u], d[q]);
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) ov[q] = fmaf(a.lsd, d[q], ov[q]);
+        } else {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) ov[q] = fmaf(a.lsd, lora_b_dot(a.Bd, ad, a.H, n + q, a.rd, z), ov[q]);
+        }
+    }
+    const float gm = sigmoid(a.gate[t]);
+    float acc[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
     for (int k = 0; k < a.K; ++k) {
@@ -664,7 +742,6 @@ __global__ void __launch_bounds__(256) k_pf_combine(MoeArgs a) {
     *reinterpret_cast<uint4*>(a.y + i8) = *reinterpret_cast<const uint4*>(out);
 }
 
-// Launch with the step loop unrolled for the common input sizes (512, 1024, 2048).
 template <int NMAT, int BITS, int NT, int FL>
 void pf_gemm(const PfGemm& p, hipStream_t s) {
     const dim3 grid((unsigned)(p.nrb * p.items));
@@ -684,6 +761,7 @@ PfGemm gemm_args(const QW& w0, const QW* w1, int N, int K, const uint16_t* act, 
     p.p[0] = w0.p; p.s[0] = w0.s; p.b[0] = w0.b;
     if (w1) { p.p[1] = w1->p; p.s[1] = w1->s; p.b[1] = w1->b; }
     p.N = N; p.K = K; p.act = act; p.ostride = N;
+    p.ksplit = 1;
     p.nrb = (feat + PF_ROWS - 1) / PF_ROWS;
     p.items = (items + 7) / 8 * 8;
     return p;
@@ -705,31 +783,30 @@ int prefill_max_items(int E, int T, int K) {
     return (E + (T * K + PF_ITEM - 1) / PF_ITEM + 7) / 8 * 8;
 }
 
+int prefill_ksplit(int hidden) { return hidden / PF_XS_K; }
+
 hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s) {
     const int items = prefill_max_items(a.E, a.T, a.K);
     const int tgroups = (a.T + PF_TOK - 1) / PF_TOK;
+    const int ksplit = prefill_ksplit(a.H);
     const bool all = stage == QMOE_STAGE_ALL;
     if (all || stage == QMOE_STAGE_ROUTE) {
+        // x side: split-K blocks of PF_XS_K inputs write partial sums, k_pf_token adds them
         XsideArgs xa{};
-        xa.router = gemm_args(a.router, nullptr, a.E, a.H, a.x, a.E + 1, tgroups);
+        xa.router = gemm_args(a.router, nullptr, a.E, a.H, a.x, a.E + 1, tgroups * ksplit);
         xa.router.T = a.T;
-        xa.router.out0 = a.logits; xa.router.ostride = a.Ep;
+        xa.router.ksplit = ksplit;
+        xa.router.out0 = a.logits; xa.router.ostride = a.Ep; xa.router.pstride = (long)a.T * a.Ep;
         xa.router.xp = a.sgate.p; xa.router.xs = a.sgate.s; xa.router.xb = a.sgate.b; xa.router.xout = a.gate;
-        xa.shared = gemm_args(a.shg, &a.shu, a.SI, a.H, a.x, a.SI, tgroups);
+        xa.shared = gemm_args(a.shg, &a.shu, a.SI, a.H, a.x, a.SI, tgroups * ksplit);
         xa.shared.T = a.T;
-        xa.shared.out0 = a.gs; xa.shared.out1 = a.us;
+        xa.shared.ksplit = ksplit;
+        xa.shared.out0 = a.gs; xa.shared.out1 = a.us; xa.shared.pstride = (long)a.T * a.SI;
         xa.nb_router = xa.router.nrb * xa.router.items;
         xa.nb_shared = xa.shared.nrb * xa.shared.items;
         xa.zjobs = (a.Ag ? a.T * a.rg : 0) + (a.Au ? a.T * a.ru : 0);
-        const dim3 grid((unsigned)(xa.nb_router + xa.nb_shared + (xa.zjobs + 3) / 4));
-        switch (a.H / PF_KS) {
-            case 4: k_pf_xside<4><<<grid, 256, 0, s>>>(xa, a); break;
-            case 8: k_pf_xside<8><<<grid, 256, 0, s>>>(xa, a); break;
-            case 16: k_pf_xside<16><<<grid, 256, 0, s>>>(xa, a); break;
-            default: k_pf_xside<0><<<grid, 256, 0, s>>>(xa, a); break;
-        }
-        k_pf_shared_h<<<a.T, 256, (size_t)a.SI * 2, s>>>(a);
-        k_pf_topk<<<(a.T + 3) / 4, 256, 0, s>>>(a);
+        k_pf_xside<<<(unsigned)(xa.nb_router + xa.nb_shared + (xa.zjobs + 3) / 4), 256, 0, s>>>(xa, a);
+        k_pf_token<<<a.T, 256, (size_t)a.Ep * 4 + (size_t)a.SI * 2, s>>>(a, ksplit);
         k_pf_sort<<<1, 1024, 0, s>>>(a, items);
     }
     if (all || stage == QMOE_STAGE_GATE_UP) {
@@ -744,8 +821,7 @@ hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s) {
         PfGemm q = gemm_args(a.shd, nullptr, a.H, a.SI, a.hs, a.H, tgroups);
         q.T = a.T;
         q.out0 = a.os;
-        q.B = a.Bd; q.z = a.zd; q.rank = a.rd; q.nad = a.nad; q.lscale = a.lsd; q.adapter = a.adapter;
-        pf_gemm<1, 4, PF_TOK / 16, F_LORA>(q, s);
+        pf_gemm<1, 4, PF_TOK / 16, 0>(q, s);
         k_pf_combine<<<(unsigned)(((long)a.T * a.H / 8 + 255) / 256), 256, 0, s>>>(a);
     }
     return hipGetLastError();

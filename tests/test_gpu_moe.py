@@ -168,6 +168,18 @@ def test_multi_tenant_stack_teacher_forced(q):
         x = moe.residual(x, moe.moe_layer(x, Lc, ad)["y"])
 
 
+def test_decode_path_top8_adapters(q):
+    """Few tokens at top-8 (under the token-sorted path's threshold): the decode kernels'
+    eight-expert case with per-token adapters."""
+    S = Shape(top_k=8, n_adapters=4)
+    wl = synth.Workload.MOE_STACK
+    x = synth.activations(3, S.hidden, wl, 5)
+    ad = np.array([3, 0, 2], np.int32)
+    Lc = build_layer(wl, 5, S, only_experts=routed_experts(x, wl, 5, S))
+    y, idx, w = run_device(q, Lc, S, x, ad, residual=True)
+    check_layer(Lc, x, ad, y, idx, w, residual=True)
+
+
 @pytest.mark.parametrize("T", [23, 100])
 def test_deterministic(q, T):
     Lc = build_layer(synth.Workload.TEST, 13, SMALL)
