@@ -490,9 +490,11 @@ def bench_supergroup(args, q, torch):
            "config": {"workload": f"qlinear_supergroup W[3072x1024] (1 in 4 channels 4-bit, 3 ternary), "
                                   f"x[{B}x1024], {COPIES} weight copies rotated", "global_batch": B,
                       "tflops": flops / (us * 1e-6) / 1e12},
-           "roofline": {"kernel": "k_sg_gemv", "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS,
-                        "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None,
-                        "bytes_per_launch": bytes_, "us_per_launch": us}}
+           "roofline": {"kernel": "k_sg_gemv" if B <= 8 else "k_sg_mfma", "bound": "hbm",
+                        "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": ach / HBM_PEAK_GBS, "traffic": None, "bytes_per_launch": bytes_,
+                        "us_per_launch": us, "mfma_tflops": flops / (us * 1e-6) / 1e12,
+                        "mfma_frac": flops / (us * 1e-6) / 1e12 / FP16_MFMA_PEAK_TFLOPS}}
     return res, (lambda: cpu_baseline_supergroup(B))
 
 

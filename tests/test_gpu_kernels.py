@@ -219,13 +219,28 @@ def test_supergroup_quantize_bit_exact(q, rows, cols, period):
         assert np.array_equal(host(got.p2).view(np.uint32), ref.p2)
 
 
-@pytest.mark.parametrize("b", [1, 3, 64])
+@pytest.mark.parametrize("b", [1, 3, 8, 9, 64, 100])
 def test_supergroup_gemm(q, b):
+    """GEMV (b <= 8) and MFMA (b > 8, ragged token tiles at 9 and 100) forms."""
     rows, cols = 3072, 1024
     w = synth.normal_f32((rows, cols), 0.02, synth.Workload.SUPERGROUP, 0, synth.Role.SUPERGROUP)
     ref, _ = supergroup.quantize(w, 4)
     x = synth.activations(b, cols, synth.Workload.SUPERGROUP, 0, b)
     W_ = q.SuperGroupWeight(dev(ref.p4.view(np.int32)), dev(ref.p2.view(np.int32)), dev(ref.scales),
                             4, rows, cols)
+    y = host(q.qlinear_supergroup(dev(x), W_))
+    assert_close(y, supergroup.gemm(x, ref), what="supergroup")
+
+
+@pytest.mark.parametrize("period,rows,cols,b", [(1, 128, 2048, 20), (2, 200, 1024, 33), (3, 96, 3072, 17),
+                                                (4, 64, 512, 40)])
+def test_supergroup_gemm_shapes(q, period, rows, cols, b):
+    """Other periods (all 4-bit at 1), row counts that are not a multiple of 64, K of two
+    and three 1024-input chunks, and K = 512 (GEMV form) in batched calls."""
+    w = synth.normal_f32((rows, cols), 0.02, synth.Workload.TEST, 21, synth.Role.SUPERGROUP, period)
+    ref, _ = supergroup.quantize(w, period)
+    x = synth.activations(b, cols, synth.Workload.TEST, 21, period)
+    p2 = dev(ref.p2.view(np.int32)) if ref.p2.size else torch.empty(0, dtype=torch.int32, device=DEV)
+    W_ = q.SuperGroupWeight(dev(ref.p4.view(np.int32)), p2, dev(ref.scales), period, rows, cols)
     y = host(q.qlinear_supergroup(dev(x), W_))
     assert_close(y, supergroup.gemm(x, ref), what="supergroup")
