@@ -77,6 +77,30 @@ __device__ __forceinline__ void pair_perm4(const f16* x, f16x2* out) {
     out[1] = f16x2{x[1], x[3]};
 }
 
+// The same permutations on whole dwords (v_perm_b32), for data fresh from a load: taking a
+// loaded register apart into 16-bit halves lets the compiler schedule that split right after
+// the load, and the wait for it then also waits for every load issued before.
+// v = 8 halves x0..x7 as dwords (x0,x1) (x2,x3) (x4,x5) (x6,x7).
+__device__ __forceinline__ uint4 pair_perm8_w(const uint4& v) {   // (x0,x4) (x1,x5) (x2,x6) (x3,x7)
+    return uint4{__builtin_amdgcn_perm(v.z, v.x, 0x05040100u), __builtin_amdgcn_perm(v.z, v.x, 0x07060302u),
+                 __builtin_amdgcn_perm(v.w, v.y, 0x05040100u), __builtin_amdgcn_perm(v.w, v.y, 0x07060302u)};
+}
+__device__ __forceinline__ uint4 pair_perm4x2_w(const uint4& v) {  // (x0,x2) (x1,x3) (x4,x6) (x5,x7)
+    return uint4{__builtin_amdgcn_perm(v.y, v.x, 0x05040100u), __builtin_amdgcn_perm(v.y, v.x, 0x07060302u),
+                 __builtin_amdgcn_perm(v.w, v.z, 0x05040100u), __builtin_amdgcn_perm(v.w, v.z, 0x07060302u)};
+}
+// Sum of the 8 halves in fp32 by dot products against ones (no 16-bit extraction).
+__device__ __forceinline__ float sum8_w(const uint4& v) {
+    const f16x2 one = {(f16)1.0f, (f16)1.0f};
+    float s = __builtin_amdgcn_fdot2(as_h2(v.x), one, 0.0f, false);
+    s = __builtin_amdgcn_fdot2(as_h2(v.y), one, s, false);
+    s = __builtin_amdgcn_fdot2(as_h2(v.z), one, s, false);
+    return __builtin_amdgcn_fdot2(as_h2(v.w), one, s, false);
+}
+// fp32 value of half j (0 = low) of a dword
+__device__ __forceinline__ float half_lo(uint32_t w) { return (float)as_h2(w)[0]; }
+__device__ __forceinline__ float half_hi(uint32_t w) { return (float)as_h2(w)[1]; }
+
 // ---- cross-lane sums without LDS round trips -------------------------------------------
 // DPP controls (gfx9): quad_perm [1,0,3,2] and [2,3,0,1], row_half_mirror (lane i <-> 7-i
 // in each 8), row_mirror (i <-> 15-i in each 16).  After the first two steps the four lanes
@@ -121,6 +145,15 @@ __device__ __forceinline__ int adapter_of(const int32_t* adapter_idx, int t, int
     if (!adapter_idx) return 0;
     const int a = adapter_idx[t];
     return a < 0 ? 0 : (a >= n ? n - 1 : a);
+}
+
+// Pins the first use of a loaded value to this point.  The compiler may otherwise schedule
+// work on a loaded register (splitting it into halves, converting it) right after the load,
+// and the wait for that load then also waits for every load issued before it, since memory
+// waits count in issue order.  After hold(), every read of `v` is of the asm's output, so the
+// wait lands here.
+__device__ __forceinline__ void hold(uint4& v) {
+    asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }

@@ -26,14 +26,7 @@ __device__ __forceinline__ void stage_tokens(const uint16_t* __restrict__ src, c
     for (int u = threadIdx.x; u < mt * units; u += blockDim.x) {
         const int t = u / units, c = u % units;
         const uint4 raw = *reinterpret_cast<const uint4*>(src + (long)rows[t] * K + c * 8);
-        const f16* h = reinterpret_cast<const f16*>(&raw);
-        f16x2* dst = xs + (long)t * (K / 2) + c * 4;
-        if constexpr (BITS == 4) {
-            pair_perm8(h, dst);
-        } else {
-            pair_perm4(h, dst);
-            pair_perm4(h + 4, dst + 2);
-        }
+        reinterpret_cast<uint4*>(xs + (long)t * (K / 2))[c] = BITS == 4 ? pair_perm8_w(raw) : pair_perm4x2_w(raw);
     }
     const int chunks = K / 32;
     for (int u = threadIdx.x; u < mt * chunks; u += blockDim.x) {
@@ -41,24 +34,11 @@ __device__ __forceinline__ void stage_tokens(const uint16_t* __restrict__ src, c
         const uint4* p = reinterpret_cast<const uint4*>(src + (long)rows[t] * K + c * 32);
         float s = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint4 raw = p[i];
-            const f16* h = reinterpret_cast<const f16*>(&raw);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) s += (float)h[j];
-        }
+        for (int i = 0; i < 4; ++i) s += sum8_w(p[i]);
         xsum[t * chunks + c] = s;
     }
 }
 
-// Sum of the 8 fp16 values of a 16-byte vector, in order.
-__device__ __forceinline__ float sum8(const uint4& raw) {
-    const f16* h = reinterpret_cast<const f16*>(&raw);
-    float s = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) s += (float)h[j];
-    return s;
-}
 
 constexpr int NT = 256;   // threads per block of every kernel that stages rows
 
@@ -67,19 +47,11 @@ constexpr int NT = 256;   // threads per block of every kernel that stages rows
 template <int BITS>
 __device__ __forceinline__ void commit_unit(const uint4& raw, int u, bool valid, f16x2* xs,
                                             float* xsum) {
-    float s = valid ? sum8(raw) : 0.0f;
+    float s = valid ? sum8_w(raw) : 0.0f;
     s += dpp<DPP_XOR1>(s);
     s += dpp<DPP_XOR2>(s);
     if (valid) {
-        const f16* h = reinterpret_cast<const f16*>(&raw);
-        f16x2 p[4];
-        if constexpr (BITS == 4) {
-            pair_perm8(h, p);
-        } else {
-            pair_perm4(h, p);
-            pair_perm4(h + 4, p + 2);
-        }
-        reinterpret_cast<uint4*>(xs)[u] = __builtin_bit_cast(uint4, p);   // one 16-byte LDS store
+        reinterpret_cast<uint4*>(xs)[u] = BITS == 4 ? pair_perm8_w(raw) : pair_perm4x2_w(raw);   // one 16-byte LDS store
         if ((threadIdx.x & 3) == 0) xsum[u / 4] = s;
     }
 }

@@ -83,9 +83,12 @@ __device__ __forceinline__ float lora_b_dot(const uint16_t* __restrict__ B, int 
 #pragma unroll
         for (int i = 0; i < MAX_RANK / 8; ++i) {
             if (i < rank / 8) {
-                const f16* h = reinterpret_cast<const f16*>(&v[i]);
+                const uint32_t w4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
-                for (int j = 0; j < 8; ++j) d = fmaf((float)h[j], z[i * 8 + j], d);
+                for (int j = 0; j < 4; ++j) {
+                    d = fmaf(half_lo(w4[j]), z[i * 8 + 2 * j], d);
+                    d = fmaf(half_hi(w4[j]), z[i * 8 + 2 * j + 1], d);
+                }
             }
         }
         return d;

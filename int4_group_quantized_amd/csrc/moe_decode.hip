@@ -204,15 +204,21 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
     const bool one_pass = (K + 1) * (Kd / 8) <= 256 * DN_STAGE;
 
     // phase 1: the routing decision (published by the gate/up stage), the K + 1 activation
-    // rows and the LoRA A_down slices in flight together
-    int sel[MAX_DEC_K];
+    // rows and the LoRA A_down slices in flight together.  Each lane loads the expert of its
+    // own first-pass items first (per-lane loads: a per-lane pick from a uniform array would
+    // become an indexed scratch access whose wait drains every load in flight).
+    const int n_items = (K + 1) * DN_ROWS;
+    const int slots = 4 * rpw;            // lane segments in the block
+    const int slot = wave * rpw + seg;
+    int eit[DN_ITEMS];
+#pragma unroll
+    for (int i = 0; i < DN_ITEMS; ++i) {
+        const int m = min(i * slots + slot, n_items - 1) / DN_ROWS;
+        eit[i] = a.idx[(long)t * K + min(m, K - 1)];
+    }
     float selw[MAX_DEC_K];
 #pragma unroll
-    for (int r = 0; r < MAX_DEC_K; ++r) {
-        const int rc = min(r, K - 1);
-        sel[r] = a.idx[(long)t * K + rc];
-        selw[r] = a.wts[(long)t * K + rc];
-    }
+    for (int r = 0; r < MAX_DEC_K; ++r) selw[r] = a.wts[(long)t * K + min(r, K - 1)];
     const uint16_t* hsrow = a.hs + (long)t * Kd;
     const uint4* hbase4 = reinterpret_cast<const uint4*>(a.h + (long)t * K * Kd);
     const uint4* hsrow4 = reinterpret_cast<const uint4*>(hsrow);
@@ -224,6 +230,23 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
     const int zper = Kd / 16;
     const bool zfast = a.Ad && a.rd <= 16 && zper <= 8 * ZI;
     const int ad = adapter_of(a.adapter, t, a.nad);   // after the loads above are issued
+    // the combine's own inputs (gate logit, residual x, LoRA-B rows of this block's outputs)
+    // are loaded now, not after the dots: one round trip less at the end
+    constexpr int BQ = 2;   // prefetched B rows up to rank 16; larger ranks read B at the end
+    uint4 bq[BQ];
+    float gate_t = 0.0f;
+    uint16_t x_res = 0;
+    const bool bfast = a.Bd && (a.rd & 7) == 0 && a.rd <= 8 * BQ;
+    {   // every thread loads (rows clamped; only threads < DN_ROWS use them): no branch
+        const int nn = min(n0 + (int)(threadIdx.x % DN_ROWS), H - 1);
+        gate_t = a.gate[t];
+        x_res = a.x[(long)t * H + nn];
+        if (bfast) {
+            const uint4* brow = reinterpret_cast<const uint4*>(a.Bd + ((long)ad * H + nn) * a.rd);
+#pragma unroll
+            for (int i = 0; i < BQ; ++i) bq[i] = brow[min(i, a.rd / 8 - 1)];
+        }
+    }
     uint4 av[ZI];
     if (zfast) {
         const uint16_t* arow = a.Ad + ((long)ad * a.rd + min(zrow, a.rd - 1)) * Kd + lane16 * zper;
@@ -231,9 +254,6 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
         for (int i = 0; i < ZI; ++i) av[i] = *reinterpret_cast<const uint4*>(arow + min(i * 8, zper - 8));
     }
     // phase 2: the K + 1 down rows' loads (they need only the routing)
-    const int n_items = (K + 1) * DN_ROWS;
-    const int slots = 4 * rpw;            // lane segments in the block
-    const int slot = wave * rpw + seg;
     RowRegs<4, 1> rr[DN_ITEMS];
     int mi[DN_ITEMS], ri[DN_ITEMS];
     auto load_items = [&](int base) {
@@ -244,10 +264,7 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
             const int m = ic / DN_ROWS, r = ic % DN_ROWS;
             const bool ok = item < n_items && n0 + r < H;
             const int nn = ok ? n0 + r : 0;
-            int e = sel[0];
-#pragma unroll
-            for (int q = 1; q < MAX_DEC_K; ++q)
-                if (q == m) e = sel[q];
+            const int e = base == 0 ? eit[i] : a.idx[(long)t * K + min(m, K - 1)];
             mi[i] = ok ? m : -1;
             ri[i] = r;
             const bool routed = m < K;
@@ -263,15 +280,18 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
     __syncthreads();
     // z_down = A_down[ad] . h_s[t], from the staged h_s in the pair order of A's registers
     if (zfast) {
+#pragma unroll
+        for (int i = 0; i < ZI; ++i) hold(av[i]);
         const f16x2* hp = hs_l + K * (Kd / 2) + lane16 * (zper / 2);
         float acc = 0.0f;
 #pragma unroll
         for (int i = 0; i < ZI; ++i) {
             if (i * 8 < zper) {
-                f16x2 ap[4];
-                pair_perm8(reinterpret_cast<const f16*>(&av[i]), ap);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_fdot2(ap[q], hp[i * 4 + q], acc, false);
+                const uint4 ap = pair_perm8_w(av[i]);
+                acc = __builtin_amdgcn_fdot2(as_h2(ap.x), hp[i * 4 + 0], acc, false);
+                acc = __builtin_amdgcn_fdot2(as_h2(ap.y), hp[i * 4 + 1], acc, false);
+                acc = __builtin_amdgcn_fdot2(as_h2(ap.z), hp[i * 4 + 2], acc, false);
+                acc = __builtin_amdgcn_fdot2(as_h2(ap.w), hp[i * 4 + 3], acc, false);
             }
         }
         acc = seg_sum<16>(acc);
@@ -300,12 +320,29 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
             for (int k = 0; k < MAX_DEC_K; ++k)
                 if (k < K) acc = fmaf(selw[k], o_l[k * DN_ROWS + r], acc);
             float os = o_l[K * DN_ROWS + r];
-            if (a.Bd) os = fmaf(a.lsd, lora_b_dot(a.Bd, ad, H, n, a.rd, zd), os);
-            acc = fmaf(sigmoid(a.gate[t]), os, acc);
+            if (bfast) {
+#pragma unroll
+                for (int i = 0; i < BQ; ++i) hold(bq[i]);
+                float d = 0.0f;
+#pragma unroll
+                for (int i = 0; i < BQ; ++i) {
+                    if (i < a.rd / 8) {
+                        const uint32_t w4[4] = {bq[i].x, bq[i].y, bq[i].z, bq[i].w};
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            d = fmaf(half_lo(w4[u]), zd[i * 8 + 2 * u], d);
+                            d = fmaf(half_hi(w4[u]), zd[i * 8 + 2 * u + 1], d);
+                        }
+                    }
+                }
+                os = fmaf(a.lsd, d, os);
+            } else if (a.Bd) {
+                os = fmaf(a.lsd, lora_b_dot(a.Bd, ad, H, n, a.rd, zd), os);
+            }
+            acc = fmaf(sigmoid(gate_t), os, acc);
             uint16_t outv = f2h(acc);
-            const long i = (long)t * H + n;
-            if (a.add_residual) outv = f2h(h2f(a.x[i]) + h2f(outv));
-            a.y[i] = outv;
+            if (a.add_residual) outv = f2h(h2f(x_res) + h2f(outv));
+            a.y[(long)t * H + n] = outv;
         }
     }
 }

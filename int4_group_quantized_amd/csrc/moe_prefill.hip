@@ -81,15 +81,7 @@ struct PfSmem {
 // the unpacking.
 template <int BITS>
 __device__ __forceinline__ void pf_commit(const uint4& raw, int r, int c, f16* tile) {
-    const f16* h = reinterpret_cast<const f16*>(&raw);
-    f16x2 p[4];
-    if constexpr (BITS == 4) {
-        pair_perm8(h, p);
-    } else {
-        pair_perm4(h, p);
-        pair_perm4(h + 4, p + 2);
-    }
-    *reinterpret_cast<uint4*>(tile + r * PF_PITCH + c * 8) = __builtin_bit_cast(uint4, p);
+    *reinterpret_cast<uint4*>(tile + r * PF_PITCH + c * 8) = BITS == 4 ? pair_perm8_w(raw) : pair_perm4x2_w(raw);
 }
 
 // fp16 codes C + q of one 8-input unit in pair order (4-bit: one word, pairs (q_j, q_j+4);
@@ -704,9 +696,12 @@ __global__ void __launch_bounds__(256) k_pf_combine(MoeArgs a) {
                     if (r0 + i < rv) {
 #pragma unroll
                         for (int q = 0; q < 8; ++q) {
-                            const f16* h = reinterpret_cast<const f16*>(&bv[q][i]);
+                            const uint32_t w4[4] = {bv[q][i].x, bv[q][i].y, bv[q][i].z, bv[q][i].w};
 #pragma unroll
-                            for (int u = 0; u < 8; ++u) d[q] = fmaf((float)h[u], zf[i * 8 + u], d[q]);
+                            for (int u = 0; u < 4; ++u) {
+                                d[q] = fmaf(half_lo(w4[u]), zf[i * 8 + 2 * u], d[q]);
+                                d[q] = fmaf(half_hi(w4[u]), zf[i * 8 + 2 * u + 1], d[q]);
+                            }
                         }
                     }
                 }
