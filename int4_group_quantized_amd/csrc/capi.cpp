@@ -49,7 +49,7 @@ int check_lora(const qmoe_lora* l, int in_dim, int out_dim) {
     if (l->rank > 64) return QMOE_ERR_UNSUPPORTED;
     if (l->in_dim != in_dim || l->out_dim != out_dim) return QMOE_ERR_INVALID_ARG;
     if (l->in_dim % 512 != 0) return QMOE_ERR_UNSUPPORTED;
-    if (!aligned16(l->A)) return QMOE_ERR_MISALIGNED;
+    if (!aligned16(l->A) || !aligned16(l->B)) return QMOE_ERR_MISALIGNED;
     return QMOE_OK;
 }
 

@@ -42,8 +42,9 @@ Layout layout_of(const qmoe_moe_layer& L, int T) {
     const size_t ks = (size_t)prefill_ksplit(L.hidden);   // split-K partials of the x side
     l.logits = take(ks * T * ((L.n_experts + 63) / 64 * 64) * 4);
     l.gate = take(ks * T * 4);
-    l.zg = take((size_t)T * MAX_RANK * 4);
-    l.zu = take((size_t)T * MAX_RANK * 4);
+    // LoRA z of gate and up: partial sums per 256 inputs (prefill), the first slice for decode
+    l.zg = take((size_t)(L.hidden / 256) * T * MAX_RANK * 4);
+    l.zu = take((size_t)(L.hidden / 256) * T * MAX_RANK * 4);
     l.zd = take((size_t)T * MAX_RANK * 4);
     l.gs = take(ks * T * L.shared_inter * 4);
     l.us = take(ks * T * L.shared_inter * 4);

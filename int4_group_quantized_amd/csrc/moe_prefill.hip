@@ -412,6 +412,22 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) k
     pf_gemm_block<NMAT, BITS, NT, FL, NS, NMAT>(a, rb, item, sm);
 }
 
+// The grouped down GEMM and the shared expert's dense down GEMM in one launch (they are
+// independent; equal inner sizes, so one step count): blocks below nbg take work items.
+template <int NS>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
+k_pf_down(PfGemm g, PfGemm d, int nbg) {
+    __shared__ __align__(16) PfSmem<PF_ITEM / 16, 1, NS> sm;
+    int rb, item;
+    if ((int)blockIdx.x < nbg) {
+        pf_block(blockIdx.x, g.nrb, rb, item);
+        pf_gemm_block<1, 4, PF_ITEM / 16, F_GROUPED, NS, 1>(g, rb, item, sm);
+    } else {
+        pf_block(blockIdx.x - nbg, d.nrb, rb, item);
+        pf_gemm_block<1, 4, PF_ITEM / 16, 0, NS, 1>(d, rb, item, sm);
+    }
+}
+
 // v . A-row over K inputs in one wave (fp16 x fp16 into fp32), every load of a 4096-input
 // chunk issued before its sum.
 __device__ __forceinline__ float wave_dot16(const uint16_t* __restrict__ arow,
@@ -441,14 +457,55 @@ __device__ __forceinline__ float wave_dot16(const uint16_t* __restrict__ arow,
     return seg_sum<64>(acc);
 }
 
-// x side of the layer in one launch: the router rows plus the shared-gate row (8-bit), the
-// shared expert's gate and up (int4), then the LoRA down-projections of x (one wave per
-// (projection, token, rank row)).
+// Partial LoRA z over inputs k0 .. k0 + 255 for adapter ad: zpart[t][r] = A[ad][r][k0..] .
+// v[t][k0..] for those of the 16 tokens t0.. that use adapter ad and 16 rank rows r0.. of one
+// projection.  One wave, 8 MFMAs with every load issued first: the tokens' v as A and the fp16
+// LoRA rows as B, both straight from memory in the same k order; fp16 products are exact in
+// fp32.  A wave whose adapter no token of the tile uses returns at once.
+__device__ void lora_z_chunk(const uint16_t* __restrict__ v, int T, int K,
+                             const uint16_t* __restrict__ A, int rank, int nad, int ad,
+                             const int32_t* __restrict__ adapter, float* __restrict__ zpart,
+                             int t0, int r0, int k0) {
+    const int lane = threadIdx.x & 63, col = lane & 15, j = lane >> 4;
+    const int tok = min(t0 + col, T - 1);
+    if (!__any(lane < 16 && t0 + col < T && adapter_of(adapter, tok, nad) == ad)) return;
+    const int rrow = min(r0 + col, rank - 1);
+    const uint16_t* vrow = v + (long)tok * K + k0 + 8 * j;
+    const uint16_t* arow = A + ((long)ad * rank + rrow) * K + k0 + 8 * j;
+    uint4 xa[8], wb[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        xa[m] = *reinterpret_cast<const uint4*>(vrow + 32 * m);
+        wb[m] = *reinterpret_cast<const uint4*>(arow + 32 * m);
+    }
+    int tad[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) tad[q] = adapter_of(adapter, min(t0 + 4 * j + q, T - 1), nad);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, xa[m]),
+                                                     __builtin_bit_cast(f16x8, wb[m]), acc, 0, 0, 0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int t = t0 + 4 * j + q;
+        if (t < T && tad[q] == ad && r0 + col < rank) zpart[(long)t * MAX_RANK + r0 + col] = acc[q];
+    }
+}
+
 struct XsideArgs {
     PfGemm router, shared;
     int nb_router, nb_shared, zjobs;
 };
 
+// LoRA z jobs of one projection: (adapter, 16-token tile, 16-row rank tile, 256-input chunk).
+__host__ __device__ inline int lora_z_jobs(int T, int H, int rank, int nad) {
+    return nad * ((T + 15) / 16) * ((rank + 15) / 16) * (H / 256);
+}
+
+// x side of the layer in one launch: the router rows plus the shared-gate row (8-bit), the
+// shared expert's gate and up (int4), all as split-K partial sums, then the LoRA z's of the
+// shared gate and up as partial sums over 256-input chunks (one wave per lora_z_chunk job).
 __global__ void __launch_bounds__(256) k_pf_xside(XsideArgs xa, MoeArgs a) {
     constexpr int NS = PF_XS_K / PF_KS;
     __shared__ __align__(16) PfSmem<4, 2, NS> sm;
@@ -466,100 +523,247 @@ __global__ void __launch_bounds__(256) k_pf_xside(XsideArgs xa, MoeArgs a) {
     }
     const int jb = (b - xa.nb_router - xa.nb_shared) * 4 + (threadIdx.x >> 6);
     if (jb >= xa.zjobs) return;
-    const int ng = a.Ag ? a.T * a.rg : 0;
+    const int ng = a.Ag ? lora_z_jobs(a.T, a.H, a.rg, a.nag) : 0;
     const bool isg = jb < ng;
-    const int jj = isg ? jb : jb - ng;
-    const int rank = isg ? a.rg : a.ru;
-    const int t = jj / rank, r = jj % rank;
-    const int ad = adapter_of(a.adapter, t, isg ? a.nag : a.nau);
-    const float v = wave_dot16((isg ? a.Ag : a.Au) + ((long)ad * rank + r) * a.H, a.x + (long)t * a.H, a.H);
-    if ((threadIdx.x & 63) == 0) (isg ? a.zg : a.zu)[(long)t * MAX_RANK + r] = v;
+    int jj = isg ? jb : jb - ng;
+    const int rank = isg ? a.rg : a.ru, nad = isg ? a.nag : a.nau;
+    const int kc = a.H / 256, rtiles = (rank + 15) / 16, tt = (a.T + 15) / 16;
+    const int c = jj % kc;
+    jj /= kc;
+    const int rt = jj % rtiles;
+    jj /= rtiles;
+    const int tile = jj % tt, ad = jj / tt;
+    lora_z_chunk(a.x, a.T, a.H, isg ? a.Ag : a.Au, rank, nad, ad, a.adapter,
+                 (isg ? a.zg : a.zu) + (long)c * a.T * MAX_RANK, tile * 16, rt * 16, c * 256);
 }
 
-// Per-token finish of the x side, one block per token: sums the split-K partials of the
-// router logits, shared-gate logit and shared gate/up in split order; wave 0 runs top-K on the
-// logits row in LDS while the others go on; hs = silu(gs + LoRA_gate) * (us + LoRA_up) (fp16,
-// to HBM and LDS); then the down LoRA's z = A_down hs, one wave per four rank rows with all
-// of a wave's loads in flight together.
+// The n <= KP split-K partials p[s * stride] of one value, every load issued at once (index
+// clamped into the n partials), summed in split order.
+template <int KP>
+struct Parts {
+    float v[KP];
+    __device__ __forceinline__ void load(const float* __restrict__ p, long stride, int n) {
+#pragma unroll
+        for (int s = 0; s < KP; ++s) v[s] = p[(long)min(s, n - 1) * stride];
+    }
+    __device__ __forceinline__ float sum(int n) const {
+        float acc = 0.0f;
+#pragma unroll
+        for (int s = 0; s < KP; ++s) acc += s < n ? v[s] : 0.0f;
+        return acc;
+    }
+};
+
+// Wave 0 of k_pf_token: the token's router logits (split-K sums, PER per lane, in registers)
+// plus the selection bias, then top-K; lane 0 leaves the experts and weights in sel / sw.
+template <int PER, int KP>
+__device__ void token_topk(const MoeArgs& a, int t, int ksplit, int* sel, float* sw) {
+    const int lane = threadIdx.x & 63;
+    TopkKeys<PER, false> keys;
+    keys.has_bias = a.rbias != nullptr;
+    const float* bias = keys.has_bias ? a.rbias : a.logits;   // read either way, used if bias
+    Parts<KP> p[PER];
+    float b[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int e = min(lane * PER + i, a.E - 1);
+        p[i].load(a.logits + (long)t * a.Ep + e, (long)a.T * a.Ep, ksplit);
+        b[i] = bias[e];
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        keys.raw[i] = p[i].sum(ksplit);
+        keys.braw[i] = keys.has_bias ? b[i] : 0.0f;
+    }
+    keys.select(a.E, a.K, sel, sw);
+}
+
+template <int KP>
+__device__ void token_topk_any(const MoeArgs& a, int t, int ksplit, int* sel, float* sw) {
+    switch (topk_per_lane(a.E)) {
+        case 1: token_topk<1, KP>(a, t, ksplit, sel, sw); break;
+        case 2: token_topk<2, KP>(a, t, ksplit, sel, sw); break;
+        case 4: token_topk<4, KP>(a, t, ksplit, sel, sw); break;
+        case 8: token_topk<8, KP>(a, t, ksplit, sel, sw); break;
+        default: token_topk<16, KP>(a, t, ksplit, sel, sw); break;
+    }
+}
+
+// LoRA-B term of one output row from 16 rank entries held as two uint4 (entries r < rank
+// count), z from LDS.
+__device__ __forceinline__ float bdot16(const uint4 (&v)[2], const float* z, int rank) {
+    float d = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        if (8 * i < rank) {
+            const uint32_t w4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                d = fmaf(half_lo(w4[j]), z[8 * i + 2 * j], d);
+                d = fmaf(half_hi(w4[j]), z[8 * i + 2 * j + 1], d);
+            }
+        }
+    }
+    return d;
+}
+
+// The remaining rank entries 16 .. rank - 1 (rank a multiple of 8) of the same dot.
+__device__ __forceinline__ float bdot_tail(const uint16_t* __restrict__ brow, const float* z,
+                                           int rank, float d) {
+    for (int r = 16; r < rank; r += 8) {
+        const uint4 v = *reinterpret_cast<const uint4*>(brow + r);
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            d = fmaf(half_lo(w4[j]), z[r + 2 * j], d);
+            d = fmaf(half_hi(w4[j]), z[r + 2 * j + 1], d);
+        }
+    }
+    return d;
+}
+
+constexpr int TOK_HW = 3;   // waves of k_pf_token on the shared expert's h
+constexpr int TOK_NPC = 4;  // h outputs per thread whose loads are issued together
+
+// Per-token finish of the x side, one block of 4 waves per token.  Wave 0 sums the token's
+// router-logit partials in registers and runs top-K.  Waves 1-3 sum the shared-gate logit and
+// (each for itself, into its own LDS row) the LoRA z's of gate and up, then h_s =
+// silu(g_s + LoRA_g) * (u_s + LoRA_u), every load of TOK_NPC outputs issued together; h_s goes to
+// LDS.  Every wave meanwhile fetches its first rows of the down LoRA's A.  After the one barrier:
+// h_s and the selection are written out and z_d = A_down h_s is taken, one wave per four rank
+// rows.  Split-K partials are added in split order, LoRA chunks in chunk order.
+template <int KP>
 __global__ void __launch_bounds__(256) k_pf_token(MoeArgs a, int ksplit) {
-    extern __shared__ __align__(16) float tl[];          // logits row [Ep], then hs [SI] fp16
+    extern __shared__ __align__(16) uint16_t hl[];        // h_s of the token, fp16 [SI]
     __shared__ int sel[MAX_K];
     __shared__ float sw[MAX_K];
-    float* lrow = tl;
-    uint16_t* hl = reinterpret_cast<uint16_t*>(tl + a.Ep);
-    const int t = blockIdx.x, T = a.T;
-    const long plog = (long)T * a.Ep, pgu = (long)T * a.SI;
-    for (int e = threadIdx.x; e < a.E; e += 256) {
-        float v = 0.0f;
-        for (int s = 0; s < ksplit; ++s) v += a.logits[s * plog + (long)t * a.Ep + e];
-        lrow[e] = v;
-    }
-    if (threadIdx.x == 0) {
-        float v = 0.0f;
-        for (int s = 0; s < ksplit; ++s) v += a.gate[s * T + t];
-        a.gate[t] = v;   // split 0's slot holds the sum (read by the combine)
-    }
-    __syncthreads();
-    if (threadIdx.x < 64) {
-        wave_topk(lrow, a.rbias, a.E, a.K, sel, sw);
-        if (threadIdx.x == 0) {   // the lane that wrote the selection
-            for (int r = 0; r < a.K; ++r) {
-                const long i = (long)t * a.K + r;
-                a.idx[i] = sel[r];
-                a.wts[i] = sw[r];
-                if (a.idx_out) a.idx_out[i] = sel[r];
-                if (a.w_out) a.w_out[i] = sw[r];
-            }
-        }
-    }
-    const int adg = adapter_of(a.adapter, t, a.nag), adu = adapter_of(a.adapter, t, a.nau);
-    for (int n = threadIdx.x; n < a.SI; n += 256) {
-        float gv = 0.0f, uv = 0.0f;
-        for (int s = 0; s < ksplit; ++s) {
-            gv += a.gs[s * pgu + (long)t * a.SI + n];
-            uv += a.us[s * pgu + (long)t * a.SI + n];
-        }
-        if (a.Bg) gv = fmaf(a.lsg, lora_b_dot(a.Bg, adg, a.SI, n, a.rg, a.zg + (long)t * MAX_RANK), gv);
-        if (a.Bu) uv = fmaf(a.lsu, lora_b_dot(a.Bu, adu, a.SI, n, a.ru, a.zu + (long)t * MAX_RANK), uv);
-        const uint16_t h = f2h(silu(gv) * uv);
-        a.hs[(long)t * a.SI + n] = h;
-        hl[n] = h;
-    }
-    if (!a.Ad) return;
-    __syncthreads();
-    const int ad = adapter_of(a.adapter, t, a.nad), lane = threadIdx.x & 63;
-    const int SI = a.SI;
-    for (int r0 = (threadIdx.x >> 6) * 4; r0 < a.rd; r0 += 16) {
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int k0 = 0; k0 < SI; k0 += 1024) {   // 1024 inputs per pass: 2 x 8 per lane
-            uint4 av[4][2], xv[2];
+    __shared__ float zw[TOK_HW][2][MAX_RANK];
+    const int t = blockIdx.x, T = a.T, SI = a.SI;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+
+    // first rows of the down LoRA: rows 4 wave .. + 3, inputs lane * 8 + 512 i (clamped)
+    const bool has_d = a.Ad != nullptr;
+    const uint16_t* abase = has_d ? a.Ad + (long)adapter_of(a.adapter, t, a.nad) * a.rd * SI : a.hs;
+    const long astride = has_d ? SI : 0;
+    const int rd = has_d ? a.rd : 0;
+    uint4 av0[4][2];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int k = k0 + lane * 8 + i * 512;
-                const bool ok = k < SI;
-                xv[i] = ok ? *reinterpret_cast<const uint4*>(hl + k) : uint4{0u, 0u, 0u, 0u};
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int r = min(r0 + q, a.rd - 1);
-                    av[q][i] = ok ? *reinterpret_cast<const uint4*>(a.Ad + ((long)ad * a.rd + r) * SI + k)
-                                  : uint4{0u, 0u, 0u, 0u};
+        for (int i = 0; i < 2; ++i)
+            av0[q][i] = *reinterpret_cast<const uint4*>(abase + min(4 * wave + q, max(rd - 1, 0)) * astride +
+                                                        min(lane * 8 + i * 512, SI - 8));
+
+    if (wave == 0) {
+        token_topk_any<KP>(a, t, ksplit, sel, sw);
+    } else {
+        const int w = wave - 1, u = threadIdx.x - 64;
+        Parts<KP> g;   // the shared-gate logit (every lane loads, one stores)
+        g.load(a.gate + t, T, ksplit);
+        const long pz = (long)T * MAX_RANK, pgu = (long)T * SI;
+        const int kc = a.H / 256;
+        Parts<2 * KP> zg, zu;
+        zg.load(a.zg + (long)t * MAX_RANK + lane, pz, kc);
+        zu.load(a.zu + (long)t * MAX_RANK + lane, pz, kc);
+        const int adg = adapter_of(a.adapter, t, a.nag), adu = adapter_of(a.adapter, t, a.nau);
+        const bool fg = a.Bg && (a.rg & 7) == 0, fu = a.Bu && (a.ru & 7) == 0;
+        const uint16_t* gb = fg ? a.Bg + (long)adg * SI * a.rg : a.hs;
+        const uint16_t* ub = fu ? a.Bu + (long)adu * SI * a.ru : a.hs;
+        const int gs = fg ? a.rg : 0, us = fu ? a.ru : 0;
+        const int g8 = max(min(a.rg, 16) - 8, 0), u8 = max(min(a.ru, 16) - 8, 0);
+        bool first = true;
+        for (int n0 = u; n0 < SI; n0 += TOK_NPC * TOK_HW * 64) {
+            Parts<KP> pg[TOK_NPC], pu[TOK_NPC];
+            uint4 bg[TOK_NPC][2], bu[TOK_NPC][2];
+#pragma unroll
+            for (int c = 0; c < TOK_NPC; ++c) {
+                const int n = min(n0 + c * TOK_HW * 64, SI - 1);
+                pg[c].load(a.gs + (long)t * SI + n, pgu, ksplit);
+                pu[c].load(a.us + (long)t * SI + n, pgu, ksplit);
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    bg[c][i] = *reinterpret_cast<const uint4*>(gb + (long)n * gs + min(8 * i, g8));
+                    bu[c][i] = *reinterpret_cast<const uint4*>(ub + (long)n * us + min(8 * i, u8));
                 }
             }
+            if (first) {   // this wave's LoRA z's, read back by every lane below
+                zw[w][0][lane] = zg.sum(kc);
+                zw[w][1][lane] = zu.sum(kc);
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                first = false;
+            }
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const f16x2* xh = reinterpret_cast<const f16x2*>(&xv[i]);
+            for (int c = 0; c < TOK_NPC; ++c) {
+                const int n = n0 + c * TOK_HW * 64;
+                if (n < SI) {
+                    float gv = pg[c].sum(ksplit), uv = pu[c].sum(ksplit);
+                    if (a.Bg) {
+                        const float d = fg ? bdot_tail(gb + (long)n * gs, zw[w][0], a.rg, bdot16(bg[c], zw[w][0], a.rg))
+                                           : lora_b_dot(a.Bg, adg, SI, n, a.rg, zw[w][0]);
+                        gv = fmaf(a.lsg, d, gv);
+                    }
+                    if (a.Bu) {
+                        const float d = fu ? bdot_tail(ub + (long)n * us, zw[w][1], a.ru, bdot16(bu[c], zw[w][1], a.ru))
+                                           : lora_b_dot(a.Bu, adu, SI, n, a.ru, zw[w][1]);
+                        uv = fmaf(a.lsu, d, uv);
+                    }
+                    hl[n] = f2h(silu(gv) * uv);
+                }
+            }
+        }
+        if (u == 0) a.gate[t] = g.sum(ksplit);   // split 0's slot holds the sum
+    }
+    __syncthreads();
+
+    for (int n = threadIdx.x * 8; n < SI; n += 256 * 8)
+        *reinterpret_cast<uint4*>(a.hs + (long)t * SI + n) = *reinterpret_cast<const uint4*>(hl + n);
+    if (threadIdx.x < a.K) {
+        const long i = (long)t * a.K + threadIdx.x;
+        a.idx[i] = sel[threadIdx.x];
+        a.wts[i] = sw[threadIdx.x];
+        if (a.idx_out) a.idx_out[i] = sel[threadIdx.x];
+        if (a.w_out) a.w_out[i] = sw[threadIdx.x];
+    }
+    if (!has_d) return;
+    // z_d: rows r0 .. r0 + 3 per wave, 1024 inputs (2 x 8 per lane) per pass
+    auto pass = [&](const uint4 (&av)[4][2], int k0, float (&acc)[4]) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int k = k0 + lane * 8 + i * 512;
+            if (k < SI) {
+                const uint4 xv = *reinterpret_cast<const uint4*>(hl + k);
+                const f16x2* xh = reinterpret_cast<const f16x2*>(&xv);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const f16x2* ah = reinterpret_cast<const f16x2*>(&av[q][i]);
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) acc[q] = __builtin_amdgcn_fdot2(ah[u], xh[u], acc[q], false);
+                    for (int e = 0; e < 4; ++e) acc[q] = __builtin_amdgcn_fdot2(ah[e], xh[e], acc[q], false);
                 }
+            }
+        }
+    };
+    for (int r0 = 4 * wave; r0 < rd; r0 += 16) {
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int k0 = 0; k0 < SI; k0 += 1024) {
+            if (r0 == 4 * wave && k0 == 0) {
+                pass(av0, 0, acc);
+            } else {
+                uint4 av[4][2];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+                        av[q][i] = *reinterpret_cast<const uint4*>(abase + min(r0 + q, rd - 1) * astride +
+                                                                   min(k0 + lane * 8 + i * 512, SI - 8));
+                pass(av, k0, acc);
             }
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const float v = seg_sum<64>(acc[q]);
-            if (lane == 0 && r0 + q < a.rd) a.zd[(long)t * MAX_RANK + r0 + q] = v;
+            if (lane == 0 && r0 + q < rd) a.zd[(long)t * MAX_RANK + r0 + q] = v;
         }
     }
 }
@@ -717,13 +921,26 @@ __global__ void __launch_bounds__(256) k_pf_combine(MoeArgs a) {
     float acc[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
-    for (int k = 0; k < a.K; ++k) {
-        const float w = a.wts[(long)t * a.K + k];
-        const float4* ok = reinterpret_cast<const float4*>(a.o + ((long)t * a.K + k) * a.H + n);
-        const float4 p0 = ok[0], p1 = ok[1];
-        const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+    for (int k0 = 0; k0 < a.K; k0 += 4) {   // four experts' rows in flight at a time
+        float4 p[4][2];
+        float w[4];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) acc[q] = fmaf(w, pv[q], acc[q]);
+        for (int u = 0; u < 4; ++u) {
+            const int k = min(k0 + u, a.K - 1);
+            w[u] = a.wts[(long)t * a.K + k];
+            const float4* ok = reinterpret_cast<const float4*>(a.o + ((long)t * a.K + k) * a.H + n);
+            p[u][0] = ok[0];
+            p[u][1] = ok[1];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (k0 + u < a.K) {
+                const float pv[8] = {p[u][0].x, p[u][0].y, p[u][0].z, p[u][0].w,
+                                     p[u][1].x, p[u][1].y, p[u][1].z, p[u][1].w};
+#pragma unroll
+                for (int q = 0; q < 8; ++q) acc[q] = fmaf(w[u], pv[q], acc[q]);
+            }
+        }
     }
     uint16_t out[8];
 #pragma unroll
@@ -799,9 +1016,12 @@ hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s) {
         xa.shared.out0 = a.gs; xa.shared.out1 = a.us; xa.shared.pstride = (long)a.T * a.SI;
         xa.nb_router = xa.router.nrb * xa.router.items;
         xa.nb_shared = xa.shared.nrb * xa.shared.items;
-        xa.zjobs = (a.Ag ? a.T * a.rg : 0) + (a.Au ? a.T * a.ru : 0);
+        xa.zjobs = (a.Ag ? lora_z_jobs(a.T, a.H, a.rg, a.nag) : 0) + (a.Au ? lora_z_jobs(a.T, a.H, a.ru, a.nau) : 0);
         k_pf_xside<<<(unsigned)(xa.nb_router + xa.nb_shared + (xa.zjobs + 3) / 4), 256, 0, s>>>(xa, a);
-        k_pf_token<<<a.T, 256, (size_t)a.Ep * 4 + (size_t)a.SI * 2, s>>>(a, ksplit);
+        const size_t tsm = (size_t)a.SI * 2;   // hidden <= 4096: at most 8 splits
+        if (ksplit <= 2) k_pf_token<2><<<a.T, 256, tsm, s>>>(a, ksplit);
+        else if (ksplit <= 4) k_pf_token<4><<<a.T, 256, tsm, s>>>(a, ksplit);
+        else k_pf_token<8><<<a.T, 256, tsm, s>>>(a, ksplit);
         k_pf_sort<<<1, 1024, 0, s>>>(a, items);
     }
     if (all || stage == QMOE_STAGE_GATE_UP) {
@@ -812,11 +1032,21 @@ hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s) {
     if (all || stage == QMOE_STAGE_DOWN) {
         PfGemm p = grouped(a, a.ed, nullptr, a.H, a.I, a.h, 1, items);
         p.out0 = a.o;
-        pf_gemm<1, 4, PF_ITEM / 16, F_GROUPED>(p, s);
-        PfGemm q = gemm_args(a.shd, nullptr, a.H, a.SI, a.hs, a.H, tgroups);
+        PfGemm q = gemm_args(a.shd, nullptr, a.H, a.SI, a.hs, a.H, (a.T + PF_ITEM - 1) / PF_ITEM);
         q.T = a.T;
         q.out0 = a.os;
-        pf_gemm<1, 4, PF_TOK / 16, 0>(q, s);
+        const int nbg = p.nrb * p.items;
+        const dim3 grid((unsigned)(nbg + q.nrb * q.items));
+        if (a.I == a.SI && (a.I == 512 || a.I == 1024 || a.I == 2048)) {
+            switch (a.I / PF_KS) {
+                case 4: k_pf_down<4><<<grid, 256, 0, s>>>(p, q, nbg); break;
+                case 8: k_pf_down<8><<<grid, 256, 0, s>>>(p, q, nbg); break;
+                default: k_pf_down<16><<<grid, 256, 0, s>>>(p, q, nbg); break;
+            }
+        } else {
+            pf_gemm<1, 4, PF_ITEM / 16, F_GROUPED>(p, s);
+            pf_gemm<1, 4, PF_ITEM / 16, 0>(q, s);
+        }
         k_pf_combine<<<(unsigned)(((long)a.T * a.H / 8 + 255) / 256), 256, 0, s>>>(a);
     }
     return hipGetLastError();
