@@ -12,7 +12,7 @@ constexpr int MAX_RANK = 64;
 constexpr int MAX_K = 32;
 constexpr int MAX_DEC_T = 32;  // the decode path serves up to this many tokens per call
 constexpr int MAX_DEC_K = 8;   // ... and up to this many experts per token
-constexpr int PF_ITEM = 32;    // pairs per work item of the token-sorted GEMMs
+constexpr int PF_ITEM = 32;    // most pairs per work item of the token-sorted GEMMs (slots per item)
 
 struct QW {
     const uint32_t* p;
@@ -36,7 +36,7 @@ struct MoeArgs {
     float *logits, *gate, *zg, *zu, *zd, *gs, *us;
     int32_t *idx, *offs, *perm;
     int32_t* wrec;     // per work item of the token-sorted GEMMs: (expert, tokens, 0, 0)
-    int32_t* wpairs;   // per work item: PF_ITEM pair ids, the last one repeated
+    int32_t* wpairs;   // per work item: PF_ITEM slots of pair ids (the item's count used)
     float* wts;
     uint16_t *h, *hs;
     float *o, *os;
@@ -176,6 +176,7 @@ bool decode_path_fits(const qmoe_moe_layer& L, int T);
 hipError_t launch_moe_decode(const MoeArgs& a, int stage, hipStream_t s);
 // moe_prefill.hip
 int prefill_max_items(int E, int T, int K);
+int prefill_item_size(int E, int T, int K);
 int prefill_ksplit(int hidden);
 hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s);
 

@@ -122,36 +122,31 @@ struct PfSlot {
     uint32_t s[NMAT], b[NMAT];        // the step's two groups as fp16 pairs
 };
 
-// One block of the GEMM: features rb*64 .. +63 (16 per wave) of item `item`, up to NT
-// tiles of 16 tokens.  Weights and activations are loaded two steps ahead: the weights into
-// two register slots (the loop unrolled by two), the activations into registers that are
-// staged into the LDS double buffer one step later, so neither wait sits on a step's
-// critical path.  The weight rows of one block share a base address (the expert's matrix)
-// held in scalar registers; a lane only keeps 32-bit offsets.
-template <int NMAT, int BITS, int NT, int FL, int NS, int SM_NMAT>
-__device__ __forceinline__ void pf_gemm_block(const PfGemm& a, int rb, int item,
-                                              PfSmem<NT, SM_NMAT, NS>& sm) {
-    static_assert(SM_NMAT >= NMAT, "LDS holds the scales of every matrix");
-    constexpr bool GROUPED = FL & F_GROUPED, HOUT = FL & F_HOUT, EXTRA = FL & F_EXTRA;
+// The block's token rows: for a work item (GROUPED) the expert and its pair ids, padded
+// by repeating the last pair (activation rows of the padding are loaded, their results never
+// stored); for a dense GEMM the token group and split of `item`.  False: nothing to do.
+template <int NT, int FL, int NS, int SM_NMAT, int NTS>
+__device__ __forceinline__ bool pf_setup(const PfGemm& a, int item, PfSmem<NTS, SM_NMAT, NS>& sm,
+                                         int& ntok, int& e, int& split) {
+    constexpr bool GROUPED = FL & F_GROUPED;
     constexpr int TOKB = 16 * NT;
-    int ntok, e = 0, split = 0;
+    e = 0;
+    split = 0;
     if constexpr (GROUPED) {
-        static_assert(!GROUPED || TOKB == PF_ITEM, "one work item per block");
+        static_assert(!GROUPED || TOKB <= PF_ITEM, "one work item per block");
         // the record and the pair ids in one round trip (both indexed by the item alone)
         const int4 rec = reinterpret_cast<const int4*>(a.wrec)[item];
         const int pair = threadIdx.x < TOKB ? a.wpairs[(long)item * PF_ITEM + threadIdx.x] : 0;
-        if (rec.y == 0) return;   // past the last item
+        if (rec.y == 0) return false;   // past the last item
         e = rec.x;
         ntok = rec.y;
-        // slots past the item's pairs hold no valid pair: their activation rows repeat the
-        // last pair's (their results are never stored)
         if (threadIdx.x < TOKB) sm.orow[threadIdx.x] = pair;
         __syncthreads();
         if (threadIdx.x < TOKB) sm.arow[threadIdx.x] = sm.orow[min((int)threadIdx.x, ntok - 1)] / a.act_div;
     } else {
         const int t0 = (item / a.ksplit) * TOKB;
         split = item % a.ksplit;
-        if (t0 >= a.T) return;
+        if (t0 >= a.T) return false;
         ntok = min(TOKB, a.T - t0);
         if (threadIdx.x < TOKB) {
             sm.arow[threadIdx.x] = t0 + min((int)threadIdx.x, ntok - 1);
@@ -159,7 +154,22 @@ __device__ __forceinline__ void pf_gemm_block(const PfGemm& a, int rb, int item,
         }
     }
     __syncthreads();
-    const int ntiles = (ntok + 15) >> 4;
+    return true;
+}
+
+// One block of the GEMM: features rb*64 .. +63 (16 per wave) of the block's tokens, NTE
+// tiles of 16 (the token rows set up by pf_setup in LDS sized for NT tiles).  Weights and
+// activations are loaded D steps ahead: the weights into D register slots (the loop
+// unrolled by D), the activations into registers that are staged into the LDS double
+// buffer one step before their use.  The weight rows of one block share a base address (the
+// expert's matrix) held in scalar registers; a lane only keeps 32-bit offsets.
+template <int NMAT, int BITS, int NTE, int FL, int NS, int SM_NMAT, int NTS>
+__device__ __forceinline__ void pf_gemm_body(const PfGemm& a, int rb, int ntok, int e, int split,
+                                             PfSmem<NTS, SM_NMAT, NS>& sm) {
+    static_assert(SM_NMAT >= NMAT, "LDS holds the scales of every matrix");
+    static_assert(NTE <= NTS, "LDS holds every tile");
+    constexpr bool HOUT = FL & F_HOUT, EXTRA = FL & F_EXTRA;
+    const int ntiles = (ntok + 15) >> 4;   // <= NTE
     // NS > 0: the block's step count known at compile time (the loop fully unrolled); the
     // block covers steps kofs .. kofs + nsteps - 1 of the row (split-K for dense GEMMs)
     const int K = a.K, G = K / 64, nsteps = NS ? NS : K / PF_KS;   // even
@@ -239,17 +249,21 @@ __device__ __forceinline__ void pf_gemm_block(const PfGemm& a, int rb, int item,
     // Loads are unconditional (rows past the item repeat its last row; a step past the end
     // repeats the last step): a load inside a branch gets its wait placed right after it,
     // which would also drain every weight load in flight.
-    uint4 xr[NT];
-    auto load_x = [&](int ks) {
+    // D steps of activations and weights in flight: step ks issues the loads of step ks + D,
+    // activations before weights, so the wait for the activations of step ks + 1 leaves the
+    // weights of steps ks + 1 .. ks + D - 1 in flight
+    constexpr int D = NTE >= 4 ? 2 : 4;
+    uint4 xr[D][NTE];
+    auto load_x = [&](uint4 (&x)[NTE], int ks) {
         ks = min(ks, nsteps - 1);
 #pragma unroll
-        for (int q = 0; q < NT; ++q)
-            xr[q] = reinterpret_cast<const uint4*>(a.act + (long)sm.arow[q * 16 + sr] * K + (kofs + ks) * PF_KS)[sc];
+        for (int q = 0; q < NTE; ++q)
+            x[q] = reinterpret_cast<const uint4*>(a.act + (long)sm.arow[q * 16 + sr] * K + (kofs + ks) * PF_KS)[sc];
     };
-    auto commit_x = [&](int buf) {
+    auto commit_x = [&](const uint4 (&x)[NTE], int buf) {
 #pragma unroll
-        for (int q = 0; q < NT; ++q)
-            if (q < ntiles) pf_commit<BITS>(xr[q], q * 16 + sr, sc, sm.tile[buf]);
+        for (int q = 0; q < NTE; ++q)
+            if (q < ntiles) pf_commit<BITS>(x[q], q * 16 + sr, sc, sm.tile[buf]);
     };
     using Slot = PfSlot<NMAT, BITS>;
     auto load_w = [&](Slot& sl, int ks) {
@@ -276,11 +290,11 @@ __device__ __forceinline__ void pf_gemm_block(const PfGemm& a, int rb, int item,
         }
     };
 
-    f32x4 acc[NMAT][NT];
+    f32x4 acc[NMAT][NTE];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-        for (int c = 0; c < NT; ++c) acc[m][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < NTE; ++c) acc[m][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     constexpr float C = code_div<BITS>();
     uint32_t magic = BITS == 4 ? 0x4C004C00u : 0x5C005C00u;   // fp16 C in both halves
@@ -294,11 +308,11 @@ __device__ __forceinline__ void pf_gemm_block(const PfGemm& a, int rb, int item,
     // before its reload is issued, so old and new values never live together: the register
     // allocator keeps them in place and the loop back-edge needs no copy of a loaded register
     // (such a copy would wait for every load in flight).
-    auto step = [&](Slot& sl, int ks) {
+    auto step = [&](Slot& sl, uint4 (&xnext)[NTE], uint4 (&xfree)[NTE], int ks) {
         const int buf = ks & 1;
-        // stage the activations of step ks + 1 (loaded a step ago) into the other buffer, which
-        // every wave finished reading before the barrier that ended step ks - 1
-        if (ks + 1 < nsteps) commit_x(buf ^ 1);
+        // stage the activations of step ks + 1 into the other buffer, which every wave
+        // finished reading before the barrier that ended step ks - 1
+        if (ks + 1 < nsteps) commit_x(xnext, buf ^ 1);
         // exchange halves: afterwards units 0 and 2 of the lane hold group 0, 1 and 3 group 1
         uint32_t cw[NMAT][Slot::LW];
         float sv[NMAT][2], bv[NMAT][2];   // s and b - C s of the step's two groups
@@ -330,10 +344,12 @@ __device__ __forceinline__ void pf_gemm_block(const PfGemm& a, int rb, int item,
                 }
             }
         }
-        // then the loads of step ks + 2: activations first, since memory waits are in issue
-        // order and the activations are needed a step earlier than the weights
-        load_x(ks + 2);
-        load_w(sl, ks + 2);
+        // then the loads of step ks + D (into the slot and the activation registers just
+        // consumed): activations first, since they are needed a step earlier than the weights
+        if (NS == 0 || ks + D < nsteps) {
+            load_x(xfree, ks + D);
+            load_w(sl, ks + D);
+        }
         const f16* tb = sm.tile[buf];
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
@@ -343,7 +359,7 @@ __device__ __forceinline__ void pf_gemm_block(const PfGemm& a, int rb, int item,
 #pragma unroll
                 for (int mm = 0; mm < 2; ++mm) bw[m][mm] = pf_codes<BITS>(&cw[m][(2 * mm + g) * WPU], magic);
 #pragma unroll
-            for (int c = 0; c < NT; ++c) {
+            for (int c = 0; c < NTE; ++c) {
                 if (c < ntiles) {
                     const f16* trow = tb + (c * 16 + col) * PF_PITCH;
                     const f16x8 a0 = *reinterpret_cast<const f16x8*>(trow + 8 * (8 * g + ubase));
@@ -364,26 +380,28 @@ __device__ __forceinline__ void pf_gemm_block(const PfGemm& a, int rb, int item,
         __syncthreads();
     };
 
-    Slot s0, s1;
+    Slot sl[D];
     load_sb();
-    load_x(0);
-    load_w(s0, 0);
-    commit_sb();
-    commit_x(0);
-    load_x(1);
-    load_w(s1, 1);
-    __syncthreads();
 #pragma unroll
-    for (int ks = 0; ks < (NS ? NS : nsteps); ks += 2) {
-        step(s0, ks);
-        step(s1, ks + 1);
+    for (int d = 0; d < D; ++d) {
+        load_x(xr[d], d);
+        load_w(sl[d], d);
+    }
+    commit_sb();
+    commit_x(xr[0], 0);
+    __syncthreads();
+    static_assert(NS % D == 0, "whole rounds of D steps");
+#pragma unroll
+    for (int ks = 0; ks < (NS ? NS : nsteps); ks += D) {   // nsteps is a multiple of 4
+#pragma unroll
+        for (int d = 0; d < D; ++d) step(sl[d], xr[(d + 1) % D], xr[d], ks + d);
     }
 
     // epilogue: tokens 16 c + 4 j + r of feature n
     const bool extra = EXTRA && n == a.N;
     if (n >= a.N && !extra) return;
 #pragma unroll
-    for (int c = 0; c < NT; ++c) {
+    for (int c = 0; c < NTE; ++c) {
         if (c >= ntiles) break;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -404,6 +422,17 @@ __device__ __forceinline__ void pf_gemm_block(const PfGemm& a, int rb, int item,
     }
 }
 
+// One block: the token rows of `item` (NT tiles of 16), then the GEMM over them.  LDS is
+// sized for NTS >= NT tiles, so kernels that run GEMMs of two tile counts share one layout.
+// (One body per kernel: with two inlined bodies the register allocation spills.)
+template <int NMAT, int BITS, int NT, int FL, int NS, int SM_NMAT, int NTS = NT>
+__device__ __forceinline__ void pf_gemm_block(const PfGemm& a, int rb, int item,
+                                              PfSmem<NTS, SM_NMAT, NS>& sm) {
+    int ntok, e, split;
+    if (!pf_setup<NT, FL, NS, SM_NMAT, NTS>(a, item, sm, ntok, e, split)) return;
+    pf_gemm_body<NMAT, BITS, NT, FL, NS, SM_NMAT, NTS>(a, rb, ntok, e, split, sm);
+}
+
 template <int NMAT, int BITS, int NT, int FL, int NS>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) k_pf_gemm(PfGemm a) {
     __shared__ __align__(16) PfSmem<NT, NMAT, NS> sm;
@@ -414,17 +443,17 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) k
 
 // The grouped down GEMM and the shared expert's dense down GEMM in one launch (they are
 // independent; equal inner sizes, so one step count): blocks below nbg take work items.
-template <int NS>
+template <int NS, int NTG>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
 k_pf_down(PfGemm g, PfGemm d, int nbg) {
-    __shared__ __align__(16) PfSmem<PF_ITEM / 16, 1, NS> sm;
+    __shared__ __align__(16) PfSmem<2, 1, NS> sm;
     int rb, item;
     if ((int)blockIdx.x < nbg) {
         pf_block(blockIdx.x, g.nrb, rb, item);
-        pf_gemm_block<1, 4, PF_ITEM / 16, F_GROUPED, NS, 1>(g, rb, item, sm);
+        pf_gemm_block<1, 4, NTG, F_GROUPED, NS, 1, 2>(g, rb, item, sm);
     } else {
         pf_block(blockIdx.x - nbg, d.nrb, rb, item);
-        pf_gemm_block<1, 4, PF_ITEM / 16, 0, NS, 1>(d, rb, item, sm);
+        pf_gemm_block<1, 4, 2, 0, NS, 1, 2>(d, rb, item, sm);
     }
 }
 
@@ -798,11 +827,11 @@ __device__ int block_scan_excl(int v, int* wsum, int* total) {
 }
 
 // Stable counting sort of the (token, k) pairs by expert (pair p = t * K + k), written as
-// GEMM work items: chunks of at most PF_ITEM pairs of one expert, each a record (expert,
-// tokens) and its pair ids; records past the last item get zero tokens.  One block of 1024 threads.  Ranks inside each chunk of 64 pairs come from
+// GEMM work items: chunks of at most isz pairs of one expert, each a record (expert,
+// tokens) and its pair ids (PF_ITEM slots per item); records past the last item get zero tokens.  One block of 1024 threads.  Ranks inside each chunk of 64 pairs come from
 // ballots on the expert index bits (lanes with the same expert); the chunks of a segment of
 // 1024 pairs are then offset per expert by a prefix over the segment's 16 chunk counts.
-__global__ void __launch_bounds__(1024) k_pf_sort(MoeArgs a, int max_items) {
+__global__ void __launch_bounds__(1024) k_pf_sort(MoeArgs a, int max_items, int isz) {
     __shared__ int cnt[1024], base[1024], eoff[1024], ewex[1024], wsum[32], tot;
     __shared__ uint16_t tab[16][1024];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -813,7 +842,7 @@ __global__ void __launch_bounds__(1024) k_pf_sort(MoeArgs a, int max_items) {
     __syncthreads();
     const int c = tid < E ? cnt[tid] : 0;
     const int excl = block_scan_excl(c, wsum, &tot);
-    const int nw = (c + PF_ITEM - 1) / PF_ITEM;
+    const int nw = (c + isz - 1) / isz;
     const int wex = block_scan_excl(nw, wsum, &tot);
     if (tid < E) {
         a.offs[tid] = excl;
@@ -821,7 +850,7 @@ __global__ void __launch_bounds__(1024) k_pf_sort(MoeArgs a, int max_items) {
         eoff[tid] = excl;
         ewex[tid] = wex;
         for (int w = 0; w < nw; ++w)
-            reinterpret_cast<int4*>(a.wrec)[wex + w] = int4{tid, min(PF_ITEM, c - w * PF_ITEM), 0, 0};
+            reinterpret_cast<int4*>(a.wrec)[wex + w] = int4{tid, min(isz, c - w * isz), 0, 0};
     }
     if (tid == 0) a.offs[E] = TK;
     __syncthreads();
@@ -857,9 +886,9 @@ __global__ void __launch_bounds__(1024) k_pf_sort(MoeArgs a, int max_items) {
         if (valid) {
             const int pos = base[ex] + tab[wave][ex] + rank;
             a.perm[pos] = p;
-            // the pair's slot in its work item; the item's last pair also fills the padding
+            // the pair's slot in its work item
             const int r = pos - eoff[ex];
-            a.wpairs[(long)(ewex[ex] + r / PF_ITEM) * PF_ITEM + r % PF_ITEM] = p;
+            a.wpairs[(long)(ewex[ex] + r / isz) * PF_ITEM + r % isz] = p;
         }
         __syncthreads();
         if (tid < E) base[tid] += cnt[tid];
@@ -989,16 +1018,22 @@ PfGemm grouped(const MoeArgs& a, const QW& w0, const QW* w1, int N, int K, const
 
 }  // namespace
 
+// Pairs per work item: 16 (one token tile: no activation loads for a second, mostly padding
+// tile) while experts average at most 8 pairs, so that few experts need a second item and a
+// second pass over their weights; else 32.
+int prefill_item_size(int E, int T, int K) { return (long)T * K <= 8l * E ? 16 : PF_ITEM; }
+
 // Upper bound on the work items of the sort, rounded up to the 8 XCDs of the block order:
-// sum over experts of ceil(count / PF_ITEM) <= E + T K / PF_ITEM.
+// sum over experts of ceil(count / isz) <= E + T K / isz.
 int prefill_max_items(int E, int T, int K) {
-    return (E + (T * K + PF_ITEM - 1) / PF_ITEM + 7) / 8 * 8;
+    const int isz = prefill_item_size(E, T, K);
+    return (E + (T * K + isz - 1) / isz + 7) / 8 * 8;
 }
 
 int prefill_ksplit(int hidden) { return hidden / PF_XS_K; }
 
 hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s) {
-    const int items = prefill_max_items(a.E, a.T, a.K);
+    const int items = prefill_max_items(a.E, a.T, a.K), isz = prefill_item_size(a.E, a.T, a.K);
     const int tgroups = (a.T + PF_TOK - 1) / PF_TOK;
     const int ksplit = prefill_ksplit(a.H);
     const bool all = stage == QMOE_STAGE_ALL;
@@ -1022,12 +1057,13 @@ hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s) {
         if (ksplit <= 2) k_pf_token<2><<<a.T, 256, tsm, s>>>(a, ksplit);
         else if (ksplit <= 4) k_pf_token<4><<<a.T, 256, tsm, s>>>(a, ksplit);
         else k_pf_token<8><<<a.T, 256, tsm, s>>>(a, ksplit);
-        k_pf_sort<<<1, 1024, 0, s>>>(a, items);
+        k_pf_sort<<<1, 1024, 0, s>>>(a, items, isz);
     }
     if (all || stage == QMOE_STAGE_GATE_UP) {
         PfGemm p = grouped(a, a.eg, &a.eu, a.I, a.H, a.x, a.K, items);
         p.hout = a.h;
-        pf_gemm<2, 4, PF_ITEM / 16, F_GROUPED | F_HOUT>(p, s);
+        if (isz == 16) pf_gemm<2, 4, 1, F_GROUPED | F_HOUT>(p, s);
+        else pf_gemm<2, 4, 2, F_GROUPED | F_HOUT>(p, s);
     }
     if (all || stage == QMOE_STAGE_DOWN) {
         PfGemm p = grouped(a, a.ed, nullptr, a.H, a.I, a.h, 1, items);
@@ -1038,14 +1074,19 @@ hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s) {
         const int nbg = p.nrb * p.items;
         const dim3 grid((unsigned)(nbg + q.nrb * q.items));
         if (a.I == a.SI && (a.I == 512 || a.I == 1024 || a.I == 2048)) {
-            switch (a.I / PF_KS) {
-                case 4: k_pf_down<4><<<grid, 256, 0, s>>>(p, q, nbg); break;
-                case 8: k_pf_down<8><<<grid, 256, 0, s>>>(p, q, nbg); break;
-                default: k_pf_down<16><<<grid, 256, 0, s>>>(p, q, nbg); break;
+            const int sel = (a.I / PF_KS) * 2 + (isz == 16);
+            switch (sel) {
+                case 8: k_pf_down<4, 2><<<grid, 256, 0, s>>>(p, q, nbg); break;
+                case 9: k_pf_down<4, 1><<<grid, 256, 0, s>>>(p, q, nbg); break;
+                case 16: k_pf_down<8, 2><<<grid, 256, 0, s>>>(p, q, nbg); break;
+                case 17: k_pf_down<8, 1><<<grid, 256, 0, s>>>(p, q, nbg); break;
+                case 32: k_pf_down<16, 2><<<grid, 256, 0, s>>>(p, q, nbg); break;
+                default: k_pf_down<16, 1><<<grid, 256, 0, s>>>(p, q, nbg); break;
             }
         } else {
-            pf_gemm<1, 4, PF_ITEM / 16, F_GROUPED>(p, s);
-            pf_gemm<1, 4, PF_ITEM / 16, 0>(q, s);
+            if (isz == 16) pf_gemm<1, 4, 1, F_GROUPED>(p, s);
+            else pf_gemm<1, 4, 2, F_GROUPED>(p, s);
+            pf_gemm<1, 4, 2, 0>(q, s);
         }
         k_pf_combine<<<(unsigned)(((long)a.T * a.H / 8 + 255) / 256), 256, 0, s>>>(a);
     }
