@@ -65,6 +65,7 @@ struct PfGemm {
 constexpr int F_GROUPED = 1;   // work items of the expert sort (else token groups of all tokens)
 constexpr int F_HOUT = 2;      // fp16 silu(out0) * out1 (else fp32 outputs)
 constexpr int F_EXTRA = 4;     // one extra feature row from a second matrix (single matrix)
+constexpr int PF_RES_RBG = 4;  // row blocks per block of the resident-activation GEMM
 
 // LDS of one GEMM block: the activation tile (double buffer: step ks computes from ks % 2
 // while step ks + 1's tile is staged into the other), and with a compile-time step count NS
@@ -454,6 +455,183 @@ k_pf_down(PfGemm g, PfGemm d, int nbg) {
     } else {
         pf_block(blockIdx.x - nbg, d.nrb, rb, item);
         pf_gemm_block<1, 4, 2, 0, NS, 1, 2>(d, rb, item, sm);
+    }
+}
+
+// LDS of the resident-activation GEMM: the block's 16 NT token rows over all K inputs (pair
+// order, 16-byte row pad against bank conflicts) and their sums over each group of 64.
+template <int NT, int NS>
+struct PfResSmem {
+    static constexpr int PITCH = NS * PF_KS + 8;
+    f16 tile[16 * NT * PITCH];
+    float xsum[2 * NS][16 * NT];   // [group][token]
+    int arow[16 * NT], orow[16 * NT];
+};
+
+// GEMM block for a short reduction (K = 128 NS <= 1024), one 4-bit matrix: the block's
+// activations stay in LDS for all of K, so the block then runs RBG row blocks of 64 features
+// back to back with no barrier: the weights stream through D register slots across row-block
+// boundaries, each row block's scales and biases (one 16-byte load per 8 groups) come in
+// with them, and the b term uses the group sums taken once per block (acc += s P + (b - C s)
+// X with X from LDS), so each step is two MFMAs per group and tile.
+template <int NT, int NS, int RBG, int FL>
+__device__ __forceinline__ void pf_res_block(const PfGemm& a, int rbg, int item, PfResSmem<NT, NS>& sm) {
+    constexpr int PITCH = PfResSmem<NT, NS>::PITCH, K = NS * PF_KS, G = K / 64, SBV = G / 8;
+    constexpr int NSTEP = RBG * NS, D = 4;
+    int ntok, e, split;
+    {   // the token rows (pf_setup's rules)
+        constexpr int TOKB = 16 * NT;
+        e = 0; split = 0;
+        if constexpr (FL & F_GROUPED) {
+            const int4 rec = reinterpret_cast<const int4*>(a.wrec)[item];
+            const int pair = threadIdx.x < TOKB ? a.wpairs[(long)item * PF_ITEM + threadIdx.x] : 0;
+            if (rec.y == 0) return;
+            e = rec.x;
+            ntok = rec.y;
+            if (threadIdx.x < TOKB) sm.orow[threadIdx.x] = pair;
+            __syncthreads();
+            if (threadIdx.x < TOKB) sm.arow[threadIdx.x] = sm.orow[min((int)threadIdx.x, ntok - 1)] / a.act_div;
+        } else {
+            const int t0 = item * TOKB;
+            if (t0 >= a.T) return;
+            ntok = min(TOKB, a.T - t0);
+            if (threadIdx.x < TOKB) {
+                sm.arow[threadIdx.x] = t0 + min((int)threadIdx.x, ntok - 1);
+                sm.orow[threadIdx.x] = t0 + threadIdx.x;
+            }
+        }
+        __syncthreads();
+    }
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 15, j = lane >> 4;
+    constexpr int UPR = K / 8;                      // 8-input units per row
+    const int wpr = K / 8;                          // packed words per row
+    const uint32_t* wb = a.p[0] + (long)e * a.N * wpr;
+    const uint16_t* sbase = a.s[0] + (long)e * a.N * G;
+    const uint16_t* bbase = a.b[0] + (long)e * a.N * G;
+    // weights of flattened step f (row block f / NS, step f % NS); rows past N clamped
+    auto row_of = [&](int rbl) { return min((rbg * RBG + rbl) * PF_ROWS + wave * 16 + col, a.N - 1); };
+    uint32_t sl[D][4];
+    auto load_w = [&](int f) {
+        const uint4 v = reinterpret_cast<const uint4*>(wb + (uint32_t)row_of(f / NS) * wpr + (f % NS) * (PF_KS / 8))[j];
+        uint32_t* d = sl[f % D];
+        d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+    };
+    uint4 sv[2][SBV], bvv[2][SBV];   // scales and biases of a row block: current and next
+    auto load_sb = [&](int rbl) {
+        const long o = (long)row_of(rbl) * G;
+#pragma unroll
+        for (int i = 0; i < SBV; ++i) {
+            sv[rbl & 1][i] = reinterpret_cast<const uint4*>(sbase + o)[i];
+            bvv[rbl & 1][i] = reinterpret_cast<const uint4*>(bbase + o)[i];
+        }
+    };
+    // the activations: 16 NT rows x K, one 16-byte unit per thread per pass, all loads first
+    {
+        constexpr int NU = 16 * NT * UPR / 256;
+        uint4 xr[NU];
+#pragma unroll
+        for (int i = 0; i < NU; ++i) {
+            const int u = i * 256 + threadIdx.x, r = u / UPR, c = u % UPR;
+            xr[i] = reinterpret_cast<const uint4*>(a.act + (long)sm.arow[r] * a.K)[c];
+        }
+        load_sb(0);
+#pragma unroll
+        for (int f = 0; f < D; ++f) load_w(f);
+#pragma unroll
+        for (int i = 0; i < NU; ++i) {
+            const int u = i * 256 + threadIdx.x, r = u / UPR, c = u % UPR;
+            *reinterpret_cast<uint4*>(sm.tile + r * PITCH + c * 8) = pair_perm8_w(xr[i]);
+        }
+    }
+    __syncthreads();
+    // group sums of the activation rows (fp32; the pair order stays inside a unit)
+    for (int q = threadIdx.x; q < 16 * NT * G; q += 256) {
+        const int r = q % (16 * NT), g = q / (16 * NT);
+        const uint4* row = reinterpret_cast<const uint4*>(sm.tile + r * PITCH + g * 64);
+        float acc = 0.0f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += sum8_w(row[u]);
+        sm.xsum[g][r] = acc;
+    }
+    __syncthreads();
+
+    constexpr float C = code_div<4>();
+    uint32_t magic = 0x4C004C00u;
+    asm volatile("" : "+v"(magic));
+    const int ubase = 4 * (j & 1) + (j >> 1);
+    const int ntiles = (ntok + 15) >> 4;
+    f32x4 acc[NT];
+#pragma unroll
+    for (int c = 0; c < NT; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int f = 0; f < NSTEP; ++f) {
+        const int rbl = f / NS, ks = f % NS;
+        uint32_t cw[4];
+        {
+            const uint32_t* w = sl[f % D];
+            const auto r0 = __builtin_amdgcn_permlane32_swap(w[0], w[1], false, false);
+            const auto r1 = __builtin_amdgcn_permlane32_swap(w[2], w[3], false, false);
+            cw[0] = r0[0]; cw[1] = r0[1]; cw[2] = r1[0]; cw[3] = r1[1];
+        }
+        // the loads D steps ahead (the slot just consumed), and the next row block's scales
+        if (f + D < NSTEP) load_w(f + D);
+        if (ks == 0 && rbl + 1 < RBG) load_sb(rbl + 1);
+        const uint32_t* svw = reinterpret_cast<const uint32_t*>(&sv[rbl & 1][0]);
+        const uint32_t* bvw = reinterpret_cast<const uint32_t*>(&bvv[rbl & 1][0]);
+        const uint32_t s2 = svw[ks], b2 = bvw[ks];   // groups 2 ks, 2 ks + 1 as fp16 pairs
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            const float s = g ? half_hi(s2) : half_lo(s2);
+            const float bb = fmaf(-C, s, g ? half_hi(b2) : half_lo(b2));
+            const f16x8 bw0 = pf_codes<4>(&cw[g], magic), bw1 = pf_codes<4>(&cw[2 + g], magic);
+#pragma unroll
+            for (int c = 0; c < NT; ++c) {
+                if (c < ntiles) {
+                    const f16* trow = sm.tile + (c * 16 + col) * PITCH + ks * PF_KS;
+                    const f16x8 a0 = *reinterpret_cast<const f16x8*>(trow + 8 * (8 * g + ubase));
+                    const f16x8 a1 = *reinterpret_cast<const f16x8*>(trow + 8 * (8 * g + 2 + ubase));
+                    f32x4 P = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bw0, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                    P = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bw1, P, 0, 0, 0);
+                    const float4 X = *reinterpret_cast<const float4*>(&sm.xsum[2 * ks + g][c * 16 + 4 * j]);
+                    acc[c][0] = fmaf(s, P[0], fmaf(bb, X.x, acc[c][0]));
+                    acc[c][1] = fmaf(s, P[1], fmaf(bb, X.y, acc[c][1]));
+                    acc[c][2] = fmaf(s, P[2], fmaf(bb, X.z, acc[c][2]));
+                    acc[c][3] = fmaf(s, P[3], fmaf(bb, X.w, acc[c][3]));
+                }
+            }
+        }
+        if (ks == NS - 1) {   // row block done: tokens 16 c + 4 j + r of feature n
+            const int n = (rbg * RBG + rbl) * PF_ROWS + wave * 16 + col;
+            if (n < a.N) {
+#pragma unroll
+                for (int c = 0; c < NT; ++c) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int t = c * 16 + 4 * j + r;
+                        if (c < ntiles && t < ntok) a.out0[(long)sm.orow[t] * a.ostride + n] = acc[c][r];
+                    }
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < NT; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+}
+
+// The grouped down GEMM and the shared expert's dense down GEMM in one launch, both with
+// resident activations: blocks below nbg take (work item, row group), the rest (token
+// group, row group).
+template <int NS, int NT, int RBG>
+__global__ void __launch_bounds__(256) k_pf_down_res(PfGemm g, PfGemm d, int nbg) {
+    __shared__ __align__(16) PfResSmem<NT, NS> sm;
+    int rbg, item;
+    if ((int)blockIdx.x < nbg) {
+        pf_block(blockIdx.x, g.nrb, rbg, item);
+        pf_res_block<NT, NS, RBG, F_GROUPED>(g, rbg, item, sm);
+    } else {
+        pf_block(blockIdx.x - nbg, d.nrb, rbg, item);
+        pf_res_block<NT, NS, RBG, 0>(d, rbg, item, sm);
     }
 }
 
@@ -1073,11 +1251,25 @@ hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s) {
         q.out0 = a.os;
         const int nbg = p.nrb * p.items;
         const dim3 grid((unsigned)(nbg + q.nrb * q.items));
-        if (a.I == a.SI && (a.I == 512 || a.I == 1024 || a.I == 2048)) {
+        if (a.I == a.SI && (a.I == 512 || (a.I == 1024 && isz == 16))) {
+            // resident activations: row groups of PF_RES_RBG row blocks, token groups of isz
+            constexpr int RBG = PF_RES_RBG;
+            const int nt = isz / 16;
+            p.nrb = (a.H + PF_ROWS * RBG - 1) / (PF_ROWS * RBG);
+            q = gemm_args(a.shd, nullptr, a.H, a.SI, a.hs, a.H, (a.T + isz - 1) / isz);
+            q.T = a.T;
+            q.out0 = a.os;
+            q.nrb = p.nrb;
+            const int nbr = p.nrb * p.items;
+            const dim3 gr((unsigned)(nbr + q.nrb * q.items));
+            switch ((a.I / PF_KS) * 2 + nt - 1) {
+                case 8: k_pf_down_res<4, 1, RBG><<<gr, 256, 0, s>>>(p, q, nbr); break;
+                case 9: k_pf_down_res<4, 2, RBG><<<gr, 256, 0, s>>>(p, q, nbr); break;
+                default: k_pf_down_res<8, 1, RBG><<<gr, 256, 0, s>>>(p, q, nbr); break;
+            }
+        } else if (a.I == a.SI && (a.I == 1024 || a.I == 2048)) {
             const int sel = (a.I / PF_KS) * 2 + (isz == 16);
             switch (sel) {
-                case 8: k_pf_down<4, 2><<<grid, 256, 0, s>>>(p, q, nbg); break;
-                case 9: k_pf_down<4, 1><<<grid, 256, 0, s>>>(p, q, nbg); break;
                 case 16: k_pf_down<8, 2><<<grid, 256, 0, s>>>(p, q, nbg); break;
                 case 17: k_pf_down<8, 1><<<grid, 256, 0, s>>>(p, q, nbg); break;
                 case 32: k_pf_down<16, 2><<<grid, 256, 0, s>>>(p, q, nbg); break;

@@ -120,6 +120,19 @@ def test_prefill_wide_inter_many_items(q):
     check_layer(Lc, x, ad, y, idx, w)
 
 
+@pytest.mark.parametrize("T", [64, 200])
+def test_prefill_inter_1024(q, T):
+    """Routed and shared inner size 1024: 16-pair work items at 64 tokens (the down GEMMs
+    with activations resident over all 1024 inputs), 32-pair items at 200 tokens."""
+    S = Shape(hidden=1024, inter=1024, shared_inter=1024, n_experts=64, top_k=4, rank=16, n_adapters=2)
+    Lc = build_layer(synth.Workload.TEST, 17, S)
+    x = synth.activations(T, S.hidden, synth.Workload.TEST, 17, T)
+    ad = (np.arange(T) % 2).astype(np.int32)
+    y, idx, w = run_device(q, Lc, S, x, ad)
+    err, rel, n_alt = check_layer(Lc, x, ad, y, idx, w)
+    print(f"inter 1024 T={T}: max abs {err:.2e} rel L2 {rel:.2e} alternatives {n_alt}", flush=True)
+
+
 def test_decode_one_token_full_shape(q):
     """The single-token decode workload: hidden 2048, 256 experts, top-4, shared expert with
     8-bit gate, LoRA rank 16 alpha 32 on the shared projections."""
