@@ -530,7 +530,7 @@ def bench_gemv(args, q, torch):
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
            "data": "synthetic",
            "config": {"workload": "qlinear_int4 x[1x2048] W[512x2048] int4 g64, 2048 weight copies rotated"},
-           "roofline": {"kernel": "k_qgemv<4>", "bound": "hbm", "achieved": ach,
+           "roofline": {"kernel": "k_qgemv_fast<4>", "bound": "hbm", "achieved": ach,
                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
                         "traffic": None, "bytes_per_launch": bytes_, "us_per_launch": ms / K * 1e3}}
     return res, None
