@@ -12,7 +12,7 @@ constexpr int MAX_RANK = 64;
 constexpr int MAX_K = 32;
 constexpr int MAX_DEC_T = 32;  // the decode path serves up to this many tokens per call
 constexpr int MAX_DEC_K = 8;   // ... and up to this many experts per token
-constexpr int PF_ITEM = 32;    // most pairs per work item of the token-sorted GEMMs (slots per item)
+constexpr int PF_ITEM = 64;    // most pairs per work item of the token-sorted GEMMs (slots per item)
 
 struct QW {
     const uint32_t* p;

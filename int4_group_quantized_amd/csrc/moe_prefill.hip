@@ -447,14 +447,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) k
 template <int NS, int NTG>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
 k_pf_down(PfGemm g, PfGemm d, int nbg) {
-    __shared__ __align__(16) PfSmem<2, 1, NS> sm;
+    constexpr int NTS = NTG > 2 ? NTG : 2;   // LDS for both tile counts
+    __shared__ __align__(16) PfSmem<NTS, 1, NS> sm;
     int rb, item;
     if ((int)blockIdx.x < nbg) {
         pf_block(blockIdx.x, g.nrb, rb, item);
-        pf_gemm_block<1, 4, NTG, F_GROUPED, NS, 1, 2>(g, rb, item, sm);
+        pf_gemm_block<1, 4, NTG, F_GROUPED, NS, 1, NTS>(g, rb, item, sm);
     } else {
         pf_block(blockIdx.x - nbg, d.nrb, rb, item);
-        pf_gemm_block<1, 4, 2, 0, NS, 1, 2>(d, rb, item, sm);
+        pf_gemm_block<1, 4, 2, 0, NS, 1, NTS>(d, rb, item, sm);
     }
 }
 
@@ -1075,85 +1076,108 @@ __global__ void __launch_bounds__(1024) k_pf_sort(MoeArgs a, int max_items, int 
 }
 
 // y = fp16(sum_k w_k o_k + sigmoid(gate) (os + LoRA_down)) (+ residual), k in order.  Eight
-// outputs per thread with 16-byte loads; the LoRA-down delta scale * B[a_t][n..n+7] . z_d[t]
-// reads the eight B rows (contiguous) and z once.
+// outputs per thread with 16-byte loads.  Every load of the common case (up to 8 experts,
+// LoRA rank a multiple of 8 up to 16) is issued before any use, one memory round trip: the
+// experts' rows and weights, the shared output and gate logit, the residual, the eight
+// LoRA-B rows (contiguous) and z_d.  Absent operands are read from a valid stand-in and not
+// used; more experts or a larger rank continue with further passes.
 __global__ void __launch_bounds__(256) k_pf_combine(MoeArgs a) {
+    constexpr int KF = 8;
     const long i8 = ((long)blockIdx.x * 256 + threadIdx.x) * 8;
     if (i8 >= (long)a.T * a.H) return;
     const int t = (int)(i8 / a.H), n = (int)(i8 % a.H);
-    const float4* os = reinterpret_cast<const float4*>(a.os + i8);
-    const float4 o0 = os[0], o1 = os[1];
+    const int K = a.K;
+    float4 p[KF][2];
+    float w[KF];
+#pragma unroll
+    for (int u = 0; u < KF; ++u) {
+        const int k = min(u, K - 1);
+        w[u] = a.wts[(long)t * K + k];
+        const float4* ok = reinterpret_cast<const float4*>(a.o + ((long)t * K + k) * a.H + n);
+        p[u][0] = ok[0];
+        p[u][1] = ok[1];
+    }
+    const float4 o0 = reinterpret_cast<const float4*>(a.os + i8)[0];
+    const float4 o1 = reinterpret_cast<const float4*>(a.os + i8)[1];
+    const float g = a.gate[t];
+    const uint4 xr = *reinterpret_cast<const uint4*>(a.x + i8);
+    const bool bfast = a.Bd && (a.rd & 7) == 0;
+    const int rv = bfast ? a.rd / 8 : 1;   // uint4 per B row
+    const int ad = a.Bd ? adapter_of(a.adapter, t, a.nad) : 0;
+    // 8 rows of rd halves are 8 rd contiguous halves; stand-in: the shared output
+    const uint4* b4 = bfast ? reinterpret_cast<const uint4*>(a.Bd + ((long)ad * a.H + n) * a.rd)
+                            : reinterpret_cast<const uint4*>(a.os + i8);
+    const float* z = a.zd + (long)t * MAX_RANK;
+    uint4 bv[8][2];
+    float4 zv[4];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) bv[q][i] = b4[bfast ? q * rv + min(i, rv - 1) : 0];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) zv[i] = reinterpret_cast<const float4*>(z)[i];
+
     float ov[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
-    if (a.Bd) {
-        const int ad = adapter_of(a.adapter, t, a.nad);
-        const float* z = a.zd + (long)t * MAX_RANK;
-        if ((a.rd & 7) == 0) {
-            // 8 rows of rd halves are 8 * rd contiguous halves: 16-byte loads, 16 ranks a pass
-            const uint4* b4 = reinterpret_cast<const uint4*>(a.Bd + ((long)ad * a.H + n) * a.rd);
-            const int rv = a.rd / 8;   // uint4 per row
-            float d[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            for (int r0 = 0; r0 < rv; r0 += 2) {
-                uint4 bv[8][2];
-                float4 zv[4];
+    if (bfast) {
+        float d[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        const float* zf = reinterpret_cast<const float*>(zv);
+        auto add = [&](const uint4 (&v)[8], const float* zs) {   // one uint4 per row: 8 ranks
 #pragma unroll
-                for (int q = 0; q < 8; ++q)
+            for (int q = 0; q < 8; ++q) {
+                const uint32_t w4[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
 #pragma unroll
-                    for (int i = 0; i < 2; ++i) bv[q][i] = b4[q * rv + min(r0 + i, rv - 1)];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) zv[i] = reinterpret_cast<const float4*>(z)[min(r0 * 2 + i, 2 * rv - 1)];
-                const float* zf = reinterpret_cast<const float*>(zv);
-#pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    if (r0 + i < rv) {
-#pragma unroll
-                        for (int q = 0; q < 8; ++q) {
-                            const uint32_t w4[4] = {bv[q][i].x, bv[q][i].y, bv[q][i].z, bv[q][i].w};
-#pragma unroll
-                            for (int u = 0; u < 4; ++u) {
-                                d[q] = fmaf(half_lo(w4[u]), zf[i * 8 + 2 * u], d[q]);
-                                d[q] = fmaf(half_hi(w4[u]), zf[i * 8 + 2 * u + 1], d[q]);
-                            }
-                        }
-                    }
+                for (int u = 0; u < 4; ++u) {
+                    d[q] = fmaf(half_lo(w4[u]), zs[2 * u], d[q]);
+                    d[q] = fmaf(half_hi(w4[u]), zs[2 * u + 1], d[q]);
                 }
             }
+        };
 #pragma unroll
-            for (int q = 0; q < 8; ++q) ov[q] = fmaf(a.lsd, d[q], ov[q]);
-        } else {
+        for (int i = 0; i < 2; ++i) {
+            if (i < rv) {
+                uint4 v[8];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) ov[q] = fmaf(a.lsd, lora_b_dot(a.Bd, ad, a.H, n + q, a.rd, z), ov[q]);
+                for (int q = 0; q < 8; ++q) v[q] = bv[q][i];
+                add(v, zf + 8 * i);
+            }
         }
+        for (int r = 2; r < rv; ++r) {   // ranks past 16
+            uint4 v[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] = b4[q * rv + r];
+            add(v, z + 8 * r);
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) ov[q] = fmaf(a.lsd, d[q], ov[q]);
+    } else if (a.Bd) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) ov[q] = fmaf(a.lsd, lora_b_dot(a.Bd, ad, a.H, n + q, a.rd, z), ov[q]);
     }
-    const float gm = sigmoid(a.gate[t]);
     float acc[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
-    for (int k0 = 0; k0 < a.K; k0 += 4) {   // four experts' rows in flight at a time
-        float4 p[4][2];
-        float w[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int k = min(k0 + u, a.K - 1);
-            w[u] = a.wts[(long)t * a.K + k];
-            const float4* ok = reinterpret_cast<const float4*>(a.o + ((long)t * a.K + k) * a.H + n);
-            p[u][0] = ok[0];
-            p[u][1] = ok[1];
-        }
+    for (int u = 0; u < KF; ++u) {
+        if (u < K) {
+            const float pv[8] = {p[u][0].x, p[u][0].y, p[u][0].z, p[u][0].w,
+                                 p[u][1].x, p[u][1].y, p[u][1].z, p[u][1].w};
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if (k0 + u < a.K) {
-                const float pv[8] = {p[u][0].x, p[u][0].y, p[u][0].z, p[u][0].w,
-                                     p[u][1].x, p[u][1].y, p[u][1].z, p[u][1].w};
-#pragma unroll
-                for (int q = 0; q < 8; ++q) acc[q] = fmaf(w[u], pv[q], acc[q]);
-            }
+            for (int q = 0; q < 8; ++q) acc[q] = fmaf(w[u], pv[q], acc[q]);
         }
     }
+    for (int k = KF; k < K; ++k) {   // experts past the eighth
+        const float wk = a.wts[(long)t * K + k];
+        const float4* ok = reinterpret_cast<const float4*>(a.o + ((long)t * K + k) * a.H + n);
+        const float4 q0 = ok[0], q1 = ok[1];
+        const float pv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] = fmaf(wk, pv[q], acc[q]);
+    }
+    const float gm = sigmoid(g);
     uint16_t out[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) out[q] = f2h(fmaf(gm, ov[q], acc[q]));
     if (a.add_residual) {
-        const uint4 xr = *reinterpret_cast<const uint4*>(a.x + i8);
         const uint16_t* xh = reinterpret_cast<const uint16_t*>(&xr);
 #pragma unroll
         for (int q = 0; q < 8; ++q) out[q] = f2h(h2f(xh[q]) + h2f(out[q]));
@@ -1198,8 +1222,12 @@ PfGemm grouped(const MoeArgs& a, const QW& w0, const QW* w1, int N, int K, const
 
 // Pairs per work item: 16 (one token tile: no activation loads for a second, mostly padding
 // tile) while experts average at most 8 pairs, so that few experts need a second item and a
-// second pass over their weights; else 32.
-int prefill_item_size(int E, int T, int K) { return (long)T * K <= 8l * E ? 16 : PF_ITEM; }
+// second pass over their weights; 32 up to an average of 32; else 64 (four tiles: each
+// weight step feeds four times the MFMA work, the regime where the GEMMs turn compute-bound).
+int prefill_item_size(int E, int T, int K) {
+    const long tk = (long)T * K;
+    return tk <= 8l * E ? 16 : tk <= 32l * E ? 32 : 64;
+}
 
 // Upper bound on the work items of the sort, rounded up to the 8 XCDs of the block order:
 // sum over experts of ceil(count / isz) <= E + T K / isz.
@@ -1241,17 +1269,18 @@ hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s) {
         PfGemm p = grouped(a, a.eg, &a.eu, a.I, a.H, a.x, a.K, items);
         p.hout = a.h;
         if (isz == 16) pf_gemm<2, 4, 1, F_GROUPED | F_HOUT>(p, s);
-        else pf_gemm<2, 4, 2, F_GROUPED | F_HOUT>(p, s);
+        else if (isz == 32) pf_gemm<2, 4, 2, F_GROUPED | F_HOUT>(p, s);
+        else pf_gemm<2, 4, 4, F_GROUPED | F_HOUT>(p, s);
     }
     if (all || stage == QMOE_STAGE_DOWN) {
         PfGemm p = grouped(a, a.ed, nullptr, a.H, a.I, a.h, 1, items);
         p.out0 = a.o;
-        PfGemm q = gemm_args(a.shd, nullptr, a.H, a.SI, a.hs, a.H, (a.T + PF_ITEM - 1) / PF_ITEM);
+        PfGemm q = gemm_args(a.shd, nullptr, a.H, a.SI, a.hs, a.H, (a.T + 31) / 32);   // 32-token groups
         q.T = a.T;
         q.out0 = a.os;
         const int nbg = p.nrb * p.items;
         const dim3 grid((unsigned)(nbg + q.nrb * q.items));
-        if (a.I == a.SI && (a.I == 512 || (a.I == 1024 && isz == 16))) {
+        if (a.I == a.SI && isz <= 32 && (a.I == 512 || (a.I == 1024 && isz == 16))) {
             // resident activations: row groups of PF_RES_RBG row blocks, token groups of isz
             constexpr int RBG = PF_RES_RBG;
             const int nt = isz / 16;
@@ -1267,17 +1296,21 @@ hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s) {
                 case 9: k_pf_down_res<4, 2, RBG><<<gr, 256, 0, s>>>(p, q, nbr); break;
                 default: k_pf_down_res<8, 1, RBG><<<gr, 256, 0, s>>>(p, q, nbr); break;
             }
-        } else if (a.I == a.SI && (a.I == 1024 || a.I == 2048)) {
-            const int sel = (a.I / PF_KS) * 2 + (isz == 16);
-            switch (sel) {
-                case 16: k_pf_down<8, 2><<<grid, 256, 0, s>>>(p, q, nbg); break;
-                case 17: k_pf_down<8, 1><<<grid, 256, 0, s>>>(p, q, nbg); break;
-                case 32: k_pf_down<16, 2><<<grid, 256, 0, s>>>(p, q, nbg); break;
-                default: k_pf_down<16, 1><<<grid, 256, 0, s>>>(p, q, nbg); break;
+        } else if (a.I == a.SI && (a.I == 512 || a.I == 1024 || a.I == 2048)) {
+            // both GEMMs in one launch, per-step staging; grouped tiles isz / 16
+            switch ((a.I / PF_KS) * 4 + isz / 16) {
+                case 20: k_pf_down<4, 4><<<grid, 256, 0, s>>>(p, q, nbg); break;
+                case 33: k_pf_down<8, 1><<<grid, 256, 0, s>>>(p, q, nbg); break;
+                case 34: k_pf_down<8, 2><<<grid, 256, 0, s>>>(p, q, nbg); break;
+                case 36: k_pf_down<8, 4><<<grid, 256, 0, s>>>(p, q, nbg); break;
+                case 65: k_pf_down<16, 1><<<grid, 256, 0, s>>>(p, q, nbg); break;
+                case 66: k_pf_down<16, 2><<<grid, 256, 0, s>>>(p, q, nbg); break;
+                default: k_pf_down<16, 4><<<grid, 256, 0, s>>>(p, q, nbg); break;
             }
         } else {
             if (isz == 16) pf_gemm<1, 4, 1, F_GROUPED>(p, s);
-            else pf_gemm<1, 4, 2, F_GROUPED>(p, s);
+            else if (isz == 32) pf_gemm<1, 4, 2, F_GROUPED>(p, s);
+            else pf_gemm<1, 4, 4, F_GROUPED>(p, s);
             pf_gemm<1, 4, 2, 0>(q, s);
         }
         k_pf_combine<<<(unsigned)(((long)a.T * a.H / 8 + 255) / 256), 256, 0, s>>>(a);

@@ -133,6 +133,23 @@ def test_prefill_inter_1024(q, T):
     print(f"inter 1024 T={T}: max abs {err:.2e} rel L2 {rel:.2e} alternatives {n_alt}", flush=True)
 
 
+@pytest.mark.parametrize("T", [256, 300])
+def test_prefill_64_pair_items(q, T):
+    """Many pairs per expert (above 32 on average): 64-pair work items, four token tiles per
+    GEMM block; hidden 512 (short steps) and hidden 2048 (the full step count)."""
+    if T == 256:
+        S = SMALL
+    else:
+        S = Shape(hidden=2048, inter=512, shared_inter=512, n_experts=16, top_k=2, rank=16, n_adapters=2)
+    assert T * S.top_k > 32 * S.n_experts
+    Lc = build_layer(synth.Workload.TEST, 18, S)
+    x = synth.activations(T, S.hidden, synth.Workload.TEST, 18, T)
+    ad = (np.arange(T) % 2).astype(np.int32)
+    y, idx, w = run_device(q, Lc, S, x, ad)
+    err, rel, n_alt = check_layer(Lc, x, ad, y, idx, w)
+    print(f"64-pair items T={T}: max abs {err:.2e} rel L2 {rel:.2e} alternatives {n_alt}", flush=True)
+
+
 def test_decode_one_token_full_shape(q):
     """The single-token decode workload: hidden 2048, 256 experts, top-4, shared expert with
     8-bit gate, LoRA rank 16 alpha 32 on the shared projections."""
