@@ -39,7 +39,7 @@ Layout layout_of(const qmoe_moe_layer& L, int T) {
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t r = off; off = up256(off + bytes); return r; };
     const size_t TK = (size_t)T * L.top_k;
-    const size_t ks = (size_t)prefill_ksplit(L.hidden);   // split-K partials of the x side
+    const size_t ks = (size_t)prefill_ksplit(L.hidden, T);   // split-K partials of the x side
     l.logits = take(ks * T * ((L.n_experts + 63) / 64 * 64) * 4);
     l.gate = take(ks * T * 4);
     // LoRA z of gate and up: partial sums per 256 inputs (prefill), the first slice for decode

@@ -177,7 +177,7 @@ hipError_t launch_moe_decode(const MoeArgs& a, int stage, hipStream_t s);
 // moe_prefill.hip
 int prefill_max_items(int E, int T, int K);
 int prefill_item_size(int E, int T, int K);
-int prefill_ksplit(int hidden);
+int prefill_ksplit(int hidden, int T);
 hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s);
 
 }  // namespace qmoe

@@ -39,7 +39,9 @@ constexpr int PF_TOK = 64;            // tokens per block of the dense GEMMs: 4 
 constexpr int PF_ROWS = 64;           // output features per block: 4 waves x 16
 constexpr int PF_KS = 128;            // inputs per k step (two groups)
 constexpr int PF_PITCH = PF_KS + 8;   // LDS row pitch in halves (272 bytes: no bank conflicts)
-constexpr int PF_XS_K = 512;          // inputs per block of the split-K x-side GEMMs
+constexpr int PF_XS_K = 512;          // inputs per block of the split-K x-side GEMMs (few tokens)
+constexpr int PF_XS_K_BIG = 2048;     // the same from PF_XS_BIG_T tokens up (enough blocks unsplit)
+constexpr int PF_XS_BIG_T = 2048;
 
 struct PfGemm {
     const uint32_t* p[2];
@@ -714,8 +716,8 @@ __host__ __device__ inline int lora_z_jobs(int T, int H, int rank, int nad) {
 // x side of the layer in one launch: the router rows plus the shared-gate row (8-bit), the
 // shared expert's gate and up (int4), all as split-K partial sums, then the LoRA z's of the
 // shared gate and up as partial sums over 256-input chunks (one wave per lora_z_chunk job).
+template <int NS>
 __global__ void __launch_bounds__(256) k_pf_xside(XsideArgs xa, MoeArgs a) {
-    constexpr int NS = PF_XS_K / PF_KS;
     __shared__ __align__(16) PfSmem<4, 2, NS> sm;
     const int b = blockIdx.x;
     int rb, item;
@@ -1076,16 +1078,20 @@ __global__ void __launch_bounds__(1024) k_pf_sort(MoeArgs a, int max_items, int 
 }
 
 // y = fp16(sum_k w_k o_k + sigmoid(gate) (os + LoRA_down)) (+ residual), k in order.  Eight
-// outputs per thread with 16-byte loads.  Every load of the common case (up to 8 experts,
+// outputs of one token per thread with 16-byte loads.  Every load of the common case (up to 8 experts,
 // LoRA rank a multiple of 8 up to 16) is issued before any use, one memory round trip: the
 // experts' rows and weights, the shared output and gate logit, the residual, the eight
 // LoRA-B rows (contiguous) and z_d.  Absent operands are read from a valid stand-in and not
 // used; more experts or a larger rank continue with further passes.
 __global__ void __launch_bounds__(256) k_pf_combine(MoeArgs a) {
     constexpr int KF = 8;
-    const long i8 = ((long)blockIdx.x * 256 + threadIdx.x) * 8;
-    if (i8 >= (long)a.T * a.H) return;
-    const int t = (int)(i8 / a.H), n = (int)(i8 % a.H);
+    // block: 16 tokens x 128 features, so the block's LoRA-B rows (128 x rank) are read
+    // from L2 once and shared by its tokens through L1
+    const int nch = a.H / 128, ch = blockIdx.x % nch;
+    const int t = (blockIdx.x / nch) * 16 + (threadIdx.x >> 4);
+    if (t >= a.T) return;
+    const int n = ch * 128 + (threadIdx.x & 15) * 8;
+    const long i8 = (long)t * a.H + n;
     const int K = a.K;
     float4 p[KF][2];
     float w[KF];
@@ -1236,12 +1242,15 @@ int prefill_max_items(int E, int T, int K) {
     return (E + (T * K + isz - 1) / isz + 7) / 8 * 8;
 }
 
-int prefill_ksplit(int hidden) { return hidden / PF_XS_K; }
+// Inputs per x-side block: 512 (split-K partials keep a few tokens' launch wide), or up to
+// 2048 once there are PF_XS_BIG_T tokens (the partials' traffic would grow with T).
+static int xs_inputs(int hidden, int T) { return T >= PF_XS_BIG_T ? std::min(hidden, PF_XS_K_BIG) : PF_XS_K; }
+int prefill_ksplit(int hidden, int T) { return hidden / xs_inputs(hidden, T); }
 
 hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s) {
     const int items = prefill_max_items(a.E, a.T, a.K), isz = prefill_item_size(a.E, a.T, a.K);
     const int tgroups = (a.T + PF_TOK - 1) / PF_TOK;
-    const int ksplit = prefill_ksplit(a.H);
+    const int ksplit = prefill_ksplit(a.H, a.T);
     const bool all = stage == QMOE_STAGE_ALL;
     if (all || stage == QMOE_STAGE_ROUTE) {
         // x side: split-K blocks of PF_XS_K inputs write partial sums, k_pf_token adds them
@@ -1258,10 +1267,18 @@ hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s) {
         xa.nb_router = xa.router.nrb * xa.router.items;
         xa.nb_shared = xa.shared.nrb * xa.shared.items;
         xa.zjobs = (a.Ag ? lora_z_jobs(a.T, a.H, a.rg, a.nag) : 0) + (a.Au ? lora_z_jobs(a.T, a.H, a.ru, a.nau) : 0);
-        k_pf_xside<<<(unsigned)(xa.nb_router + xa.nb_shared + (xa.zjobs + 3) / 4), 256, 0, s>>>(xa, a);
+        const unsigned xgrid = (unsigned)(xa.nb_router + xa.nb_shared + (xa.zjobs + 3) / 4);
+        switch (xs_inputs(a.H, a.T) / PF_KS) {
+            case 4: k_pf_xside<4><<<xgrid, 256, 0, s>>>(xa, a); break;
+            case 8: k_pf_xside<8><<<xgrid, 256, 0, s>>>(xa, a); break;
+            default: k_pf_xside<16><<<xgrid, 256, 0, s>>>(xa, a); break;
+        }
         const size_t tsm = (size_t)a.SI * 2;   // hidden <= 4096: at most 8 splits
-        if (ksplit <= 2) k_pf_token<2><<<a.T, 256, tsm, s>>>(a, ksplit);
-        else if (ksplit <= 4) k_pf_token<4><<<a.T, 256, tsm, s>>>(a, ksplit);
+        // KP covers the split-K partials (<= hidden / 512) and half the LoRA z chunks
+        // (hidden / 256), whatever the split
+        const int kp = std::max(ksplit, a.H / 512);
+        if (kp <= 2) k_pf_token<2><<<a.T, 256, tsm, s>>>(a, ksplit);
+        else if (kp <= 4) k_pf_token<4><<<a.T, 256, tsm, s>>>(a, ksplit);
         else k_pf_token<8><<<a.T, 256, tsm, s>>>(a, ksplit);
         k_pf_sort<<<1, 1024, 0, s>>>(a, items, isz);
     }
@@ -1313,7 +1330,7 @@ hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s) {
             else pf_gemm<1, 4, 4, F_GROUPED>(p, s);
             pf_gemm<1, 4, 2, 0>(q, s);
         }
-        k_pf_combine<<<(unsigned)(((long)a.T * a.H / 8 + 255) / 256), 256, 0, s>>>(a);
+        k_pf_combine<<<(unsigned)((a.T + 15) / 16 * (a.H / 128)), 256, 0, s>>>(a);
     }
     return hipGetLastError();
 }

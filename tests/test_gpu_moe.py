@@ -133,10 +133,11 @@ def test_prefill_inter_1024(q, T):
     print(f"inter 1024 T={T}: max abs {err:.2e} rel L2 {rel:.2e} alternatives {n_alt}", flush=True)
 
 
-@pytest.mark.parametrize("T", [256, 300])
+@pytest.mark.parametrize("T", [256, 300, 2048])
 def test_prefill_64_pair_items(q, T):
     """Many pairs per expert (above 32 on average): 64-pair work items, four token tiles per
-    GEMM block; hidden 512 (short steps) and hidden 2048 (the full step count)."""
+    GEMM block; hidden 512 (short steps) and hidden 2048 (the full step count).  At 2048
+    tokens the x side runs unsplit (2048 inputs per block)."""
     if T == 256:
         S = SMALL
     else:
