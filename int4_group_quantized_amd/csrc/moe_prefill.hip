@@ -14,13 +14,17 @@
 // weights as B (32 inputs x 16 features): lane l supplies feature l % 16 and inputs
 // 8 (l / 16) .. +7, and ends with tokens 4 (l / 16) .. +3 of feature l % 16.
 //
-// Exactness.  The weights enter the MFMA as the exact fp16 codes C + q (C = 16 for 4-bit,
-// 256 for 8-bit: the code's bits dropped into the mantissa of C), never rounded to fp16
-// after scaling; fp16 products are exact in fp32.  Each MFMA pair covers exactly one
-// 64-input group, so the group's sum P = sum (C + q) x is formed apart, and with the
-// group's sum of inputs X (one more MFMA pair against a ones operand) the affine terms are
-// applied per group in fp32:
+// Weights.  A lane turns each packed word into the fp16 codes C + q (the code's bits dropped
+// into the mantissa of C = 16 or 256; exact).  Where the GEMM is bound by HBM (up to two
+// token tiles) the weights stay exact: each MFMA pair covers exactly one 64-input group, so
+// the group's sum P = sum (C + q) x is formed apart and, with the group's sum of inputs X
+// (one more MFMA pair against a ones operand), the affine terms are applied per group in
+// fp32:
 //     acc += s P + (b - C s) X.
+// In the grouped GEMMs with four token tiles the per-group terms would cost as much as the
+// MFMAs, so 4-bit weights are dequantized in fp16 there, fp16(s q + b) with q = codes - C (one rounding per
+// weight), and every MFMA accumulates into the row's fp32 sum.  The 8-bit router, whose
+// logits decide top-K, is always exact.
 // For that, a lane's 16-byte load of packed words (inputs 32 j .. 32 j + 31 of a 128-input
 // step, j = lane / 16, i.e. half of group j / 2) is exchanged across the wave halves with
 // v_permlane32_swap so that every register then holds words of a single group; the
@@ -107,6 +111,14 @@ __device__ __forceinline__ f16x8 pf_codes(const uint32_t* w, uint32_t magic) {
     return __builtin_bit_cast(f16x8, u);
 }
 
+// 4-bit weights in fp16 from their exact codes C + q: q = codes - C is exact, then one fp16
+// fma gives fp16(s q + b), a single rounding of the dequantized weight (the tile fed to MFMA).
+__device__ __forceinline__ f16x8 pf_dequant(f16x8 codes, f16 s, f16 b) {
+    const f16x8 cv = {(f16)16.0f, (f16)16.0f, (f16)16.0f, (f16)16.0f, (f16)16.0f, (f16)16.0f, (f16)16.0f, (f16)16.0f};
+    const f16x8 sv = {s, s, s, s, s, s, s, s}, bv = {b, b, b, b, b, b, b, b};
+    return __builtin_elementwise_fma(codes - cv, sv, bv);
+}
+
 // XCD-aware block order: blocks are handed to the 8 XCDs round-robin by linear id, so the
 // id's low 3 bits pick the XCD.  Every row block of one item (expert chunk or token group)
 // lands on the same XCD, and that XCD runs them back to back: the item's activations are
@@ -172,6 +184,8 @@ __device__ __forceinline__ void pf_gemm_body(const PfGemm& a, int rb, int ntok, 
     static_assert(SM_NMAT >= NMAT, "LDS holds the scales of every matrix");
     static_assert(NTE <= NTS, "LDS holds every tile");
     constexpr bool HOUT = FL & F_HOUT, EXTRA = FL & F_EXTRA;
+    // fp16 weights for the grouped 4-bit GEMMs with four token tiles (MFMA-bound); exact codes else
+    constexpr bool DQ = BITS == 4 && NTE >= 4 && (FL & F_GROUPED);
     const int ntiles = (ntok + 15) >> 4;   // <= NTE
     // NS > 0: the block's step count known at compile time (the loop fully unrolled); the
     // block covers steps kofs .. kofs + nsteps - 1 of the row (split-K for dense GEMMs)
@@ -318,7 +332,8 @@ __device__ __forceinline__ void pf_gemm_body(const PfGemm& a, int rb, int ntok, 
         if (ks + 1 < nsteps) commit_x(xnext, buf ^ 1);
         // exchange halves: afterwards units 0 and 2 of the lane hold group 0, 1 and 3 group 1
         uint32_t cw[NMAT][Slot::LW];
-        float sv[NMAT][2], bv[NMAT][2];   // s and b - C s of the step's two groups
+        float sv[NMAT][2], bv[NMAT][2];   // 8-bit: s and b - C s of the step's two groups
+        f16 sh[NMAT][2], bh[NMAT][2];     // 4-bit: s and b as stored
 #pragma unroll
         for (int m = 0; m < NMAT; ++m) {
 #pragma unroll
@@ -334,17 +349,17 @@ __device__ __forceinline__ void pf_gemm_body(const PfGemm& a, int rb, int ntok, 
             if constexpr (NS > 0) {
                 const uint2 p = *reinterpret_cast<const uint2*>(&sm.sb[m][wave * 16 + col][2 * ks]);
                 const f16x2 g0 = as_h2(p.x), g1 = as_h2(p.y);   // (s, b) of the step's groups
-                sv[m][0] = (float)g0[0];
-                bv[m][0] = fmaf(-C, sv[m][0], (float)g0[1]);
-                sv[m][1] = (float)g1[0];
-                bv[m][1] = fmaf(-C, sv[m][1], (float)g1[1]);
+                sh[m][0] = g0[0]; bh[m][0] = g0[1];
+                sh[m][1] = g1[0]; bh[m][1] = g1[1];
             } else {
                 const f16x2 s2 = as_h2(sl.s[m]), b2 = as_h2(sl.b[m]);
 #pragma unroll
-                for (int g = 0; g < 2; ++g) {
-                    sv[m][g] = (float)s2[g];
-                    bv[m][g] = fmaf(-C, sv[m][g], (float)b2[g]);
-                }
+                for (int g = 0; g < 2; ++g) { sh[m][g] = s2[g]; bh[m][g] = b2[g]; }
+            }
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                sv[m][g] = (float)sh[m][g];
+                bv[m][g] = fmaf(-C, sv[m][g], (float)bh[m][g]);
             }
         }
         // then the loads of step ks + D (into the slot and the activation registers just
@@ -360,13 +375,24 @@ __device__ __forceinline__ void pf_gemm_body(const PfGemm& a, int rb, int ntok, 
 #pragma unroll
             for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-                for (int mm = 0; mm < 2; ++mm) bw[m][mm] = pf_codes<BITS>(&cw[m][(2 * mm + g) * WPU], magic);
+                for (int mm = 0; mm < 2; ++mm) {
+                    bw[m][mm] = pf_codes<BITS>(&cw[m][(2 * mm + g) * WPU], magic);
+                    if constexpr (DQ) bw[m][mm] = pf_dequant(bw[m][mm], sh[m][g], bh[m][g]);
+                }
 #pragma unroll
             for (int c = 0; c < NTE; ++c) {
                 if (c < ntiles) {
                     const f16* trow = tb + (c * 16 + col) * PF_PITCH;
                     const f16x8 a0 = *reinterpret_cast<const f16x8*>(trow + 8 * (8 * g + ubase));
                     const f16x8 a1 = *reinterpret_cast<const f16x8*>(trow + 8 * (8 * g + 2 + ubase));
+                    if constexpr (DQ) {   // fp16 weights: accumulate over the whole row
+#pragma unroll
+                        for (int m = 0; m < NMAT; ++m) {
+                            acc[m][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bw[m][0], acc[m][c], 0, 0, 0);
+                            acc[m][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bw[m][1], acc[m][c], 0, 0, 0);
+                        }
+                        continue;
+                    }
                     f32x4 X = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, ones, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
                     X = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, ones, X, 0, 0, 0);
 #pragma unroll
