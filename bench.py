@@ -123,7 +123,7 @@ def time_graph(torch, g, reps=1):
 
 # ------------------------------------------------------------------------------ CPU baseline
 
-def cpu_baseline_moe_decode(n_tokens=96, budget_s=20.0):
+def cpu_baseline_moe_decode(n_tokens=600, budget_s=20.0):
     """The oracle (float64 numpy) on a bounded sample: n_tokens single-token decodes of one
     seeded layer of the same shapes; only the experts those tokens reach are quantized."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
