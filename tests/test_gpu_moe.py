@@ -120,10 +120,10 @@ def test_prefill_wide_inter_many_items(q):
     check_layer(Lc, x, ad, y, idx, w)
 
 
-@pytest.mark.parametrize("T", [64, 200])
+@pytest.mark.parametrize("T", [64, 100, 200])
 def test_prefill_inter_1024(q, T):
-    """Routed and shared inner size 1024: 16-pair work items at 64 tokens (the down GEMMs
-    with activations resident over all 1024 inputs), 32-pair items at 200 tokens."""
+    """Routed and shared inner size 1024: 16-pair work items at 64 and 100 tokens (the down
+    GEMMs with activations resident over all 1024 inputs), 32-pair items at 200 tokens."""
     S = Shape(hidden=1024, inter=1024, shared_inter=1024, n_experts=64, top_k=4, rank=16, n_adapters=2)
     Lc = build_layer(synth.Workload.TEST, 17, S)
     x = synth.activations(T, S.hidden, synth.Workload.TEST, 17, T)
