@@ -39,7 +39,10 @@ Layout layout_of(const qmoe_moe_layer& L, int T) {
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t r = off; off = up256(off + bytes); return r; };
     const size_t TK = (size_t)T * L.top_k;
-    const size_t ks = (size_t)prefill_ksplit(L.hidden, T);   // split-K partials of the x side
+    // sized for the largest split and the smallest work items at any token count, so that a
+    // workspace sized for max_tokens serves every smaller call (the offsets depend on T only
+    // through T itself)
+    const size_t ks = (size_t)L.hidden / 512;   // split-K partials of the x side (at most)
     l.logits = take(ks * T * ((L.n_experts + 63) / 64 * 64) * 4);
     l.gate = take(ks * T * 4);
     // LoRA z of gate and up: partial sums per 256 inputs (prefill), the first slice for decode
@@ -52,7 +55,7 @@ Layout layout_of(const qmoe_moe_layer& L, int T) {
     l.wts = take(TK * 4);
     l.offs = take((size_t)(L.n_experts + 1) * 4);
     l.perm = take(TK * 4);
-    const size_t items = (size_t)prefill_max_items(L.n_experts, T, L.top_k);
+    const size_t items = ((size_t)L.n_experts + (TK + 15) / 16 + 7) / 8 * 8;   // >= the sort's items
     l.wrec = take(items * 16);
     l.wpairs = take(items * PF_ITEM * 4);
     l.h = take(TK * L.inter * 2);

@@ -381,18 +381,25 @@ __device__ __forceinline__ void pf_gemm_body(const PfGemm& a, int rb, int ntok, 
                 }
 #pragma unroll
             for (int c = 0; c < NTE; ++c) {
+                if constexpr (DQ) {
+                    // fp16 weights: accumulate over the whole row.  Every tile is computed
+                    // (tiles past the item's tokens read padding rows; their results are never
+                    // stored): with no branch between the MFMAs the compiler places no
+                    // accumulator writes next to an MFMA still reading them.
+                    const f16* trow = tb + (c * 16 + col) * PF_PITCH;
+                    const f16x8 a0 = *reinterpret_cast<const f16x8*>(trow + 8 * (8 * g + ubase));
+                    const f16x8 a1 = *reinterpret_cast<const f16x8*>(trow + 8 * (8 * g + 2 + ubase));
+#pragma unroll
+                    for (int m = 0; m < NMAT; ++m) {
+                        acc[m][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bw[m][0], acc[m][c], 0, 0, 0);
+                        acc[m][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bw[m][1], acc[m][c], 0, 0, 0);
+                    }
+                    continue;
+                }
                 if (c < ntiles) {
                     const f16* trow = tb + (c * 16 + col) * PF_PITCH;
                     const f16x8 a0 = *reinterpret_cast<const f16x8*>(trow + 8 * (8 * g + ubase));
                     const f16x8 a1 = *reinterpret_cast<const f16x8*>(trow + 8 * (8 * g + 2 + ubase));
-                    if constexpr (DQ) {   // fp16 weights: accumulate over the whole row
-#pragma unroll
-                        for (int m = 0; m < NMAT; ++m) {
-                            acc[m][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bw[m][0], acc[m][c], 0, 0, 0);
-                            acc[m][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bw[m][1], acc[m][c], 0, 0, 0);
-                        }
-                        continue;
-                    }
                     f32x4 X = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, ones, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
                     X = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, ones, X, 0, 0, 0);
 #pragma unroll

@@ -133,15 +133,17 @@ def test_prefill_inter_1024(q, T):
     print(f"inter 1024 T={T}: max abs {err:.2e} rel L2 {rel:.2e} alternatives {n_alt}", flush=True)
 
 
-@pytest.mark.parametrize("T", [256, 300, 2048])
-def test_prefill_64_pair_items(q, T):
+WIDE_64 = Shape(hidden=2048, inter=512, shared_inter=512, n_experts=16, top_k=2, rank=16, n_adapters=2)
+DEEP_64 = Shape(hidden=512, inter=2048, shared_inter=2048, n_experts=8, top_k=2, rank=16, n_adapters=2)
+
+
+@pytest.mark.parametrize("T,S", [(256, SMALL), (300, WIDE_64), (2048, WIDE_64), (300, DEEP_64)],
+                         ids=["256-small", "300-wide", "2048-wide", "300-deep"])
+def test_prefill_64_pair_items(q, T, S):
     """Many pairs per expert (above 32 on average): 64-pair work items, four token tiles per
-    GEMM block; hidden 512 (short steps) and hidden 2048 (the full step count).  At 2048
-    tokens the x side runs unsplit (2048 inputs per block)."""
-    if T == 256:
-        S = SMALL
-    else:
-        S = Shape(hidden=2048, inter=512, shared_inter=512, n_experts=16, top_k=2, rank=16, n_adapters=2)
+    GEMM block, including the short last items of an expert; hidden 512 (short steps),
+    hidden 2048 (the full step count; at 2048 tokens the x side runs unsplit), and inner
+    size 2048 (the down GEMMs over 2048 inputs)."""
     assert T * S.top_k > 32 * S.n_experts
     Lc = build_layer(synth.Workload.TEST, 18, S)
     x = synth.activations(T, S.hidden, synth.Workload.TEST, 18, T)
