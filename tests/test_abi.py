@@ -134,6 +134,14 @@ def test_moe_workspace_and_validation():
     assert f(ctypes.byref(bad), X, 1, None, Y, None, None, FAKE * 64, 1 << 30, None) == _lib.QMOE_ERR_INVALID_ARG
 
 
+def test_moe_workspace_grows_with_the_token_count():
+    """A workspace sized for max_tokens serves every smaller call: the size never drops as the
+    token count grows, across the changes of split and work-item size (every T to 4096)."""
+    L = layer_c()
+    sizes = [q.lib.moe_switchglu_int4_workspace_bytes(ctypes.byref(L), t) for t in range(1, 4097)]
+    assert all(b >= a for a, b in zip(sizes, sizes[1:]))
+
+
 def test_supergroup_rejects_bad_arguments():
     f = q.lib.qlinear_supergroup
     assert f(FAKE, 1, FAKE, FAKE, FAKE, 3070, 1024, 4, FAKE * 4, None) == _lib.QMOE_ERR_UNSUPPORTED
