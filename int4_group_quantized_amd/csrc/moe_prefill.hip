@@ -111,12 +111,27 @@ __device__ __forceinline__ f16x8 pf_codes(const uint32_t* w, uint32_t magic) {
     return __builtin_bit_cast(f16x8, u);
 }
 
-// 4-bit weights in fp16 from their exact codes C + q: q = codes - C is exact, then one fp16
-// fma gives fp16(s q + b), a single rounding of the dequantized weight (the tile fed to MFMA).
-__device__ __forceinline__ f16x8 pf_dequant(f16x8 codes, f16 s, f16 b) {
-    const f16x8 cv = {(f16)16.0f, (f16)16.0f, (f16)16.0f, (f16)16.0f, (f16)16.0f, (f16)16.0f, (f16)16.0f, (f16)16.0f};
+// The 4-bit values q of one word as fp16, in the pair order of pf_codes, for the fp16-weight
+// path.  Each nibble stays where it is: one at bits 0..3 of a half reads as 1024 + q under
+// the exponent of 1024 (ulp 1), one at bits 4..7 as 64 + q under the exponent of 64 (ulp
+// 1/16), so a word costs one shift and four v_and_or_b32; subtracting the constants is exact.
+// m1024 and m64 hold fp16 1024 and 64 in both halves (in VGPRs, as `magic` of pf_codes).
+__device__ __forceinline__ f16x8 pf_q4(uint32_t w, uint32_t m1024, uint32_t m64) {
+    const uint32_t t = w >> 8;
+    const uint32_t u[4] = {(w & 0x000F000Fu) | m1024,    // (q0, q4)
+                           (w & 0x00F000F0u) | m64,      // (q1, q5)
+                           (t & 0x000F000Fu) | m1024,    // (q2, q6)
+                           (t & 0x00F000F0u) | m64};     // (q3, q7)
+    const f16x8 off = {(f16)1024.0f, (f16)1024.0f, (f16)64.0f, (f16)64.0f,
+                       (f16)1024.0f, (f16)1024.0f, (f16)64.0f, (f16)64.0f};
+    return __builtin_bit_cast(f16x8, u) - off;
+}
+
+// fp16(s q + b) from the exact q: one fp16 fma, a single rounding of the dequantized weight
+// (the tile fed to MFMA).
+__device__ __forceinline__ f16x8 pf_dequant(f16x8 q, f16 s, f16 b) {
     const f16x8 sv = {s, s, s, s, s, s, s, s}, bv = {b, b, b, b, b, b, b, b};
-    return __builtin_elementwise_fma(codes - cv, sv, bv);
+    return __builtin_elementwise_fma(q, sv, bv);
 }
 
 // XCD-aware block order: blocks are handed to the 8 XCDs round-robin by linear id, so the
@@ -271,11 +286,28 @@ __device__ __forceinline__ void pf_gemm_body(const PfGemm& a, int rb, int ntok, 
     // weights of steps ks + 1 .. ks + D - 1 in flight
     constexpr int D = NTE >= 4 ? 2 : 4;
     uint4 xr[D][NTE];
+    // fp16-weight path (LDS holds it to three waves per SIMD, so registers are to spare): the
+    // activation rows this thread stages and the weight rows of its feature as pointers formed
+    // once, a step's load then pointer + step offset (an immediate when NS > 0).  Elsewhere
+    // (four waves, at most 128 registers) the addresses are formed per load.
+    constexpr bool HOIST = DQ;
+    const uint16_t* xrp[HOIST ? NTE : 1];
+    const uint32_t* wrp[HOIST ? NMAT : 1];
+    if constexpr (HOIST) {
+#pragma unroll
+        for (int q = 0; q < NTE; ++q) xrp[q] = a.act + (long)sm.arow[q * 16 + sr] * K + kofs * PF_KS + sc * 8;
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) wrp[m] = (EXTRA ? xw : wb[m] + woff) + (long)kofs * (PF_KS * BITS / 32);
+    }
     auto load_x = [&](uint4 (&x)[NTE], int ks) {
         ks = min(ks, nsteps - 1);
 #pragma unroll
-        for (int q = 0; q < NTE; ++q)
-            x[q] = reinterpret_cast<const uint4*>(a.act + (long)sm.arow[q * 16 + sr] * K + (kofs + ks) * PF_KS)[sc];
+        for (int q = 0; q < NTE; ++q) {
+            if constexpr (HOIST)
+                x[q] = *reinterpret_cast<const uint4*>(xrp[q] + ks * PF_KS);
+            else
+                x[q] = reinterpret_cast<const uint4*>(a.act + (long)sm.arow[q * 16 + sr] * K + (kofs + ks) * PF_KS)[sc];
+        }
     };
     auto commit_x = [&](const uint4 (&x)[NTE], int buf) {
 #pragma unroll
@@ -288,8 +320,12 @@ __device__ __forceinline__ void pf_gemm_body(const PfGemm& a, int rb, int ntok, 
 #pragma unroll
         for (int m = 0; m < NMAT; ++m) {
             const int kg = kofs + ks;
-            const uint4* src = EXTRA ? reinterpret_cast<const uint4*>(xw + kg * (PF_KS * BITS / 32))
-                                     : reinterpret_cast<const uint4*>(wb[m] + (woff + (uint32_t)kg * (PF_KS * BITS / 32)));
+            const uint4* src;
+            if constexpr (HOIST)
+                src = reinterpret_cast<const uint4*>(wrp[m] + ks * (PF_KS * BITS / 32));
+            else
+                src = EXTRA ? reinterpret_cast<const uint4*>(xw + kg * (PF_KS * BITS / 32))
+                            : reinterpret_cast<const uint4*>(wb[m] + (woff + (uint32_t)kg * (PF_KS * BITS / 32)));
 #pragma unroll
             for (int v = 0; v < WPU; ++v) {
                 const uint4 x = src[v];
@@ -316,6 +352,8 @@ __device__ __forceinline__ void pf_gemm_body(const PfGemm& a, int rb, int ntok, 
     constexpr float C = code_div<BITS>();
     uint32_t magic = BITS == 4 ? 0x4C004C00u : 0x5C005C00u;   // fp16 C in both halves
     asm volatile("" : "+v"(magic));
+    uint32_t m1024 = 0x64006400u, m64 = 0x54005400u;            // fp16 1024 and 64 (pf_q4)
+    if constexpr (DQ) asm volatile("" : "+v"(m1024), "+v"(m64));
     const f16x8 ones = {(f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f, (f16)1.0f};
     // input unit (8 inputs) of the step that this lane's register slot (g, mm) holds after the
     // exchange: unit = 8 g + 2 mm + 4 (j & 1) + (j >> 1)
@@ -376,8 +414,10 @@ __device__ __forceinline__ void pf_gemm_body(const PfGemm& a, int rb, int ntok, 
             for (int m = 0; m < NMAT; ++m)
 #pragma unroll
                 for (int mm = 0; mm < 2; ++mm) {
-                    bw[m][mm] = pf_codes<BITS>(&cw[m][(2 * mm + g) * WPU], magic);
-                    if constexpr (DQ) bw[m][mm] = pf_dequant(bw[m][mm], sh[m][g], bh[m][g]);
+                    if constexpr (DQ)
+                        bw[m][mm] = pf_dequant(pf_q4(cw[m][2 * mm + g], m1024, m64), sh[m][g], bh[m][g]);
+                    else
+                        bw[m][mm] = pf_codes<BITS>(&cw[m][(2 * mm + g) * WPU], magic);
                 }
 #pragma unroll
             for (int c = 0; c < NTE; ++c) {
