@@ -28,7 +28,7 @@ namespace qmoe {
 namespace {
 
 struct Layout {
-    size_t logits, gate, zg, zu, zd, gs, us, idx, wts, offs, perm, wrec, wpairs, h, hs, o, os,
+    size_t logits, gate, zg, zu, zd, gs, us, idx, wts, scnt, wrec, wpairs, h, hs, o, os,
         total;
 };
 
@@ -53,8 +53,7 @@ Layout layout_of(const qmoe_moe_layer& L, int T) {
     l.us = take(ks * T * L.shared_inter * 4);
     l.idx = take(TK * 4);
     l.wts = take(TK * 4);
-    l.offs = take((size_t)(L.n_experts + 1) * 4);
-    l.perm = take(TK * 4);
+    l.scnt = take((size_t)PF_SORT_MAXSEG * L.n_experts * 4);
     const size_t items = ((size_t)L.n_experts + (TK + 15) / 16 + 7) / 8 * 8;   // >= the sort's items
     l.wrec = take(items * 16);
     l.wpairs = take(items * PF_ITEM * 4);
@@ -99,8 +98,7 @@ hipError_t launch_moe(const qmoe_moe_layer& L, int stage, const uint16_t* x, int
     a.us = reinterpret_cast<float*>(base + lo.us);
     a.idx = reinterpret_cast<int32_t*>(base + lo.idx);
     a.wts = reinterpret_cast<float*>(base + lo.wts);
-    a.offs = reinterpret_cast<int32_t*>(base + lo.offs);
-    a.perm = reinterpret_cast<int32_t*>(base + lo.perm);
+    a.scnt = reinterpret_cast<int32_t*>(base + lo.scnt);
     a.wrec = reinterpret_cast<int32_t*>(base + lo.wrec);
     a.wpairs = reinterpret_cast<int32_t*>(base + lo.wpairs);
     a.h = reinterpret_cast<uint16_t*>(base + lo.h);

@@ -13,6 +13,7 @@ constexpr int MAX_K = 32;
 constexpr int MAX_DEC_T = 32;  // the decode path serves up to this many tokens per call
 constexpr int MAX_DEC_K = 8;   // ... and up to this many experts per token
 constexpr int PF_ITEM = 64;    // most pairs per work item of the token-sorted GEMMs (slots per item)
+constexpr int PF_SORT_MAXSEG = 64;   // most blocks (segments of pairs) of the multi-block sort
 
 struct QW {
     const uint32_t* p;
@@ -34,7 +35,8 @@ struct MoeArgs {
     const float* rbias;
     // workspace
     float *logits, *gate, *zg, *zu, *zd, *gs, *us;
-    int32_t *idx, *offs, *perm;
+    int32_t* idx;
+    int32_t* scnt;     // multi-block sort: per segment of pairs, the count of each expert
     int32_t* wrec;     // per work item of the token-sorted GEMMs: (expert, tokens, 0, 0)
     int32_t* wpairs;   // per work item: PF_ITEM slots of pair ids (the item's count used)
     float* wts;

@@ -1080,69 +1080,142 @@ __device__ int block_scan_excl(int v, int* wsum, int* total) {
     return r;
 }
 
+// Stable ranks, per expert, of one chunk of 1024 pairs (thread tid holds pair s0 + tid of
+// expert ex; valid: the pair exists).  Lanes with the same expert are found by ballots on
+// the expert's index bits, which gives each pair its rank among them in its wave; the waves'
+// counts per expert are then offset by a prefix over the chunk's 16 waves (tab, LDS).
+// Returns the pair's rank among the chunk's pairs of its expert; cnt[e] (tid = e < E) gets the
+// chunk's count of expert e.  Every thread of the block calls it.
+__device__ int chunk_rank(int ex, bool valid, int E, uint16_t (&tab)[16][1024], int* cnt) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ebits = E > 1 ? 32 - __builtin_clz(E - 1) : 0;
+    uint64_t same = __ballot(valid);
+    for (int bt = 0; bt < ebits; ++bt) {
+        const bool bit = (ex >> bt) & 1;
+        const uint64_t bb = __ballot(bit);
+        same &= bit ? bb : ~bb;
+    }
+    const int rank = __popcll(same & ((1ull << lane) - 1));
+    if (tid < E)
+        for (int w = 0; w < 16; ++w) tab[w][tid] = 0;
+    __syncthreads();
+    if (valid && rank == 0) tab[wave][ex] = (uint16_t)__popcll(same);
+    __syncthreads();
+    if (tid < E) {
+        int run = 0;
+        for (int w = 0; w < 16; ++w) {
+            const int v = tab[w][tid];
+            tab[w][tid] = (uint16_t)run;
+            run += v;
+        }
+        cnt[tid] = run;
+    }
+    __syncthreads();
+    return valid ? tab[wave][ex] + rank : 0;
+}
+
+// The work items of expert e (tid = e < E; count c, first item wex): records (expert,
+// tokens) of chunks of at most isz pairs.
+__device__ __forceinline__ void write_records(const MoeArgs& a, int c, int wex, int isz) {
+    const int nw = (c + isz - 1) / isz;
+    for (int w = 0; w < nw; ++w)
+        reinterpret_cast<int4*>(a.wrec)[wex + w] = int4{(int)threadIdx.x, min(isz, c - w * isz), 0, 0};
+}
+
 // Stable counting sort of the (token, k) pairs by expert (pair p = t * K + k), written as
 // GEMM work items: chunks of at most isz pairs of one expert, each a record (expert,
-// tokens) and its pair ids (PF_ITEM slots per item); records past the last item get zero tokens.  One block of 1024 threads.  Ranks inside each chunk of 64 pairs come from
-// ballots on the expert index bits (lanes with the same expert); the chunks of a segment of
-// 1024 pairs are then offset per expert by a prefix over the segment's 16 chunk counts.
+// tokens) and its pair ids (PF_ITEM slots per item); records past the last item get zero
+// tokens.  One block of 1024 threads over chunks of 1024 pairs.
 __global__ void __launch_bounds__(1024) k_pf_sort(MoeArgs a, int max_items, int isz) {
-    __shared__ int cnt[1024], base[1024], eoff[1024], ewex[1024], wsum[32], tot;
+    __shared__ int cnt[1024], base[1024], ewex[1024], wsum[32], tot;
     __shared__ uint16_t tab[16][1024];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x;
     const int E = a.E, TK = a.T * a.K;
     cnt[tid] = 0;
     __syncthreads();
     for (int p = tid; p < TK; p += 1024) atomicAdd(&cnt[a.idx[p]], 1);
     __syncthreads();
     const int c = tid < E ? cnt[tid] : 0;
-    const int excl = block_scan_excl(c, wsum, &tot);
-    const int nw = (c + isz - 1) / isz;
-    const int wex = block_scan_excl(nw, wsum, &tot);
+    const int wex = block_scan_excl((c + isz - 1) / isz, wsum, &tot);
     if (tid < E) {
-        a.offs[tid] = excl;
-        base[tid] = excl;
-        eoff[tid] = excl;
+        base[tid] = 0;   // pairs of expert tid in the chunks before
         ewex[tid] = wex;
-        for (int w = 0; w < nw; ++w)
-            reinterpret_cast<int4*>(a.wrec)[wex + w] = int4{tid, min(isz, c - w * isz), 0, 0};
+        write_records(a, c, wex, isz);
     }
-    if (tid == 0) a.offs[E] = TK;
     __syncthreads();
     for (int it = tot + tid; it < max_items; it += 1024) reinterpret_cast<int4*>(a.wrec)[it] = int4{0, 0, 0, 0};
-    const int ebits = E > 1 ? 32 - __builtin_clz(E - 1) : 0;
-    const uint64_t lt = (1ull << lane) - 1;
     for (int s0 = 0; s0 < TK; s0 += 1024) {
         const int p = s0 + tid;
         const bool valid = p < TK;
         const int ex = valid ? a.idx[p] : 0;
-        uint64_t same = __ballot(valid);
-        for (int bt = 0; bt < ebits; ++bt) {
-            const bool bit = (ex >> bt) & 1;
-            const uint64_t bb = __ballot(bit);
-            same &= bit ? bb : ~bb;
-        }
-        const int rank = __popcll(same & lt);
-        if (tid < E)
-            for (int w = 0; w < 16; ++w) tab[w][tid] = 0;
-        __syncthreads();
-        if (valid && rank == 0) tab[wave][ex] = (uint16_t)__popcll(same);
-        __syncthreads();
-        if (tid < E) {
-            int run = 0;
-            for (int w = 0; w < 16; ++w) {
-                const int v = tab[w][tid];
-                tab[w][tid] = (uint16_t)run;
-                run += v;
-            }
-            cnt[tid] = run;
-        }
-        __syncthreads();
+        const int r = chunk_rank(ex, valid, E, tab, cnt);
         if (valid) {
-            const int pos = base[ex] + tab[wave][ex] + rank;
-            a.perm[pos] = p;
-            // the pair's slot in its work item
-            const int r = pos - eoff[ex];
-            a.wpairs[(long)(ewex[ex] + r / isz) * PF_ITEM + r % isz] = p;
+            const int q = base[ex] + r;   // the pair's rank among the pairs of its expert
+            a.wpairs[(long)(ewex[ex] + q / isz) * PF_ITEM + q % isz] = p;
+        }
+        __syncthreads();
+        if (tid < E) base[tid] += cnt[tid];
+        __syncthreads();
+    }
+}
+
+// Chunks of 1024 pairs per block of the multi-block sort (at most PF_SORT_MAXSEG blocks).
+__host__ __device__ inline int sort_chunks_per_block(int TK) {
+    const int chunks = (TK + 1023) / 1024;
+    return (chunks + PF_SORT_MAXSEG - 1) / PF_SORT_MAXSEG;
+}
+
+// Multi-block sort, pass 1: block s counts the experts of its segment (cpb chunks of 1024
+// pairs) into scnt[s][e].
+__global__ void __launch_bounds__(1024) k_pf_count(MoeArgs a, int cpb) {
+    __shared__ int cnt[1024];
+    const int tid = threadIdx.x, E = a.E, TK = a.T * a.K;
+    const int p0 = blockIdx.x * cpb * 1024;
+    if (tid < E) cnt[tid] = 0;
+    __syncthreads();
+    for (int c = 0; c < cpb; ++c) {
+        const int p = p0 + c * 1024 + tid;
+        if (p < TK) atomicAdd(&cnt[a.idx[p]], 1);
+    }
+    __syncthreads();
+    if (tid < E) a.scnt[(long)blockIdx.x * E + tid] = cnt[tid];
+}
+
+// Multi-block sort, pass 2: block s places the pairs of its segment.  Each block forms from
+// the segments' counts the rank, inside expert e, of its segment's first pair of e (the
+// counts of the earlier segments) and the items of every expert (a block scan of the totals);
+// block 0 writes the item records.  Inside the segment the ranks are those of k_pf_sort, so
+// the items hold the same pairs in the same order.
+__global__ void __launch_bounds__(1024) k_pf_place(MoeArgs a, int max_items, int isz, int cpb, int nseg) {
+    __shared__ int cnt[1024], base[1024], ewex[1024], wsum[32], tot;
+    __shared__ uint16_t tab[16][1024];
+    const int tid = threadIdx.x, E = a.E, TK = a.T * a.K, s = blockIdx.x;
+    int before = 0, total = 0;
+    if (tid < E) {
+        for (int q = 0; q < nseg; ++q) {
+            const int c = a.scnt[(long)q * E + tid];
+            total += c;
+            before += q < s ? c : 0;
+        }
+    }
+    const int wex = block_scan_excl((total + isz - 1) / isz, wsum, &tot);
+    if (tid < E) {
+        base[tid] = before;
+        ewex[tid] = wex;
+        if (s == 0) write_records(a, total, wex, isz);
+    }
+    if (s == 0)
+        for (int it = tot + tid; it < max_items; it += 1024) reinterpret_cast<int4*>(a.wrec)[it] = int4{0, 0, 0, 0};
+    __syncthreads();
+    const int p0 = s * cpb * 1024;
+    for (int c = 0; c < cpb; ++c) {
+        const int p = p0 + c * 1024 + tid;
+        const bool valid = p < TK;
+        const int ex = valid ? a.idx[p] : 0;
+        const int r = chunk_rank(ex, valid, E, tab, cnt);
+        if (valid) {
+            const int q = base[ex] + r;
+            a.wpairs[(long)(ewex[ex] + q / isz) * PF_ITEM + q % isz] = p;
         }
         __syncthreads();
         if (tid < E) base[tid] += cnt[tid];
@@ -1353,7 +1426,14 @@ hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s) {
         if (kp <= 2) k_pf_token<2><<<a.T, 256, tsm, s>>>(a, ksplit);
         else if (kp <= 4) k_pf_token<4><<<a.T, 256, tsm, s>>>(a, ksplit);
         else k_pf_token<8><<<a.T, 256, tsm, s>>>(a, ksplit);
-        k_pf_sort<<<1, 1024, 0, s>>>(a, items, isz);
+        const int TK = a.T * a.K;
+        if (TK <= 2048) {
+            k_pf_sort<<<1, 1024, 0, s>>>(a, items, isz);
+        } else {
+            const int cpb = sort_chunks_per_block(TK), nseg = (TK + cpb * 1024 - 1) / (cpb * 1024);
+            k_pf_count<<<nseg, 1024, 0, s>>>(a, cpb);
+            k_pf_place<<<nseg, 1024, 0, s>>>(a, items, isz, cpb, nseg);
+        }
     }
     if (all || stage == QMOE_STAGE_GATE_UP) {
         PfGemm p = grouped(a, a.eg, &a.eu, a.I, a.H, a.x, a.K, items);

@@ -153,6 +153,29 @@ def test_prefill_64_pair_items(q, T, S):
     print(f"64-pair items T={T}: max abs {err:.2e} rel L2 {rel:.2e} alternatives {n_alt}", flush=True)
 
 
+SORT_16 = Shape(hidden=512, inter=512, shared_inter=512, n_experts=16, top_k=4, rank=8, n_adapters=2)
+
+
+@pytest.mark.parametrize("T,S,n_check", [(1500, SMALL, None), (16500, SORT_16, 300)],
+                         ids=["3000-pairs", "66000-pairs"])
+def test_prefill_multi_block_sort(q, T, S, n_check):
+    """More than 2048 (token, expert) pairs: the expert sort runs as per-segment counts and a
+    placement pass over segments of 1024-pair chunks; 3000 pairs end in a ragged chunk,
+    66000 pairs make each block place two chunks.  The layer is per token, so at 16500 tokens
+    the oracle checks a seeded sample of the device's rows (first and last tokens included)."""
+    Lc = build_layer(synth.Workload.TEST, 19, S)
+    x = synth.activations(T, S.hidden, synth.Workload.TEST, 19, T)
+    ad = (np.arange(T) % 2).astype(np.int32)
+    y, idx, w = run_device(q, Lc, S, x, ad)
+    rows = np.arange(T)
+    if n_check is not None:
+        rng = np.random.default_rng(T)
+        rows = np.unique(np.concatenate([[0, T - 1], rng.choice(T, n_check, replace=False)]))
+    err, rel, n_alt = check_layer(Lc, x[rows], ad[rows], y[rows], idx[rows], w[rows])
+    print(f"multi-block sort T={T}: max abs {err:.2e} rel L2 {rel:.2e} alternatives {n_alt} "
+          f"({len(rows)} rows)", flush=True)
+
+
 def test_decode_one_token_full_shape(q):
     """The single-token decode workload: hidden 2048, 256 experts, top-4, shared expert with
     8-bit gate, LoRA rank 16 alpha 32 on the shared projections."""
