@@ -621,7 +621,10 @@ __device__ __forceinline__ void pf_res_block(const PfGemm& a, int rbg, int item,
         }
     }
     __syncthreads();
+    // fp16 weights for grouped blocks of four token tiles, as in pf_gemm_body; exact codes else
+    constexpr bool DQ = NT >= 4 && (FL & F_GROUPED);
     // group sums of the activation rows (fp32; the pair order stays inside a unit)
+    if constexpr (!DQ)
     for (int q = threadIdx.x; q < 16 * NT * G; q += 256) {
         const int r = q % (16 * NT), g = q / (16 * NT);
         const uint4* row = reinterpret_cast<const uint4*>(sm.tile + r * PITCH + g * 64);
@@ -635,8 +638,11 @@ __device__ __forceinline__ void pf_res_block(const PfGemm& a, int rbg, int item,
     constexpr float C = code_div<4>();
     uint32_t magic = 0x4C004C00u;
     asm volatile("" : "+v"(magic));
+    uint32_t m1024 = 0x64006400u, m64 = 0x54005400u;   // fp16 1024 and 64 (pf_q4)
+    if constexpr (DQ) asm volatile("" : "+v"(m1024), "+v"(m64));
     const int ubase = 4 * (j & 1) + (j >> 1);
     const int ntiles = (ntok + 15) >> 4;
+    int toff = 0;
     f32x4 acc[NT];
 #pragma unroll
     for (int c = 0; c < NT; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -656,6 +662,29 @@ __device__ __forceinline__ void pf_res_block(const PfGemm& a, int rbg, int item,
         const uint32_t* svw = reinterpret_cast<const uint32_t*>(&sv[rbl & 1][0]);
         const uint32_t* bvw = reinterpret_cast<const uint32_t*>(&bvv[rbl & 1][0]);
         const uint32_t s2 = svw[ks], b2 = bvw[ks];   // groups 2 ks, 2 ks + 1 as fp16 pairs
+        if constexpr (DQ) {
+            // fp16(s q + b) weights, every tile computed (padding rows of the tile included,
+            // never stored); a row block's first MFMA starts from zero, so no instruction
+            // rewrites an accumulator between MFMAs.  The tile offset is made opaque per row
+            // block: the activation fragments are the same in every row block, and the
+            // compiler would otherwise keep all of them live in registers across row blocks.
+            if (ks == 0) asm volatile("" : "+v"(toff));
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                const f16 sh = as_h2(s2)[g], bh = as_h2(b2)[g];
+                const f16x8 bw0 = pf_dequant(pf_q4(cw[g], m1024, m64), sh, bh);
+                const f16x8 bw1 = pf_dequant(pf_q4(cw[2 + g], m1024, m64), sh, bh);
+#pragma unroll
+                for (int c = 0; c < NT; ++c) {
+                    const f16* trow = sm.tile + toff + (c * 16 + col) * PITCH + ks * PF_KS;
+                    const f16x8 a0 = *reinterpret_cast<const f16x8*>(trow + 8 * (8 * g + ubase));
+                    const f16x8 a1 = *reinterpret_cast<const f16x8*>(trow + 8 * (8 * g + 2 + ubase));
+                    const f32x4 c0 = ks == 0 && g == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[c];
+                    acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bw0, c0, 0, 0, 0);
+                    acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bw1, acc[c], 0, 0, 0);
+                }
+            }
+        } else
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
             const float s = g ? half_hi(s2) : half_lo(s2);
@@ -689,8 +718,9 @@ __device__ __forceinline__ void pf_res_block(const PfGemm& a, int rbg, int item,
                     }
                 }
             }
+            if constexpr (!DQ)
 #pragma unroll
-            for (int c = 0; c < NT; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int c = 0; c < NT; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
 }
@@ -699,7 +729,8 @@ __device__ __forceinline__ void pf_res_block(const PfGemm& a, int rbg, int item,
 // resident activations: blocks below nbg take (work item, row group), the rest (token
 // group, row group).
 template <int NS, int NT, int RBG>
-__global__ void __launch_bounds__(256) k_pf_down_res(PfGemm g, PfGemm d, int nbg) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+k_pf_down_res(PfGemm g, PfGemm d, int nbg) {
     __shared__ __align__(16) PfResSmem<NT, NS> sm;
     int rbg, item;
     if ((int)blockIdx.x < nbg) {
@@ -1450,7 +1481,7 @@ hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s) {
         q.out0 = a.os;
         const int nbg = p.nrb * p.items;
         const dim3 grid((unsigned)(nbg + q.nrb * q.items));
-        if (a.I == a.SI && isz <= 32 && (a.I == 512 || (a.I == 1024 && isz == 16))) {
+        if (a.I == a.SI && (a.I == 512 || (a.I == 1024 && isz == 16))) {
             // resident activations: row groups of PF_RES_RBG row blocks, token groups of isz
             constexpr int RBG = PF_RES_RBG;
             const int nt = isz / 16;
@@ -1464,6 +1495,7 @@ hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s) {
             switch ((a.I / PF_KS) * 2 + nt - 1) {
                 case 8: k_pf_down_res<4, 1, RBG><<<gr, 256, 0, s>>>(p, q, nbr); break;
                 case 9: k_pf_down_res<4, 2, RBG><<<gr, 256, 0, s>>>(p, q, nbr); break;
+                case 11: k_pf_down_res<4, 4, RBG><<<gr, 256, 0, s>>>(p, q, nbr); break;
                 default: k_pf_down_res<8, 1, RBG><<<gr, 256, 0, s>>>(p, q, nbr); break;
             }
         } else if (a.I == a.SI && (a.I == 512 || a.I == 1024 || a.I == 2048)) {
