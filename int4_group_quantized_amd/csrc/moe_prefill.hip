@@ -14,17 +14,19 @@
 // weights as B (32 inputs x 16 features): lane l supplies feature l % 16 and inputs
 // 8 (l / 16) .. +7, and ends with tokens 4 (l / 16) .. +3 of feature l % 16.
 //
-// Weights.  A lane turns each packed word into the fp16 codes C + q (the code's bits dropped
-// into the mantissa of C = 16 or 256; exact).  Where the GEMM is bound by HBM (up to two
-// token tiles) the weights stay exact: each MFMA pair covers exactly one 64-input group, so
-// the group's sum P = sum (C + q) x is formed apart and, with the group's sum of inputs X
-// (one more MFMA pair against a ones operand), the affine terms are applied per group in
-// fp32:
+// Weights.  In the grouped expert GEMMs a lane turns each packed word into the exact values
+// q in fp16 (the nibbles masked in place under the exponent of 1024 or 64, the constant then
+// subtracted) and dequantizes them with one fp16 fma, fp16(s q + b), one rounding per weight;
+// every MFMA accumulates into the row's fp32 sum.  This costs about half the vector
+// instructions of the exact form below, which matters both where the GEMM is bound by
+// HBM (the vector work sits between a wave's loads) and where it is compute-bound.
+// The dense x-side GEMMs keep the weights exact: the codes C + q (bits dropped into the
+// mantissa of C = 16 or 256) feed the MFMAs, each MFMA pair covers exactly one 64-input
+// group, so the group's sum P = sum (C + q) x is formed apart and, with the group's sum of
+// inputs X (one more MFMA pair against a ones operand), the affine terms are applied per
+// group in fp32:
 //     acc += s P + (b - C s) X.
-// In the grouped GEMMs with four token tiles the per-group terms would cost as much as the
-// MFMAs, so 4-bit weights are dequantized in fp16 there, fp16(s q + b) with q = codes - C (one rounding per
-// weight), and every MFMA accumulates into the row's fp32 sum.  The 8-bit router, whose
-// logits decide top-K, is always exact.
+// The 8-bit router, whose logits decide top-K, is always exact.
 // For that, a lane's 16-byte load of packed words (inputs 32 j .. 32 j + 31 of a 128-input
 // step, j = lane / 16, i.e. half of group j / 2) is exchanged across the wave halves with
 // v_permlane32_swap so that every register then holds words of a single group; the
@@ -199,8 +201,8 @@ __device__ __forceinline__ void pf_gemm_body(const PfGemm& a, int rb, int ntok, 
     static_assert(SM_NMAT >= NMAT, "LDS holds the scales of every matrix");
     static_assert(NTE <= NTS, "LDS holds every tile");
     constexpr bool HOUT = FL & F_HOUT, EXTRA = FL & F_EXTRA;
-    // fp16 weights for the grouped 4-bit GEMMs with four token tiles (MFMA-bound); exact codes else
-    constexpr bool DQ = BITS == 4 && NTE >= 4 && (FL & F_GROUPED);
+    // fp16 weights for the grouped 4-bit GEMMs; exact codes for the dense ones
+    constexpr bool DQ = BITS == 4 && (FL & F_GROUPED);
     const int ntiles = (ntok + 15) >> 4;   // <= NTE
     // NS > 0: the block's step count known at compile time (the loop fully unrolled); the
     // block covers steps kofs .. kofs + nsteps - 1 of the row (split-K for dense GEMMs)
@@ -621,7 +623,9 @@ __device__ __forceinline__ void pf_res_block(const PfGemm& a, int rbg, int item,
         }
     }
     __syncthreads();
-    // fp16 weights for grouped blocks of four token tiles, as in pf_gemm_body; exact codes else
+    // fp16 weights for grouped blocks of four token tiles, as in pf_gemm_body.  With fewer
+    // tiles the exact form stays: the group sums X come from LDS here, so its per-group terms
+    // cost no more vector work than the fp16 dequantization would.
     constexpr bool DQ = NT >= 4 && (FL & F_GROUPED);
     // group sums of the activation rows (fp32; the pair order stays inside a unit)
     if constexpr (!DQ)
