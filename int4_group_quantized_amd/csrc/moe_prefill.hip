@@ -201,8 +201,9 @@ __device__ __forceinline__ void pf_gemm_body(const PfGemm& a, int rb, int ntok, 
     static_assert(SM_NMAT >= NMAT, "LDS holds the scales of every matrix");
     static_assert(NTE <= NTS, "LDS holds every tile");
     constexpr bool HOUT = FL & F_HOUT, EXTRA = FL & F_EXTRA;
-    // fp16 weights for the grouped 4-bit GEMMs; exact codes for the dense ones
-    constexpr bool DQ = BITS == 4 && (FL & F_GROUPED);
+    // fp16 weights for the grouped 4-bit GEMMs and the dense ones with four token tiles;
+    // exact codes for the 8-bit router and for dense GEMMs of fewer tiles
+    constexpr bool DQ = BITS == 4 && ((FL & F_GROUPED) || NTE >= 4);
     const int ntiles = (ntok + 15) >> 4;   // <= NTE
     // NS > 0: the block's step count known at compile time (the loop fully unrolled); the
     // block covers steps kofs .. kofs + nsteps - 1 of the row (split-K for dense GEMMs)
@@ -623,10 +624,10 @@ __device__ __forceinline__ void pf_res_block(const PfGemm& a, int rbg, int item,
         }
     }
     __syncthreads();
-    // fp16 weights for grouped blocks of four token tiles, as in pf_gemm_body.  With fewer
+    // fp16 weights for blocks of four token tiles, as in pf_gemm_body.  With fewer
     // tiles the exact form stays: the group sums X come from LDS here, so its per-group terms
     // cost no more vector work than the fp16 dequantization would.
-    constexpr bool DQ = NT >= 4 && (FL & F_GROUPED);
+    constexpr bool DQ = NT >= 4;
     // group sums of the activation rows (fp32; the pair order stays inside a unit)
     if constexpr (!DQ)
     for (int q = threadIdx.x; q < 16 * NT * G; q += 256) {
