@@ -32,6 +32,7 @@
 // v_permlane32_swap so that every register then holds words of a single group; the
 // activation side reads the matching inputs from LDS.
 #include <algorithm>
+#include <type_traits>
 
 #include "gemv_core.hpp"
 #include "launch.hpp"
@@ -48,6 +49,7 @@ constexpr int PF_PITCH = PF_KS + 8;   // LDS row pitch in halves (272 bytes: no 
 constexpr int PF_XS_K = 512;          // inputs per block of the split-K x-side GEMMs (few tokens)
 constexpr int PF_XS_K_BIG = 2048;     // the same from PF_XS_BIG_T tokens up (enough blocks unsplit)
 constexpr int PF_XS_BIG_T = 2048;
+constexpr int PF_MANY_T = 1024;       // from this many tokens the per-token kernels favour occupancy
 
 struct PfGemm {
     const uint32_t* p[2];
@@ -942,7 +944,7 @@ __device__ __forceinline__ float bdot_tail(const uint16_t* __restrict__ brow, co
 }
 
 constexpr int TOK_HW = 3;   // waves of k_pf_token on the shared expert's h
-constexpr int TOK_NPC = 4;  // h outputs per thread whose loads are issued together
+constexpr int TOK_NPC = 4;  // h outputs per thread whose loads are issued together (few tokens)
 
 // Per-token finish of the x side, one block of 4 waves per token.  Wave 0 sums the token's
 // router-logit partials in registers and runs top-K.  Waves 1-3 sum the shared-gate logit and
@@ -951,8 +953,8 @@ constexpr int TOK_NPC = 4;  // h outputs per thread whose loads are issued toget
 // LDS.  Every wave meanwhile fetches its first rows of the down LoRA's A.  After the one barrier:
 // h_s and the selection are written out and z_d = A_down h_s is taken, one wave per four rank
 // rows.  Split-K partials are added in split order, LoRA chunks in chunk order.
-template <int KP>
-__global__ void __launch_bounds__(256) k_pf_token(MoeArgs a, int ksplit) {
+template <int KP, int NPC>
+__device__ __forceinline__ void pf_token_body(const MoeArgs& a, int ksplit) {
     extern __shared__ __align__(16) uint16_t hl[];        // h_s of the token, fp16 [SI]
     __shared__ int sel[MAX_K];
     __shared__ float sw[MAX_K];
@@ -965,13 +967,17 @@ __global__ void __launch_bounds__(256) k_pf_token(MoeArgs a, int ksplit) {
     const uint16_t* abase = has_d ? a.Ad + (long)adapter_of(a.adapter, t, a.nad) * a.rd * SI : a.hs;
     const long astride = has_d ? SI : 0;
     const int rd = has_d ? a.rd : 0;
-    uint4 av0[4][2];
+    // (few tokens only: with many, the registers go to more tokens in flight instead)
+    constexpr bool PRE = NPC > 1;
+    uint4 av0[PRE ? 4 : 1][2];
+    if constexpr (PRE) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-            av0[q][i] = *reinterpret_cast<const uint4*>(abase + min(4 * wave + q, max(rd - 1, 0)) * astride +
-                                                        min(lane * 8 + i * 512, SI - 8));
+            for (int i = 0; i < 2; ++i)
+                av0[q][i] = *reinterpret_cast<const uint4*>(abase + min(4 * wave + q, max(rd - 1, 0)) * astride +
+                                                            min(lane * 8 + i * 512, SI - 8));
+    }
 
     if (wave == 0) {
         token_topk_any<KP>(a, t, ksplit, sel, sw);
@@ -991,11 +997,11 @@ __global__ void __launch_bounds__(256) k_pf_token(MoeArgs a, int ksplit) {
         const int gs = fg ? a.rg : 0, us = fu ? a.ru : 0;
         const int g8 = max(min(a.rg, 16) - 8, 0), u8 = max(min(a.ru, 16) - 8, 0);
         bool first = true;
-        for (int n0 = u; n0 < SI; n0 += TOK_NPC * TOK_HW * 64) {
-            Parts<KP> pg[TOK_NPC], pu[TOK_NPC];
-            uint4 bg[TOK_NPC][2], bu[TOK_NPC][2];
+        for (int n0 = u; n0 < SI; n0 += NPC * TOK_HW * 64) {
+            Parts<KP> pg[NPC], pu[NPC];
+            uint4 bg[NPC][2], bu[NPC][2];
 #pragma unroll
-            for (int c = 0; c < TOK_NPC; ++c) {
+            for (int c = 0; c < NPC; ++c) {
                 const int n = min(n0 + c * TOK_HW * 64, SI - 1);
                 pg[c].load(a.gs + (long)t * SI + n, pgu, ksplit);
                 pu[c].load(a.us + (long)t * SI + n, pgu, ksplit);
@@ -1014,7 +1020,7 @@ __global__ void __launch_bounds__(256) k_pf_token(MoeArgs a, int ksplit) {
                 first = false;
             }
 #pragma unroll
-            for (int c = 0; c < TOK_NPC; ++c) {
+            for (int c = 0; c < NPC; ++c) {
                 const int n = n0 + c * TOK_HW * 64;
                 if (n < SI) {
                     float gv = pg[c].sum(ksplit), uv = pu[c].sum(ksplit);
@@ -1047,7 +1053,7 @@ __global__ void __launch_bounds__(256) k_pf_token(MoeArgs a, int ksplit) {
     }
     if (!has_d) return;
     // z_d: rows r0 .. r0 + 3 per wave, 1024 inputs (2 x 8 per lane) per pass
-    auto pass = [&](const uint4 (&av)[4][2], int k0, float (&acc)[4]) {
+    auto pass = [&](const auto& av, int k0, float (&acc)[4]) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int k = k0 + lane * 8 + i * 512;
@@ -1066,7 +1072,7 @@ __global__ void __launch_bounds__(256) k_pf_token(MoeArgs a, int ksplit) {
     for (int r0 = 4 * wave; r0 < rd; r0 += 16) {
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
         for (int k0 = 0; k0 < SI; k0 += 1024) {
-            if (r0 == 4 * wave && k0 == 0) {
+            if (PRE && r0 == 4 * wave && k0 == 0) {
                 pass(av0, 0, acc);
             } else {
                 uint4 av[4][2];
@@ -1086,6 +1092,16 @@ __global__ void __launch_bounds__(256) k_pf_token(MoeArgs a, int ksplit) {
         }
     }
 }
+
+// Few tokens: every block in flight at once, each issuing all its loads together.
+template <int KP>
+__global__ void __launch_bounds__(256) k_pf_token(MoeArgs a, int ksplit) { pf_token_body<KP, TOK_NPC>(a, ksplit); }
+
+// Many tokens (several rounds of blocks): one h output per thread in flight, so that four waves
+// fit a SIMD and twice the tokens are in flight.
+template <int KP>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
+k_pf_token_many(MoeArgs a, int ksplit) { pf_token_body<KP, 1>(a, ksplit); }
 
 // Inclusive prefix sum over the wave.
 __device__ __forceinline__ int wave_scan(int v) {
@@ -1259,59 +1275,67 @@ __global__ void __launch_bounds__(1024) k_pf_place(MoeArgs a, int max_items, int
     }
 }
 
-// y = fp16(sum_k w_k o_k + sigmoid(gate) (os + LoRA_down)) (+ residual), k in order.  Eight
-// outputs of one token per thread with 16-byte loads.  Every load of the common case (up to 8 experts,
-// LoRA rank a multiple of 8 up to 16) is issued before any use, one memory round trip: the
-// experts' rows and weights, the shared output and gate logit, the residual, the eight
-// LoRA-B rows (contiguous) and z_d.  Absent operands are read from a valid stand-in and not
-// used; more experts or a larger rank continue with further passes.
-__global__ void __launch_bounds__(256) k_pf_combine(MoeArgs a) {
-    constexpr int KF = 8;
-    // block: 16 tokens x 128 features, so the block's LoRA-B rows (128 x rank) are read
+// y = fp16(sum_k w_k o_k + sigmoid(gate) (os + LoRA_down)) (+ residual), k in order.  FPT
+// outputs of one token per thread (8, or 4 with many tokens) with 16-byte loads.  Every load
+// of the common case (up to KF experts, LoRA rank a multiple of 8 up to 16) is issued before
+// any use, one memory round trip: the experts' rows and weights, the shared output and gate
+// logit, the residual, the FPT LoRA-B rows (contiguous) and z_d.  Absent operands are read
+// from a valid stand-in and not used; more experts or a larger rank continue with further
+// passes.
+template <int KF, int FPT>
+__device__ __forceinline__ void pf_combine_body(const MoeArgs& a) {
+    constexpr int TPR = 128 / FPT, TPB = 256 / TPR, NV = FPT / 4;   // threads per token row, tokens per block
+    using XV = std::conditional_t<FPT == 8, uint4, uint2>;          // FPT fp16 values
+    // block: TPB tokens x 128 features, so the block's LoRA-B rows (128 x rank) are read
     // from L2 once and shared by its tokens through L1
     const int nch = a.H / 128, ch = blockIdx.x % nch;
-    const int t = (blockIdx.x / nch) * 16 + (threadIdx.x >> 4);
+    const int t = (blockIdx.x / nch) * TPB + threadIdx.x / TPR;
     if (t >= a.T) return;
-    const int n = ch * 128 + (threadIdx.x & 15) * 8;
+    const int n = ch * 128 + (threadIdx.x % TPR) * FPT;
     const long i8 = (long)t * a.H + n;
     const int K = a.K;
-    float4 p[KF][2];
+    float4 p[KF][NV];
     float w[KF];
 #pragma unroll
     for (int u = 0; u < KF; ++u) {
         const int k = min(u, K - 1);
         w[u] = a.wts[(long)t * K + k];
         const float4* ok = reinterpret_cast<const float4*>(a.o + ((long)t * K + k) * a.H + n);
-        p[u][0] = ok[0];
-        p[u][1] = ok[1];
+#pragma unroll
+        for (int v = 0; v < NV; ++v) p[u][v] = ok[v];
     }
-    const float4 o0 = reinterpret_cast<const float4*>(a.os + i8)[0];
-    const float4 o1 = reinterpret_cast<const float4*>(a.os + i8)[1];
+    float4 osv[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) osv[v] = reinterpret_cast<const float4*>(a.os + i8)[v];
     const float g = a.gate[t];
-    const uint4 xr = *reinterpret_cast<const uint4*>(a.x + i8);
+    const XV xr = *reinterpret_cast<const XV*>(a.x + i8);
     const bool bfast = a.Bd && (a.rd & 7) == 0;
     const int rv = bfast ? a.rd / 8 : 1;   // uint4 per B row
     const int ad = a.Bd ? adapter_of(a.adapter, t, a.nad) : 0;
-    // 8 rows of rd halves are 8 rd contiguous halves; stand-in: the shared output
+    // FPT rows of rd halves are FPT rd contiguous halves; stand-in: the shared output
     const uint4* b4 = bfast ? reinterpret_cast<const uint4*>(a.Bd + ((long)ad * a.H + n) * a.rd)
                             : reinterpret_cast<const uint4*>(a.os + i8);
     const float* z = a.zd + (long)t * MAX_RANK;
-    uint4 bv[8][2];
+    uint4 bv[FPT][2];
     float4 zv[4];
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
+    for (int q = 0; q < FPT; ++q)
 #pragma unroll
         for (int i = 0; i < 2; ++i) bv[q][i] = b4[bfast ? q * rv + min(i, rv - 1) : 0];
 #pragma unroll
     for (int i = 0; i < 4; ++i) zv[i] = reinterpret_cast<const float4*>(z)[i];
 
-    float ov[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
-    if (bfast) {
-        float d[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        const float* zf = reinterpret_cast<const float*>(zv);
-        auto add = [&](const uint4 (&v)[8], const float* zs) {   // one uint4 per row: 8 ranks
+    float ov[FPT];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < FPT; ++q) ov[q] = reinterpret_cast<const float*>(osv)[q];
+    if (bfast) {
+        float d[FPT];
+#pragma unroll
+        for (int q = 0; q < FPT; ++q) d[q] = 0.0f;
+        const float* zf = reinterpret_cast<const float*>(zv);
+        auto add = [&](const uint4 (&v)[FPT], const float* zs) {   // one uint4 per row: 8 ranks
+#pragma unroll
+            for (int q = 0; q < FPT; ++q) {
                 const uint32_t w4[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
@@ -1323,55 +1347,65 @@ __global__ void __launch_bounds__(256) k_pf_combine(MoeArgs a) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             if (i < rv) {
-                uint4 v[8];
+                uint4 v[FPT];
 #pragma unroll
-                for (int q = 0; q < 8; ++q) v[q] = bv[q][i];
+                for (int q = 0; q < FPT; ++q) v[q] = bv[q][i];
                 add(v, zf + 8 * i);
             }
         }
         for (int r = 2; r < rv; ++r) {   // ranks past 16
-            uint4 v[8];
+            uint4 v[FPT];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) v[q] = b4[q * rv + r];
+            for (int q = 0; q < FPT; ++q) v[q] = b4[q * rv + r];
             add(v, z + 8 * r);
         }
 #pragma unroll
-        for (int q = 0; q < 8; ++q) ov[q] = fmaf(a.lsd, d[q], ov[q]);
+        for (int q = 0; q < FPT; ++q) ov[q] = fmaf(a.lsd, d[q], ov[q]);
     } else if (a.Bd) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) ov[q] = fmaf(a.lsd, lora_b_dot(a.Bd, ad, a.H, n + q, a.rd, z), ov[q]);
+        for (int q = 0; q < FPT; ++q) ov[q] = fmaf(a.lsd, lora_b_dot(a.Bd, ad, a.H, n + q, a.rd, z), ov[q]);
     }
-    float acc[8];
+    float acc[FPT];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+    for (int q = 0; q < FPT; ++q) acc[q] = 0.0f;
 #pragma unroll
     for (int u = 0; u < KF; ++u) {
         if (u < K) {
-            const float pv[8] = {p[u][0].x, p[u][0].y, p[u][0].z, p[u][0].w,
-                                 p[u][1].x, p[u][1].y, p[u][1].z, p[u][1].w};
+            const float* pv = reinterpret_cast<const float*>(p[u]);
 #pragma unroll
-            for (int q = 0; q < 8; ++q) acc[q] = fmaf(w[u], pv[q], acc[q]);
+            for (int q = 0; q < FPT; ++q) acc[q] = fmaf(w[u], pv[q], acc[q]);
         }
     }
-    for (int k = KF; k < K; ++k) {   // experts past the eighth
+    for (int k = KF; k < K; ++k) {   // experts past the KF-th
         const float wk = a.wts[(long)t * K + k];
         const float4* ok = reinterpret_cast<const float4*>(a.o + ((long)t * K + k) * a.H + n);
-        const float4 q0 = ok[0], q1 = ok[1];
-        const float pv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+        float4 qv[NV];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) acc[q] = fmaf(wk, pv[q], acc[q]);
+        for (int v = 0; v < NV; ++v) qv[v] = ok[v];
+        const float* pv = reinterpret_cast<const float*>(qv);
+#pragma unroll
+        for (int q = 0; q < FPT; ++q) acc[q] = fmaf(wk, pv[q], acc[q]);
     }
     const float gm = sigmoid(g);
-    uint16_t out[8];
+    uint16_t out[FPT];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) out[q] = f2h(fmaf(gm, ov[q], acc[q]));
+    for (int q = 0; q < FPT; ++q) out[q] = f2h(fmaf(gm, ov[q], acc[q]));
     if (a.add_residual) {
         const uint16_t* xh = reinterpret_cast<const uint16_t*>(&xr);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) out[q] = f2h(h2f(xh[q]) + h2f(out[q]));
+        for (int q = 0; q < FPT; ++q) out[q] = f2h(h2f(xh[q]) + h2f(out[q]));
     }
-    *reinterpret_cast<uint4*>(a.y + i8) = *reinterpret_cast<const uint4*>(out);
+    *reinterpret_cast<XV*>(a.y + i8) = *reinterpret_cast<const XV*>(out);
 }
+
+// Few tokens: up to eight experts' rows per thread in flight at once.
+__global__ void __launch_bounds__(256) k_pf_combine(MoeArgs a) { pf_combine_body<8, 8>(a); }
+
+// Many tokens: four outputs per thread and KF experts' rows in flight (KF = top-K when it is
+// at most 4), so that four waves fit a SIMD.
+template <int KF>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
+k_pf_combine_many(MoeArgs a) { pf_combine_body<KF, 4>(a); }
 
 template <int NMAT, int BITS, int NT, int FL>
 void pf_gemm(const PfGemm& p, hipStream_t s) {
@@ -1459,9 +1493,15 @@ hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s) {
         // KP covers the split-K partials (<= hidden / 512) and half the LoRA z chunks
         // (hidden / 256), whatever the split
         const int kp = std::max(ksplit, a.H / 512);
-        if (kp <= 2) k_pf_token<2><<<a.T, 256, tsm, s>>>(a, ksplit);
-        else if (kp <= 4) k_pf_token<4><<<a.T, 256, tsm, s>>>(a, ksplit);
-        else k_pf_token<8><<<a.T, 256, tsm, s>>>(a, ksplit);
+        if (a.T < PF_MANY_T) {
+            if (kp <= 2) k_pf_token<2><<<a.T, 256, tsm, s>>>(a, ksplit);
+            else if (kp <= 4) k_pf_token<4><<<a.T, 256, tsm, s>>>(a, ksplit);
+            else k_pf_token<8><<<a.T, 256, tsm, s>>>(a, ksplit);
+        } else {   // (eight partials do not fit the four-wave budget: the few-token kernel)
+            if (kp <= 2) k_pf_token_many<2><<<a.T, 256, tsm, s>>>(a, ksplit);
+            else if (kp <= 4) k_pf_token_many<4><<<a.T, 256, tsm, s>>>(a, ksplit);
+            else k_pf_token<8><<<a.T, 256, tsm, s>>>(a, ksplit);
+        }
         const int TK = a.T * a.K;
         if (TK <= 2048) {
             k_pf_sort<<<1, 1024, 0, s>>>(a, items, isz);
@@ -1520,7 +1560,14 @@ hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s) {
             else pf_gemm<1, 4, 4, F_GROUPED>(p, s);
             pf_gemm<1, 4, 2, 0>(q, s);
         }
-        k_pf_combine<<<(unsigned)((a.T + 15) / 16 * (a.H / 128)), 256, 0, s>>>(a);
+        // blocks of 16 (few tokens) or 8 (many) tokens x 128 features
+        if (a.T < PF_MANY_T) {
+            k_pf_combine<<<(unsigned)((a.T + 15) / 16 * (a.H / 128)), 256, 0, s>>>(a);
+        } else {
+            const unsigned cgrid = (unsigned)((a.T + 7) / 8 * (a.H / 128));
+            if (a.K <= 4) k_pf_combine_many<4><<<cgrid, 256, 0, s>>>(a);
+            else k_pf_combine_many<8><<<cgrid, 256, 0, s>>>(a);
+        }
     }
     return hipGetLastError();
 }
