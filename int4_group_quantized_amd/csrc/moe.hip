@@ -59,7 +59,7 @@ Layout layout_of(const qmoe_moe_layer& L, int T) {
     l.wpairs = take(items * PF_ITEM * 4);
     l.h = take(TK * L.inter * 2);
     l.hs = take((size_t)T * L.shared_inter * 2);
-    l.o = take(TK * L.hidden * 4);
+    l.o = take(TK * L.hidden * 2);
     l.os = take((size_t)T * L.hidden * 4);
     l.total = off;
     return l;
@@ -103,7 +103,7 @@ hipError_t launch_moe(const qmoe_moe_layer& L, int stage, const uint16_t* x, int
     a.wpairs = reinterpret_cast<int32_t*>(base + lo.wpairs);
     a.h = reinterpret_cast<uint16_t*>(base + lo.h);
     a.hs = reinterpret_cast<uint16_t*>(base + lo.hs);
-    a.o = reinterpret_cast<float*>(base + lo.o);
+    a.o = reinterpret_cast<uint16_t*>(base + lo.o);
     a.os = reinterpret_cast<float*>(base + lo.os);
     a.idx_out = idx_out;
     a.w_out = w_out;

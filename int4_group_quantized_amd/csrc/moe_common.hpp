@@ -41,7 +41,8 @@ struct MoeArgs {
     int32_t* wpairs;   // per work item: PF_ITEM slots of pair ids (the item's count used)
     float* wts;
     uint16_t *h, *hs;
-    float *o, *os;
+    uint16_t* o;       // fp16 down outputs of the routed (token, k) pairs [T K][hidden]
+    float* os;
     int32_t* idx_out;
     float* w_out;
 };

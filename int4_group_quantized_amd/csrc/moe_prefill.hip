@@ -65,7 +65,7 @@ struct PfGemm {
     int ostride;
     int ksplit;                    // dense: K split over this many blocks (partial outputs)
     long pstride;                  // elements between the partial outputs of two splits
-    uint16_t* hout;                // fp16 silu(out0) * out1, [pair][N]
+    uint16_t* hout;                // fp16 silu(out0) * out1, [pair][N]; or (F_O16) fp16 out0 [row][ostride]
     // one extra feature row N (dense, single matrix): read from (xp, xs, xb), written to
     // xout[split][t]
     const uint32_t* xp; const uint16_t* xs; const uint16_t* xb; float* xout;
@@ -74,6 +74,7 @@ struct PfGemm {
 // GEMM flavours
 constexpr int F_GROUPED = 1;   // work items of the expert sort (else token groups of all tokens)
 constexpr int F_HOUT = 2;      // fp16 silu(out0) * out1 (else fp32 outputs)
+constexpr int F_O16 = 8;       // fp16 outputs to hout, single matrix (the experts' down outputs)
 constexpr int F_EXTRA = 4;     // one extra feature row from a second matrix (single matrix)
 constexpr int PF_RES_RBG = 4;  // row blocks per block of the resident-activation GEMM
 
@@ -491,6 +492,8 @@ __device__ __forceinline__ void pf_gemm_body(const PfGemm& a, int rb, int ntok, 
                 const int orow = sm.orow[t];
                 if constexpr (HOUT) {
                     a.hout[(long)orow * a.N + n] = f2h(silu(acc[0][c][r]) * acc[NMAT - 1][c][r]);
+                } else if constexpr ((FL & F_O16) != 0) {
+                    a.hout[(long)orow * a.ostride + n] = f2h(acc[0][c][r]);
                 } else if (extra) {
                     a.xout[(long)split * a.T + orow] = acc[0][c][r];
                 } else {
@@ -532,7 +535,7 @@ k_pf_down(PfGemm g, PfGemm d, int nbg) {
     int rb, item;
     if ((int)blockIdx.x < nbg) {
         pf_block(blockIdx.x, g.nrb, rb, item);
-        pf_gemm_block<1, 4, NTG, F_GROUPED, NS, 1, NTS>(g, rb, item, sm);
+        pf_gemm_block<1, 4, NTG, F_GROUPED | F_O16, NS, 1, NTS>(g, rb, item, sm);
     } else {
         pf_block(blockIdx.x - nbg, d.nrb, rb, item);
         pf_gemm_block<1, 4, 2, 0, NS, 1, NTS>(d, rb, item, sm);
@@ -721,7 +724,12 @@ __device__ __forceinline__ void pf_res_block(const PfGemm& a, int rbg, int item,
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int t = c * 16 + 4 * j + r;
-                        if (c < ntiles && t < ntok) a.out0[(long)sm.orow[t] * a.ostride + n] = acc[c][r];
+                        if (c < ntiles && t < ntok) {
+                            if constexpr ((FL & F_O16) != 0)
+                                a.hout[(long)sm.orow[t] * a.ostride + n] = f2h(acc[c][r]);
+                            else
+                                a.out0[(long)sm.orow[t] * a.ostride + n] = acc[c][r];
+                        }
                     }
                 }
             }
@@ -742,7 +750,7 @@ k_pf_down_res(PfGemm g, PfGemm d, int nbg) {
     int rbg, item;
     if ((int)blockIdx.x < nbg) {
         pf_block(blockIdx.x, g.nrb, rbg, item);
-        pf_res_block<NT, NS, RBG, F_GROUPED>(g, rbg, item, sm);
+        pf_res_block<NT, NS, RBG, F_GROUPED | F_O16>(g, rbg, item, sm);
     } else {
         pf_block(blockIdx.x - nbg, d.nrb, rbg, item);
         pf_res_block<NT, NS, RBG, 0>(d, rbg, item, sm);
@@ -1275,8 +1283,9 @@ __global__ void __launch_bounds__(1024) k_pf_place(MoeArgs a, int max_items, int
     }
 }
 
-// y = fp16(sum_k w_k o_k + sigmoid(gate) (os + LoRA_down)) (+ residual), k in order.  FPT
-// outputs of one token per thread (8, or 4 with many tokens) with 16-byte loads.  Every load
+// y = fp16(sum_k w_k o_k + sigmoid(gate) (os + LoRA_down)) (+ residual), k in order, with the
+// experts' outputs o_k held in fp16.  FPT outputs of one token per thread (8, or 4 with many
+// tokens).  Every load
 // of the common case (up to KF experts, LoRA rank a multiple of 8 up to 16) is issued before
 // any use, one memory round trip: the experts' rows and weights, the shared output and gate
 // logit, the residual, the FPT LoRA-B rows (contiguous) and z_d.  Absent operands are read
@@ -1294,15 +1303,13 @@ __device__ __forceinline__ void pf_combine_body(const MoeArgs& a) {
     const int n = ch * 128 + (threadIdx.x % TPR) * FPT;
     const long i8 = (long)t * a.H + n;
     const int K = a.K;
-    float4 p[KF][NV];
+    XV p[KF];   // the experts' down outputs, fp16
     float w[KF];
 #pragma unroll
     for (int u = 0; u < KF; ++u) {
         const int k = min(u, K - 1);
         w[u] = a.wts[(long)t * K + k];
-        const float4* ok = reinterpret_cast<const float4*>(a.o + ((long)t * K + k) * a.H + n);
-#pragma unroll
-        for (int v = 0; v < NV; ++v) p[u][v] = ok[v];
+        p[u] = *reinterpret_cast<const XV*>(a.o + ((long)t * K + k) * a.H + n);
     }
     float4 osv[NV];
 #pragma unroll
@@ -1371,20 +1378,17 @@ __device__ __forceinline__ void pf_combine_body(const MoeArgs& a) {
 #pragma unroll
     for (int u = 0; u < KF; ++u) {
         if (u < K) {
-            const float* pv = reinterpret_cast<const float*>(p[u]);
+            const uint16_t* pv = reinterpret_cast<const uint16_t*>(&p[u]);
 #pragma unroll
-            for (int q = 0; q < FPT; ++q) acc[q] = fmaf(w[u], pv[q], acc[q]);
+            for (int q = 0; q < FPT; ++q) acc[q] = fmaf(w[u], h2f(pv[q]), acc[q]);
         }
     }
     for (int k = KF; k < K; ++k) {   // experts past the KF-th
         const float wk = a.wts[(long)t * K + k];
-        const float4* ok = reinterpret_cast<const float4*>(a.o + ((long)t * K + k) * a.H + n);
-        float4 qv[NV];
+        const XV qv = *reinterpret_cast<const XV*>(a.o + ((long)t * K + k) * a.H + n);
+        const uint16_t* pv = reinterpret_cast<const uint16_t*>(&qv);
 #pragma unroll
-        for (int v = 0; v < NV; ++v) qv[v] = ok[v];
-        const float* pv = reinterpret_cast<const float*>(qv);
-#pragma unroll
-        for (int q = 0; q < FPT; ++q) acc[q] = fmaf(wk, pv[q], acc[q]);
+        for (int q = 0; q < FPT; ++q) acc[q] = fmaf(wk, h2f(pv[q]), acc[q]);
     }
     const float gm = sigmoid(g);
     uint16_t out[FPT];
@@ -1520,7 +1524,7 @@ hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s) {
     }
     if (all || stage == QMOE_STAGE_DOWN) {
         PfGemm p = grouped(a, a.ed, nullptr, a.H, a.I, a.h, 1, items);
-        p.out0 = a.o;
+        p.hout = a.o;   // fp16 down outputs of the (token, k) pairs
         PfGemm q = gemm_args(a.shd, nullptr, a.H, a.SI, a.hs, a.H, (a.T + 31) / 32);   // 32-token groups
         q.T = a.T;
         q.out0 = a.os;
@@ -1555,9 +1559,9 @@ hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s) {
                 default: k_pf_down<16, 4><<<grid, 256, 0, s>>>(p, q, nbg); break;
             }
         } else {
-            if (isz == 16) pf_gemm<1, 4, 1, F_GROUPED>(p, s);
-            else if (isz == 32) pf_gemm<1, 4, 2, F_GROUPED>(p, s);
-            else pf_gemm<1, 4, 4, F_GROUPED>(p, s);
+            if (isz == 16) pf_gemm<1, 4, 1, F_GROUPED | F_O16>(p, s);
+            else if (isz == 32) pf_gemm<1, 4, 2, F_GROUPED | F_O16>(p, s);
+            else pf_gemm<1, 4, 4, F_GROUPED | F_O16>(p, s);
             pf_gemm<1, 4, 2, 0>(q, s);
         }
         // blocks of 16 (few tokens) or 8 (many) tokens x 128 features
