@@ -197,7 +197,8 @@ __device__ __forceinline__ bool pf_setup(const PfGemm& a, int item, PfSmem<NTS, 
 // activations are loaded D steps ahead: the weights into D register slots (the loop
 // unrolled by D), the activations into registers that are staged into the LDS double
 // buffer one step before their use.  The weight rows of one block share a base address (the
-// expert's matrix) held in scalar registers; a lane only keeps 32-bit offsets.
+// expert's matrix) held in scalar registers; a lane keeps 32-bit offsets, or in the fp16
+// path (registers to spare) its row pointers formed once.
 template <int NMAT, int BITS, int NTE, int FL, int NS, int SM_NMAT, int NTS>
 __device__ __forceinline__ void pf_gemm_body(const PfGemm& a, int rb, int ntok, int e, int split,
                                              PfSmem<NTS, SM_NMAT, NS>& sm) {
@@ -957,8 +958,9 @@ constexpr int TOK_NPC = 4;  // h outputs per thread whose loads are issued toget
 // Per-token finish of the x side, one block of 4 waves per token.  Wave 0 sums the token's
 // router-logit partials in registers and runs top-K.  Waves 1-3 sum the shared-gate logit and
 // (each for itself, into its own LDS row) the LoRA z's of gate and up, then h_s =
-// silu(g_s + LoRA_g) * (u_s + LoRA_u), every load of TOK_NPC outputs issued together; h_s goes to
-// LDS.  Every wave meanwhile fetches its first rows of the down LoRA's A.  After the one barrier:
+// silu(g_s + LoRA_g) * (u_s + LoRA_u), every load of NPC outputs issued together; h_s goes to
+// LDS.  With NPC > 1 every wave meanwhile fetches its first rows of the down LoRA's A.  After
+// the one barrier:
 // h_s and the selection are written out and z_d = A_down h_s is taken, one wave per four rank
 // rows.  Split-K partials are added in split order, LoRA chunks in chunk order.
 template <int KP, int NPC>

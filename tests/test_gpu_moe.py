@@ -210,6 +210,24 @@ def test_prefill_512_tokens(q, prefill_layer, skew):
         assert np.mean(idx < 16) > 0.5
 
 
+@pytest.mark.parametrize("T", [2048, 8192])
+def test_prefill_sweep_sizes_sampled(q, prefill_layer, T):
+    """The prefill sweep's token counts at the full layer shape (hidden 2048, 256 experts,
+    top-4, shared expert, LoRA): at 2048 tokens the x side runs unsplit and 32-pair items,
+    at 8192 tokens 64-pair items (four-tile fp16-weight GEMMs, the resident down with four
+    tiles), the two-pass sort and the many-token per-token and combine kernels.  The layer
+    is per token, so the oracle checks a seeded sample of the device's rows (first and last
+    tokens included)."""
+    S = Shape(top_k=4)
+    x = synth.activations(T, S.hidden, synth.Workload.MOE_PREFILL, 0, 10 + T)
+    y, idx, w = run_device(q, prefill_layer, S, x)
+    rng = np.random.default_rng(T + 1)
+    rows = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 150, replace=False)]))
+    err, rel, n_alt = check_layer(prefill_layer, x[rows], None, y[rows], idx[rows], w[rows])
+    print(f"prefill sweep T={T}: max abs {err:.2e} rel L2 {rel:.2e} alternatives {n_alt} "
+          f"({len(rows)} rows)", flush=True)
+
+
 def test_multi_tenant_stack_teacher_forced(q):
     """Three stacked layers of the multi-tenant workload (16 tokens, top-8, 4 adapter sets,
     adapter = token // 4), each compared with the oracle on the oracle's own input."""
