@@ -908,17 +908,6 @@ __device__ void token_topk(const MoeArgs& a, int t, int ksplit, int* sel, float*
     keys.select(a.E, a.K, sel, sw);
 }
 
-template <int KP>
-__device__ void token_topk_any(const MoeArgs& a, int t, int ksplit, int* sel, float* sw) {
-    switch (topk_per_lane(a.E)) {
-        case 1: token_topk<1, KP>(a, t, ksplit, sel, sw); break;
-        case 2: token_topk<2, KP>(a, t, ksplit, sel, sw); break;
-        case 4: token_topk<4, KP>(a, t, ksplit, sel, sw); break;
-        case 8: token_topk<8, KP>(a, t, ksplit, sel, sw); break;
-        default: token_topk<16, KP>(a, t, ksplit, sel, sw); break;
-    }
-}
-
 // LoRA-B term of one output row from 16 rank entries held as two uint4 (entries r < rank
 // count), z from LDS.
 __device__ __forceinline__ float bdot16(const uint4 (&v)[2], const float* z, int rank) {
@@ -963,7 +952,7 @@ constexpr int TOK_NPC = 4;  // h outputs per thread whose loads are issued toget
 // the one barrier:
 // h_s and the selection are written out and z_d = A_down h_s is taken, one wave per four rank
 // rows.  Split-K partials are added in split order, LoRA chunks in chunk order.
-template <int KP, int NPC>
+template <int KP, int PER, int NPC>
 __device__ __forceinline__ void pf_token_body(const MoeArgs& a, int ksplit) {
     extern __shared__ __align__(16) uint16_t hl[];        // h_s of the token, fp16 [SI]
     __shared__ int sel[MAX_K];
@@ -990,7 +979,7 @@ __device__ __forceinline__ void pf_token_body(const MoeArgs& a, int ksplit) {
     }
 
     if (wave == 0) {
-        token_topk_any<KP>(a, t, ksplit, sel, sw);
+        token_topk<PER, KP>(a, t, ksplit, sel, sw);
     } else {
         const int w = wave - 1, u = threadIdx.x - 64;
         Parts<KP> g;   // the shared-gate logit (every lane loads, one stores)
@@ -1103,15 +1092,31 @@ __device__ __forceinline__ void pf_token_body(const MoeArgs& a, int ksplit) {
     }
 }
 
-// Few tokens: every block in flight at once, each issuing all its loads together.
-template <int KP>
-__global__ void __launch_bounds__(256) k_pf_token(MoeArgs a, int ksplit) { pf_token_body<KP, TOK_NPC>(a, ksplit); }
+// Few tokens: every block in flight at once, each issuing all its loads together.  PER:
+// logits per lane of the top-K (4 up to 256 experts, else 16), fixed per kernel so that one
+// kernel holds one selection.
+template <int KP, int PER>
+__global__ void __launch_bounds__(256) k_pf_token(MoeArgs a, int ksplit) { pf_token_body<KP, PER, TOK_NPC>(a, ksplit); }
 
 // Many tokens (several rounds of blocks): one h output per thread in flight, so that four waves
 // fit a SIMD and twice the tokens are in flight.
-template <int KP>
+template <int KP, int PER>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
-k_pf_token_many(MoeArgs a, int ksplit) { pf_token_body<KP, 1>(a, ksplit); }
+k_pf_token_many(MoeArgs a, int ksplit) { pf_token_body<KP, PER, 1>(a, ksplit); }
+
+// The per-token kernel for T tokens: KP split-K partials, PER logits per lane.
+template <int PER>
+void launch_token(const MoeArgs& a, int ksplit, int kp, size_t tsm, hipStream_t s) {
+    if (a.T < PF_MANY_T) {
+        if (kp <= 2) k_pf_token<2, PER><<<a.T, 256, tsm, s>>>(a, ksplit);
+        else if (kp <= 4) k_pf_token<4, PER><<<a.T, 256, tsm, s>>>(a, ksplit);
+        else k_pf_token<8, PER><<<a.T, 256, tsm, s>>>(a, ksplit);
+    } else {   // (eight partials do not fit the four-wave budget: the few-token kernel)
+        if (kp <= 2) k_pf_token_many<2, PER><<<a.T, 256, tsm, s>>>(a, ksplit);
+        else if (kp <= 4) k_pf_token_many<4, PER><<<a.T, 256, tsm, s>>>(a, ksplit);
+        else k_pf_token<8, PER><<<a.T, 256, tsm, s>>>(a, ksplit);
+    }
+}
 
 // Inclusive prefix sum over the wave.
 __device__ __forceinline__ int wave_scan(int v) {
@@ -1499,15 +1504,8 @@ hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s) {
         // KP covers the split-K partials (<= hidden / 512) and half the LoRA z chunks
         // (hidden / 256), whatever the split
         const int kp = std::max(ksplit, a.H / 512);
-        if (a.T < PF_MANY_T) {
-            if (kp <= 2) k_pf_token<2><<<a.T, 256, tsm, s>>>(a, ksplit);
-            else if (kp <= 4) k_pf_token<4><<<a.T, 256, tsm, s>>>(a, ksplit);
-            else k_pf_token<8><<<a.T, 256, tsm, s>>>(a, ksplit);
-        } else {   // (eight partials do not fit the four-wave budget: the few-token kernel)
-            if (kp <= 2) k_pf_token_many<2><<<a.T, 256, tsm, s>>>(a, ksplit);
-            else if (kp <= 4) k_pf_token_many<4><<<a.T, 256, tsm, s>>>(a, ksplit);
-            else k_pf_token<8><<<a.T, 256, tsm, s>>>(a, ksplit);
-        }
+        if (a.E <= 256) launch_token<4>(a, ksplit, kp, tsm, s);
+        else launch_token<16>(a, ksplit, kp, tsm, s);
         const int TK = a.T * a.K;
         if (TK <= 2048) {
             k_pf_sort<<<1, 1024, 0, s>>>(a, items, isz);

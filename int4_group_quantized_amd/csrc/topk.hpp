@@ -1,11 +1,11 @@
 // Top-K of one token's logits inside one wave, without LDS round trips.
 //
 // Routing family SOFTMAX_TOPK with K experts per token ("Edge0 project review" MoE spec;
-// "Recover-LoRA ..." section 1).  The K largest of (logit + bias) are chosen in K rounds of
-// a wave-wide maximum over 64-bit keys (order-preserving float bits above the inverted
-// expert index, so an exact tie goes to the lower index); the reduction runs on DPP lane
-// moves within 16-lane rows and scalar readlanes across rows.  The weights are the softmax
-// over the K chosen logits (the full softmax renormalized over the selection).
+// "Recover-LoRA ..." section 1).  The K largest of (logit + bias) are chosen in K rounds: a
+// wave-wide maximum of the order-preserving float bits (DPP max within 16-lane rows, scalar
+// readlanes across rows), then the lowest expert index holding that value (a ballot over
+// the lanes), so an exact tie goes to the lower index.  The weights are the softmax over
+// the K chosen logits (the full softmax renormalized over the selection).
 #pragma once
 
 #include "device.hpp"
@@ -19,15 +19,6 @@ __device__ __forceinline__ uint32_t order_bits(float v) {
 __device__ __forceinline__ float from_order_bits(uint32_t k) {
     return __builtin_bit_cast(float, (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
-__device__ __forceinline__ bool key_gt(uint32_t ah, uint32_t al, uint32_t bh, uint32_t bl) {
-    return ah > bh || (ah == bh && al > bl);
-}
-template <int CTRL>
-__device__ __forceinline__ void key_max_dpp(uint32_t& h, uint32_t& l) {
-    const uint32_t oh = dpp_u<CTRL>(h), ol = dpp_u<CTRL>(l);
-    if (key_gt(oh, ol, h, l)) { h = oh; l = ol; }
-}
-
 // The token's logits held by this lane: entries lane*PER .. lane*PER + PER - 1 of the row;
 // entries >= e are not candidates.  VEC: the row is 16-byte aligned and padded to a
 // multiple of 64 floats, so every lane reads its PER entries with vector loads; otherwise
@@ -58,57 +49,76 @@ struct TopkKeys {
 #pragma unroll
         for (int i = 0; i < PER; ++i) braw[i] = has_bias ? bias[min(lane * PER + i, e - 1)] : 0.0f;
     }
-    __device__ __forceinline__ void keys(int e, uint32_t& live, uint32_t (&kh)[PER]) const {
-        const int lane = threadIdx.x & 63;
-        live = 0;
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            live |= (lane * PER + i < e ? 1u : 0u) << i;
-            kh[i] = order_bits(has_bias ? raw[i] + braw[i] : raw[i]);
-        }
-    }
-    // One round: the largest live key of the wave (ties to the lower index); removes it.
-    __device__ __forceinline__ int round(uint32_t& live, const uint32_t (&kh)[PER], float& val) const {
-        const int lane = threadIdx.x & 63;
-        uint32_t h = 0, l = 0;   // key = (order bits, 0xFFFFFFFF - index); 0 = empty
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const uint32_t li = 0xFFFFFFFFu - (uint32_t)(lane * PER + i);
-            if (((live >> i) & 1u) && key_gt(kh[i], li, h, l)) { h = kh[i]; l = li; }
-        }
-        key_max_dpp<DPP_XOR1>(h, l);
-        key_max_dpp<DPP_XOR2>(h, l);
-        key_max_dpp<DPP_HALF_MIRROR>(h, l);
-        key_max_dpp<DPP_MIRROR>(h, l);
-        uint32_t bh = 0, bl = 0;
-#pragma unroll
-        for (int row = 0; row < 4; ++row) {
-            const uint32_t rh = (uint32_t)__builtin_amdgcn_readlane((int)h, 16 * row);
-            const uint32_t rl = (uint32_t)__builtin_amdgcn_readlane((int)l, 16 * row);
-            if (key_gt(rh, rl, bh, bl)) { bh = rh; bl = rl; }
-        }
-        const int idx = (int)(0xFFFFFFFFu - bl);
-        if (idx / PER == lane) live &= ~(1u << (idx % PER));
-        val = from_order_bits(bh);
-        return idx;
-    }
-    // The whole wave must call this.  Lane 0 writes sel[r] (expert of rank r) and w[r] (its
-    // renormalized softmax weight), r < k.
+    // The whole wave must call this.  Lane 0 .. k - 1 write sel[r] (expert of rank r) and w[r]
+    // (its renormalized softmax weight), r < k.
+    //
+    // Each lane first sorts its entries by key, descending; an adjacent-swap sort that swaps
+    // only on a strictly larger key keeps equal keys in index order.  A round then takes the
+    // wave maximum of the lanes' head keys (DPP max within 16-lane rows, the four rows through
+    // readlanes) and the lowest lane whose head holds it (ballot): that lane's head is its lowest
+    // index with that key, and lane l holds indices l*PER .. l*PER + PER - 1, so the round picks
+    // the lowest index of the largest key.  The winner drops its head.  Lane r keeps round r's
+    // expert and key, and the k weights are taken in parallel at the end.
     __device__ void select(int e, int k, int* sel, float* w) const {
         const int lane = threadIdx.x & 63;
-        uint32_t live, kh[PER];
-        keys(e, live, kh);
-        float first = 0.0f;
-        for (int r = 0; r < k; ++r) {
-            float val;
-            const int idx = round(live, kh, val);
-            if (r == 0) first = val;
-            if (lane == 0) { sel[r] = idx; w[r] = expf(val - first); }
+        uint32_t kv[PER];   // keys (order-preserving float bits; 0: no entry)
+        int ki[PER];        // their indices
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const bool ok = lane * PER + i < e;
+            kv[i] = ok ? order_bits(has_bias ? raw[i] + braw[i] : raw[i]) : 0u;
+            ki[i] = lane * PER + i;
         }
-        if (lane == 0) {
-            float sum = 0.0f;
-            for (int r = 0; r < k; ++r) sum += w[r];
-            for (int r = 0; r < k; ++r) w[r] = w[r] / sum;
+#pragma unroll
+        for (int pass = 0; pass < PER - 1; ++pass)
+#pragma unroll
+            for (int i = 0; i + 1 < PER - pass; ++i) {
+                const bool sw = kv[i + 1] > kv[i];
+                const uint32_t ka = kv[i], kb = kv[i + 1];
+                const int ia = ki[i], ib = ki[i + 1];
+                kv[i] = sw ? kb : ka; kv[i + 1] = sw ? ka : kb;
+                ki[i] = sw ? ib : ia; ki[i + 1] = sw ? ia : ib;
+            }
+        int my_idx = 0;
+        uint32_t my_key = 0u;
+        for (int r = 0; r < k; ++r) {
+            uint32_t m = kv[0];
+            m = max(m, dpp_u<DPP_XOR1>(m));
+            m = max(m, dpp_u<DPP_XOR2>(m));
+            m = max(m, dpp_u<DPP_HALF_MIRROR>(m));
+            m = max(m, dpp_u<DPP_MIRROR>(m));
+            const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)m, 0);
+            const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)m, 16);
+            const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)m, 32);
+            const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)m, 48);
+            const uint32_t best = max(max(r0, r1), max(r2, r3));
+            const int lw = __builtin_ctzll(__ballot(kv[0] == best));   // the lowest lane holding it
+            const int idx = __builtin_amdgcn_readlane(ki[0], lw);
+            const bool win = lane == lw;
+#pragma unroll
+            for (int i = 0; i + 1 < PER; ++i) {
+                kv[i] = win ? kv[i + 1] : kv[i];
+                ki[i] = win ? ki[i + 1] : ki[i];
+            }
+            kv[PER - 1] = win ? 0u : kv[PER - 1];
+            if (lane == r) { my_idx = idx; my_key = best; }
+        }
+        // softmax over the k chosen keys, relative to the largest (round 0's, held by lane 0)
+        const float first = from_order_bits((uint32_t)__builtin_amdgcn_readlane((int)my_key, 0));
+        const float ex = lane < k ? expf(from_order_bits(my_key) - first) : 0.0f;
+        float sum = ex;
+        sum += dpp<DPP_XOR1>(sum);
+        sum += dpp<DPP_XOR2>(sum);
+        sum += dpp<DPP_HALF_MIRROR>(sum);
+        sum += dpp<DPP_MIRROR>(sum);
+        const float s0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sum), 0));
+        const float s1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sum), 16));
+        const float s2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sum), 32));
+        const float s3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sum), 48));
+        const float total = (s0 + s1) + (s2 + s3);
+        if (lane < k) {
+            sel[lane] = my_idx;
+            w[lane] = ex / total;
         }
     }
 };
