@@ -104,7 +104,7 @@ __global__ void __launch_bounds__(256) k_dec_xside(MoeArgs a) {
 
 // ------------------------------------------------------------------------------ D2 gate/up
 
-constexpr int GU_RPW = 2;  // gate/up row pairs per wave
+constexpr int GU_RPW = 1;  // gate/up row pairs per wave
 
 template <int PER>
 __global__ void __launch_bounds__(256) k_dec_gate_up(MoeArgs a) {
