@@ -181,6 +181,20 @@ struct RowRegs {
             if (valid && sl + i * lpr < chunks) n = i + 1;
         }
     }
+    // Pins the first use of every loaded register here (see hold()): called after a later
+    // round trip is issued, it keeps the compiler from converting the weights (and so waiting
+    // for them) ahead of it, e.g. by hoisting the conversions out of a loop.
+    __device__ __forceinline__ void hold() {
+#pragma unroll
+        for (int i = 0; i < MAXC; ++i) {
+#pragma unroll
+            for (int j = 0; j < WPC; ++j) asm volatile("" : "+v"(w[i][j]));
+            uint32_t sb = (uint32_t)s[i] | ((uint32_t)b[i] << 16);
+            asm volatile("" : "+v"(sb));
+            s[i] = (uint16_t)sb;
+            b[i] = (uint16_t)(sb >> 16);
+        }
+    }
     // acc[t] += chunk dots for tokens t < mt staged in xs/xsum
     __device__ __forceinline__ void dot(int K, int lpr, int sl, const f16x2* xs, const float* xsum,
                                         int mt, float (&acc)[GEMV_MT]) const {

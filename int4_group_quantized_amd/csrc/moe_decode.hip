@@ -32,66 +32,31 @@ constexpr int MT = GEMV_MT;
 
 // ------------------------------------------------------------------------------ D1 x-side
 
-__global__ void __launch_bounds__(256) k_dec_xside(MoeArgs a) {
-    __shared__ __align__(16) f16x2 xs[8192];   // 32 KB: 8192 / (hidden / 2) tokens per pass
-    __shared__ float xsum[MT * 128];
-    QMOE_SGPR_USE4(a.router.p, a.router.s, a.router.b, a.x);
-    QMOE_SGPR_USE4(a.shg.p, a.shg.s, a.shg.b, a.logits);
-    QMOE_SGPR_USE4(a.shu.p, a.shu.s, a.shu.b, a.gs);
-    QMOE_SGPR_USE4(a.us, a.T, a.H, a.E);
-    QMOE_SGPR_USE4(a.SI, a.Ep, a.Ag, a.Au);
-    QMOE_SGPR_USE4(a.rg, a.ru, a.gate, a.sgate.p);
-    QMOE_SGPR_USE4(a.sgate.s, a.sgate.b, a.zg, a.zu);
+// One x-side block's rows of a BITS-bit matrix: each lane segment owns row n of w (weights
+// loaded before x is staged, so the two memory round trips overlap), then the dot over the
+// staged tokens.  One body per width: loaded registers never meet at a branch merge, where the
+// compiler would copy them and so wait for every load in flight.
+template <int BITS>
+__device__ __forceinline__ void xside_rows(const MoeArgs& a, const QW& w, int n, bool ok, float* out,
+                                           int ostride, f16x2* xs, float* xsum, int xs_halves2) {
     const int H = a.H;
-    const int zjobs = (a.Ag ? a.T * a.rg : 0) + (a.Au ? a.T * a.ru : 0);
-    const XsideGrid g = xside_grid(a.T, H, a.E, a.SI, zjobs);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int lpr = lanes_per_row(H), rpw = 64 / lpr, seg = lane / lpr, sl = lane % lpr;
-    const int b = blockIdx.x;
-
-    if (b >= g.nb_router + g.nb_gate + g.nb_shared) {
-        xside_lora_z(a, (b - g.nb_router - g.nb_gate - g.nb_shared) * 4 + wave, zjobs);
-        return;
-    }
-    // the row this lane segment owns (block-uniform role), loaded before x is staged
-    const bool eight = b < g.nb_router + g.nb_gate;
-    int r = 0, nrows = 1;
-    const QW* w;
-    float* out;
-    int ostride;
-    if (b < g.nb_router) {
-        r = (b * 4 + wave) * rpw + seg; nrows = a.E; w = &a.router; out = a.logits; ostride = a.Ep;
-    } else if (b < g.nb_router + g.nb_gate) {
-        r = wave * rpw + seg; nrows = 1; w = &a.sgate; out = a.gate; ostride = 1;
-    } else {
-        r = ((b - g.nb_router - g.nb_gate) * 4 + wave) * rpw + seg;
-        nrows = 2 * a.SI;
-        w = r < a.SI ? &a.shg : &a.shu;
-        out = r < a.SI ? a.gs : a.us;
-        ostride = a.SI;
-    }
-    const bool ok = r < nrows;
-    const int rr_ = ok ? r : 0;
-    const int n = (b >= g.nb_router + g.nb_gate && rr_ >= a.SI) ? rr_ - a.SI : rr_;
-    RowRegs<8, 2> r8;
-    RowRegs<4, 2> r4;
-    r8.n = r4.n = 0;
-    if (eight) r8.load(w->p, w->s, w->b, H, n, lpr, sl, ok);
-    else r4.load(w->p, w->s, w->b, H, n, lpr, sl, ok);
-    const int mt_max = min(MT, (int)(sizeof(xs) / (H * 2)));
+    const int lane = threadIdx.x & 63;
+    const int lpr = lanes_per_row(H), sl = lane % lpr;
+    RowRegs<BITS, 2> rw;
+    rw.load(w.p, w.s, w.b, H, n, lpr, sl, ok);
+    const int mt_max = min(MT, xs_halves2 / (H / 2));
     for (int t0 = 0; t0 < a.T; t0 += mt_max) {
         const int mt = min(mt_max, a.T - t0);
         if (t0 > 0) __syncthreads();
         const uint4* xb = reinterpret_cast<const uint4*>(a.x + (long)t0 * H);
         auto rowp = [=](int i) { return xb + (long)i * (H / 8); };
-        if (eight) stage_rows<8, 8>(rowp, mt, H, xs, xsum);
-        else stage_rows<4, 8>(rowp, mt, H, xs, xsum);
+        stage_rows<BITS, 8>(rowp, mt, H, xs, xsum);
         __syncthreads();
+        rw.hold();   // the weights are first used here, after x is staged
         float acc[MT];
 #pragma unroll
         for (int t = 0; t < MT; ++t) acc[t] = 0.0f;
-        if (eight) r8.dot(H, lpr, sl, xs, xsum, mt, acc);
-        else r4.dot(H, lpr, sl, xs, xsum, mt, acc);
+        rw.dot(H, lpr, sl, xs, xsum, mt, acc);
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
             if (t < mt) {
@@ -99,6 +64,43 @@ __global__ void __launch_bounds__(256) k_dec_xside(MoeArgs a) {
                 if (sl == 0 && ok) out[(long)(t0 + t) * ostride + n] = v;
             }
         }
+    }
+}
+
+__global__ void __launch_bounds__(256) k_dec_xside(MoeArgs a) {
+    __shared__ __align__(16) f16x2 xs[8192];   // 32 KB: 8192 / (hidden / 2) tokens per pass
+    __shared__ float xsum[MT * 128];
+    // every argument field of the kernel in one batch of scalar loads (one round trip)
+    asm volatile("" ::"s"(a.router.p), "s"(a.router.s), "s"(a.router.b), "s"(a.x), "s"(a.shg.p),
+                 "s"(a.shg.s), "s"(a.shg.b), "s"(a.logits), "s"(a.shu.p), "s"(a.shu.s), "s"(a.shu.b),
+                 "s"(a.gs), "s"(a.us), "s"(a.T), "s"(a.H), "s"(a.E), "s"(a.SI), "s"(a.Ep), "s"(a.Ag),
+                 "s"(a.Au), "s"(a.rg), "s"(a.ru), "s"(a.gate), "s"(a.sgate.p), "s"(a.sgate.s),
+                 "s"(a.sgate.b), "s"(a.zg), "s"(a.zu));
+    const int H = a.H;
+    const int zjobs = (a.Ag ? a.T * a.rg : 0) + (a.Au ? a.T * a.ru : 0);
+    const XsideGrid g = xside_grid(a.T, H, a.E, a.SI, zjobs);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lpr = lanes_per_row(H), rpw = 64 / lpr, seg = lane / lpr;
+    const int b = blockIdx.x;
+
+    if (b >= g.nb_router + g.nb_gate + g.nb_shared) {
+        xside_lora_z(a, (b - g.nb_router - g.nb_gate - g.nb_shared) * 4 + wave, zjobs);
+        return;
+    }
+    // the row this lane segment owns (block-uniform role); the matrix chosen by value (a
+    // pointer into the argument struct would read its fields through dependent vector loads)
+    if (b < g.nb_router + g.nb_gate) {
+        const bool router = b < g.nb_router;
+        const int r = router ? (b * 4 + wave) * rpw + seg : wave * rpw + seg;
+        const bool ok = r < (router ? a.E : 1);
+        xside_rows<8>(a, router ? a.router : a.sgate, ok ? r : 0, ok, router ? a.logits : a.gate,
+                      router ? a.Ep : 1, xs, xsum, 8192);
+    } else {
+        const int r = ((b - g.nb_router - g.nb_gate) * 4 + wave) * rpw + seg;
+        const bool ok = r < 2 * a.SI;
+        const int rr = ok ? r : 0;
+        const bool up = rr >= a.SI;
+        xside_rows<4>(a, up ? a.shu : a.shg, up ? rr - a.SI : rr, ok, up ? a.us : a.gs, a.SI, xs, xsum, 8192);
     }
 }
 
@@ -207,6 +209,9 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
     // rows and the LoRA A_down slices in flight together.  Each lane loads the expert of its
     // own first-pass items first (per-lane loads: a per-lane pick from a uniform array would
     // become an indexed scratch access whose wait drains every load in flight).
+    // the token's adapter first: the addresses of the LoRA rows wait for it, and loads
+    // complete in issue order, so a load issued later would make that wait longer
+    const int ad = adapter_of(a.adapter, t, a.nad);
     const int n_items = (K + 1) * DN_ROWS;
     const int slots = 4 * rpw;            // lane segments in the block
     const int slot = wave * rpw + seg;
@@ -229,7 +234,6 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
     const int lane16 = threadIdx.x & 15, zrow = threadIdx.x >> 4;
     const int zper = Kd / 16;
     const bool zfast = a.Ad && a.rd <= 16 && zper <= 8 * ZI;
-    const int ad = adapter_of(a.adapter, t, a.nad);   // after the loads above are issued
     // the combine's own inputs (gate logit, residual x, LoRA-B rows of this block's outputs)
     // are loaded now, not after the dots: one round trip less at the end
     constexpr int BQ = 2;   // prefetched B rows up to rank 16; larger ranks read B at the end
@@ -241,17 +245,19 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
         const int nn = min(n0 + (int)(threadIdx.x % DN_ROWS), H - 1);
         gate_t = a.gate[t];
         x_res = a.x[(long)t * H + nn];
-        if (bfast) {
-            const uint4* brow = reinterpret_cast<const uint4*>(a.Bd + ((long)ad * H + nn) * a.rd);
+        // loaded unconditionally (stand-in: the token's x row): under a branch the compiler
+        // copies the loaded registers at the merge, and a copy waits for every load in flight
+        const uint4* brow = bfast ? reinterpret_cast<const uint4*>(a.Bd + ((long)ad * H + nn) * a.rd)
+                                  : reinterpret_cast<const uint4*>(a.x + (long)t * H);
 #pragma unroll
-            for (int i = 0; i < BQ; ++i) bq[i] = brow[min(i, a.rd / 8 - 1)];
-        }
+        for (int i = 0; i < BQ; ++i) bq[i] = brow[bfast ? min(i, a.rd / 8 - 1) : 0];
     }
     uint4 av[ZI];
-    if (zfast) {
-        const uint16_t* arow = a.Ad + ((long)ad * a.rd + min(zrow, a.rd - 1)) * Kd + lane16 * zper;
+    {   // unconditional as well (stand-in: the token's x row)
+        const uint16_t* arow = zfast ? a.Ad + ((long)ad * a.rd + min(zrow, a.rd - 1)) * Kd + lane16 * zper
+                                     : a.x + (long)t * H;
 #pragma unroll
-        for (int i = 0; i < ZI; ++i) av[i] = *reinterpret_cast<const uint4*>(arow + min(i * 8, zper - 8));
+        for (int i = 0; i < ZI; ++i) av[i] = *reinterpret_cast<const uint4*>(arow + (zfast ? min(i * 8, zper - 8) : 0));
     }
     // phase 2: the K + 1 down rows' loads (they need only the routing)
     RowRegs<4, 1> rr[DN_ITEMS];
