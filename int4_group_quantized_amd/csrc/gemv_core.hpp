@@ -15,6 +15,8 @@ namespace qmoe {
 
 constexpr int GEMV_MT = 8;  // most tokens per pass over a weight row
 
+constexpr int NT = 256;   // threads per block of every kernel that stages rows
+
 // Stage `mt` token rows of an fp16 source into LDS: `xs` gets the inputs as pairs in the
 // order the unpacking produces (K/2 pairs per token), `xsum` the per-chunk (32-input)
 // sums in fp32.  Token i of the batch is source row `rows[i]`.  All threads of the block
@@ -23,13 +25,13 @@ template <int BITS>
 __device__ __forceinline__ void stage_tokens(const uint16_t* __restrict__ src, const int* rows,
                                              int mt, int K, f16x2* xs, float* xsum) {
     const int units = K / 8;
-    for (int u = threadIdx.x; u < mt * units; u += blockDim.x) {
+    for (int u = threadIdx.x; u < mt * units; u += NT) {
         const int t = u / units, c = u % units;
         const uint4 raw = *reinterpret_cast<const uint4*>(src + (long)rows[t] * K + c * 8);
         reinterpret_cast<uint4*>(xs + (long)t * (K / 2))[c] = BITS == 4 ? pair_perm8_w(raw) : pair_perm4x2_w(raw);
     }
     const int chunks = K / 32;
-    for (int u = threadIdx.x; u < mt * chunks; u += blockDim.x) {
+    for (int u = threadIdx.x; u < mt * chunks; u += NT) {
         const int t = u / chunks, c = u % chunks;
         const uint4* p = reinterpret_cast<const uint4*>(src + (long)rows[t] * K + c * 32);
         float s = 0.0f;
@@ -40,7 +42,6 @@ __device__ __forceinline__ void stage_tokens(const uint16_t* __restrict__ src, c
 }
 
 
-constexpr int NT = 256;   // threads per block of every kernel that stages rows
 
 // Write one staged 8-input unit to LDS (pair order of the unpacking) and, from the quad
 // of lanes that holds a 32-input chunk, its fp32 sum.  All lanes must call (DPP).

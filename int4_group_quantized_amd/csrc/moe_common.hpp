@@ -106,7 +106,7 @@ __device__ __forceinline__ float lora_b_dot(const uint16_t* __restrict__ B, int 
 // of the block are in flight together.  Writes z (LDS); the caller synchronises.
 __device__ inline void lora_rows16(const uint16_t* __restrict__ A, int rank,
                                    const uint16_t* __restrict__ v, int K, float* z) {
-    const int lane16 = threadIdx.x & 15, row0 = threadIdx.x >> 4, nrows = blockDim.x >> 4;
+    const int lane16 = threadIdx.x & 15, row0 = threadIdx.x >> 4, nrows = NT >> 4;
     const int per = K / 16;                 // inputs per lane (a multiple of 8)
     constexpr int MAXI = 16;                // K <= 2048
     for (int r = row0; r < rank; r += nrows) {

@@ -126,7 +126,7 @@ __global__ void __launch_bounds__(256) k_dec_gate_up(MoeArgs a) {
 
     if (pair == TK) {  // shared expert: LoRA up-projections, silu(g) * u
         const int n0 = blockIdx.x * rows_per_block;
-        for (int it = threadIdx.x; it < rows_per_block * a.T; it += blockDim.x) {
+        for (int it = threadIdx.x; it < rows_per_block * a.T; it += NT) {
             const int n = n0 + it % rows_per_block, t = it / rows_per_block;
             if (n >= a.SI) continue;
             float gv = a.gs[(long)t * a.SI + n];
