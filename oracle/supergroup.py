@@ -124,3 +124,35 @@ def gemm(x: np.ndarray, W: SuperGroupWeight) -> np.ndarray:
     q = codes_of(W).astype(np.float64)
     acc = np.asarray(x, dtype=np.float64) @ q.T          # the integer-code dot product
     return acc * W.scales.astype(np.float64)[None, :]   # scale applied once per channel
+
+
+# ---- weight-activation integer path ---------------------------------------------------------
+#
+# Same section of the same page: in ``Y = sum (s_W s_X) Q(W)^T Q(X)`` the activations are
+# quantized too, so that the sum over the inputs is a pure integer dot product and the scale
+# product (s_W s_X) is applied once per output; the page's weight-activation results quantize
+# activations to 8 bits (its table of 1.58-8-8 / 1.88-8-8 runs).  Readings where the page is
+# silent: one activation scale per token (row of X), symmetric, with the page's 4-bit formula
+# at n = 8: ``s_X = max(max|x| / (2^(8-1) - 1), eps)`` stored as fp16, ``Q(x) = clip(rint(x /
+# s_X), -127, 127)`` taken in float32 against the stored scale, ties to even; the integer
+# dot is exact; the scale product and the final scaling are done in full precision here (the
+# fp16 factors are exact in float64) and the result is rounded to fp16 once.
+
+ACT_QMAX = np.float32(127)    # 2^(8-1) - 1
+
+
+def quantize_activations(x: np.ndarray):
+    """x fp16 [B, K] -> (codes int8 [B, K], scales fp16 [B]), one symmetric scale per token."""
+    x = np.asarray(x, dtype=np.float16).astype(np.float32)
+    amax = np.max(np.abs(x), axis=1)
+    s16 = np.maximum(amax / ACT_QMAX, EPS).astype(np.float16)
+    q = np.clip(np.rint(x / s16.astype(np.float32)[:, None]), -ACT_QMAX, ACT_QMAX)
+    return q.astype(np.int8), s16
+
+
+def gemm_a8(x: np.ndarray, W: SuperGroupWeight) -> np.ndarray:
+    """``y[b, n] = s_W[n] s_X[b] sum_k Q(W)[n, k] Q(X)[b, k]`` in float64 (before fp16
+    rounding); the sum over k in exact integer arithmetic."""
+    qx, sx = quantize_activations(x)
+    acc = qx.astype(np.int64) @ codes_of(W).astype(np.int64).T
+    return acc.astype(np.float64) * sx.astype(np.float64)[:, None] * W.scales.astype(np.float64)[None, :]

@@ -100,3 +100,102 @@ def test_gemm_integer_case_exact():
     x = np.random.default_rng(3).integers(-4, 5, size=(3, 64)).astype(np.float16)
     ref = x.astype(np.int64) @ codes.astype(np.int64).T
     assert np.array_equal(sg.gemm(x, Wq), ref.astype(np.float64))
+
+
+# ---- weight-activation integer path (8-bit activations) -------------------------------------
+
+def test_act8_on_grid_rows_are_exact():
+    """Rows that are already on an 8-bit grid (x = k * 2^-5, max |k| = 127): the scale is
+    max|x| / 127 = 2^-5 exactly and the codes are the integers k; the integer path then gives
+    exactly the weight-only GEMM (its dequantized activations are x itself)."""
+    g = np.random.default_rng(21)
+    k = g.integers(-127, 128, size=(4, 128))
+    k[:, 7] = [127, -127, 127, -127]
+    x = (k * 2.0 ** -5).astype(np.float16)
+    qx, sx = sg.quantize_activations(x)
+    assert np.all(sx == np.float16(2.0 ** -5))
+    assert np.array_equal(qx.astype(np.int64), k)
+    w = synth.normal_f32((16, 128), 0.02, W, 3, synth.Role.SUPERGROUP)
+    Wq, _ = sg.quantize(w, 4)
+    assert np.array_equal(sg.gemm_a8(x, Wq), sg.gemm(x, Wq))
+
+
+def test_act8_hand_example():
+    """Worked by hand from the page's quantizer at n = 8.  fp16(2.54) = 2.5390625 is the
+    row's largest magnitude; 2.5390625 / 127 = 0.0199926...; fp16 values in [2^-6, 2^-5) are
+    spaced 2^-16, and 0.0199926 / 2^-16 = 1310.2, so s = 1310 * 2^-16 = 0.019989013671875.
+    Codes: 2.5390625 / s = 127.02 -> 127; 1.0 / s = 50.03 -> 50; fp16(-0.03) =
+    -1966 * 2^-16 = -0.029998779296875, / s = -1.5007 -> -2; fp16(0.01) = 1311 * 2^-17 =
+    0.01000213623046875, / s = 0.5004 -> 1; zeros -> 0."""
+    x = np.zeros((1, 16), np.float16)
+    x[0, :4] = [2.54, 1.0, -0.03, 0.01]
+    assert [float(v) for v in x[0, :4]] == [2.5390625, 1.0, -0.029998779296875, 0.01000213623046875]
+    qx, sx = sg.quantize_activations(x)
+    assert float(sx[0]) == 0.019989013671875
+    assert qx[0, :4].tolist() == [127, 50, -2, 1] and np.all(qx[0, 4:] == 0)
+
+
+def test_act8_codes_nearest_level_and_bounds():
+    """Every code is the nearest level to x / s among -127..127 (ties aside), the largest
+    magnitude of a row maps to +-127, and an all-zero row gets the epsilon scale and zero
+    codes."""
+    x = synth.activations(6, 256, W, 4)
+    x[5] = 0
+    qx, sx = sg.quantize_activations(x)
+    assert float(sx[5]) == float(np.float16(1e-5)) and np.all(qx[5] == 0)
+    for b in range(5):
+        S = Fraction(float(sx[b]))
+        i_max = int(np.argmax(np.abs(x[b].astype(np.float32))))
+        assert abs(int(qx[b, i_max])) == 127
+        for i in range(256):
+            r = Fraction(float(x[b, i])) / S
+            best = min(127, max(-127, round(r)))
+            if int(qx[b, i]) != best:
+                frac = abs(r) - int(abs(r))
+                assert abs(float(frac) - 0.5) < 1e-5 or abs(r) > 127
+
+
+def test_gemm_a8_equals_dequantized_matmul():
+    """The factorized form s_W s_X * (integer dot) equals the float64 matmul of the two
+    dequantized operands (s_X[b] Q(X)[b, :]) . (s_W[n] Q(W)[n, :]): a transposed operand or a
+    scale applied on the wrong axis fails here."""
+    w = synth.normal_f32((32, 256), 0.02, W, 5, synth.Role.SUPERGROUP)
+    Wq, codes = sg.quantize(w, 4)
+    x = synth.activations(7, 256, W, 6)
+    qx, sx = sg.quantize_activations(x)
+    xd = qx.astype(np.float64) * sx.astype(np.float64)[:, None]
+    wd = codes.astype(np.float64) * Wq.scales.astype(np.float64)[:, None]
+    np.testing.assert_allclose(sg.gemm_a8(x, Wq), xd @ wd.T, rtol=1e-12, atol=1e-15)
+
+
+def test_gemm_a8_integer_dot_brute_force():
+    """The integer dot on a tiny case by explicit loops over the unpacked fields (Python
+    integers), scales set to 1."""
+    w = synth.normal_f32((8, 32), 0.02, W, 7, synth.Role.SUPERGROUP)
+    Wq, _ = sg.quantize(w, 4)
+    Wq.scales[:] = np.float16(1.0)
+    x = synth.activations(2, 32, W, 8)
+    qx, sx = sg.quantize_activations(x)
+    c4 = sg.unpack_fields(Wq.p4, 4)
+    c2 = sg.unpack_fields(Wq.p2, 2)
+    y = sg.gemm_a8(x, Wq)
+    for b in range(2):
+        for n in range(8):
+            row = c4[n // 4].astype(int) - 8 if n % 4 == 0 else c2[(n // 4) * 3 + n % 4 - 1].astype(int) - 1
+            dot = sum(int(row[k]) * int(qx[b, k]) for k in range(32))
+            assert y[b, n] == dot * float(sx[b])
+
+
+def test_gemm_a8_within_the_activation_rounding_bound():
+    """Against the weight-only GEMM on the same weights, the integer path differs only by the
+    activation rounding: |y_a8 - y| <= sum_k |s_W q_W[n, k]| * s_X[b] / 2 (no clipping occurs:
+    the largest |x| maps to 127 within rounding)."""
+    w = synth.normal_f32((24, 512), 0.02, W, 9, synth.Role.SUPERGROUP)
+    Wq, codes = sg.quantize(w, 4)
+    x = synth.activations(5, 512, W, 10)
+    qx, sx = sg.quantize_activations(x)
+    bound = (np.abs(codes.astype(np.float64)) * Wq.scales.astype(np.float64)[:, None]).sum(1)[None, :] \
+        * (sx.astype(np.float64)[:, None] / 2) * (1 + 1e-3)
+    diff = np.abs(sg.gemm_a8(x, Wq) - sg.gemm(x, Wq))
+    assert np.all(diff <= bound)
+    assert diff.max() > 0
