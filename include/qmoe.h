@@ -25,7 +25,8 @@
  *  [R5] "EDGERAZOR deep dive" (zhichai.net), section 2.1 SQMP: super-group allocation
  *       (one 4-bit channel in every floor(1/rho) consecutive output channels, the rest
  *       ternary), the ternary and 4-bit symmetric quantizers, and the factorisation of the
- *       matmul into a scale product times an integer dot product.
+ *       matmul into a scale product times an integer dot product; section 3.1, the
+ *       weight-activation results with 8-bit activations.
  *
  * Conventions for every entry point
  *  - Array pointers are DEVICE pointers unless stated otherwise; `stream` is a
@@ -263,6 +264,28 @@ int qmoe_quantize_supergroup(const float* w, int32_t rows, int32_t cols, int32_t
 int qlinear_supergroup(const uint16_t* x, int32_t b, const uint32_t* p4, const uint32_t* p2,
                        const uint16_t* scales, int32_t rows, int32_t cols, int32_t period,
                        uint16_t* y, void* stream);
+
+/*
+ * 8-bit activation quantization of the weight-activation integer path ([R5] 2.1, the
+ * matmul as (s_W s_X) Q(W)^T Q(X); [R5] 3.1 runs activations at 8 bits): per token b,
+ * s_X[b] = fp16(max(max_k |x[b][k]| / 127, 1e-5)) and qx[b][k] = clip(rint(x[b][k] /
+ * s_X[b]), -127, 127), the division in fp32 against the stored fp16 scale, ties to even.
+ * x fp16 [b x cols] (16-byte aligned), qx int8 [b x cols] (16-byte aligned), sx fp16 [b];
+ * cols % 512 == 0, cols <= 65536, 1 <= b <= 65536.  Deterministic.
+ */
+int qmoe_quantize_act8(const uint16_t* x, int32_t b, int32_t cols, int8_t* qx, uint16_t* sx,
+                       void* stream);
+
+/*
+ * Super-group GEMM on the weight-activation integer path ([R5] 2.1): the activations are
+ * quantized as by qmoe_quantize_act8 inside the call, the sum over the inputs is an exact
+ * integer dot product of the weight codes and the activation codes, and the scale product
+ * is applied once: y[b][n] = fp16((sum_k q_W[n][k] q_X[b][k]) * s_X[b] * s_W[n]) (the two
+ * multiplications in fp32).  Same weight layout and limits as qlinear_supergroup.
+ */
+int qlinear_supergroup_a8(const uint16_t* x, int32_t b, const uint32_t* p4, const uint32_t* p2,
+                          const uint16_t* scales, int32_t rows, int32_t cols, int32_t period,
+                          uint16_t* y, void* stream);
 
 #ifdef __cplusplus
 }

@@ -23,6 +23,8 @@ from .api import (  # noqa: F401
     moe_workspace_bytes,
     qlinear_int4,
     qlinear_supergroup,
+    qlinear_supergroup_a8,
+    quantize_act8,
     quantize_affine,
     quantize_supergroup,
     router_topk,

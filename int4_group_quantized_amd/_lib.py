@@ -70,6 +70,8 @@ _SIGS = {
                                                 _P, _P, ctypes.c_size_t, _P]),
     "qmoe_quantize_supergroup": (ctypes.c_int, [_P, _I, _I, _I, _P, _P, _P, _P]),
     "qlinear_supergroup": (ctypes.c_int, [_P, _I, _P, _P, _P, _I, _I, _I, _P, _P]),
+    "qmoe_quantize_act8": (ctypes.c_int, [_P, _I, _I, _P, _P, _P]),
+    "qlinear_supergroup_a8": (ctypes.c_int, [_P, _I, _P, _P, _P, _I, _I, _I, _P, _P]),
 }
 EXPORTED = tuple(_SIGS)
 

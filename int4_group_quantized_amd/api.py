@@ -300,3 +300,28 @@ def qlinear_supergroup(x: torch.Tensor, W: SuperGroupWeight,
                                  W.rows, W.cols, W.period, y.data_ptr(), _stream(x)),
           "qlinear_supergroup")
     return y
+
+
+def quantize_act8(x: torch.Tensor):
+    """8-bit per-token activation codes and scales: (qx int8 [b, cols], sx fp16 [b])."""
+    _dev(x, torch.float16, "x")
+    b, cols = x.shape
+    qx = torch.empty((b, cols), dtype=torch.int8, device=x.device)
+    sx = torch.empty(b, dtype=torch.float16, device=x.device)
+    check(lib.qmoe_quantize_act8(x.data_ptr(), b, cols, qx.data_ptr(), sx.data_ptr(), _stream(x)),
+          "qmoe_quantize_act8")
+    return qx, sx
+
+
+def qlinear_supergroup_a8(x: torch.Tensor, W: SuperGroupWeight,
+                          out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The super-group GEMM with 8-bit activations and an integer dot product."""
+    _dev(x, torch.float16, "x")
+    b = x.shape[0]
+    y = out if out is not None else torch.empty((b, W.rows), dtype=torch.float16, device=x.device)
+    _dev(y, torch.float16, "out")
+    check(lib.qlinear_supergroup_a8(x.data_ptr(), b, W.p4.data_ptr(),
+                                    W.p2.data_ptr() if W.p2.numel() else None, W.scales.data_ptr(),
+                                    W.rows, W.cols, W.period, y.data_ptr(), _stream(x)),
+          "qlinear_supergroup_a8")
+    return y

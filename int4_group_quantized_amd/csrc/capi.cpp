@@ -221,4 +221,25 @@ int qlinear_supergroup(const uint16_t* x, int32_t b, const uint32_t* p4, const u
                                                       as_stream(stream)));
 }
 
+int qmoe_quantize_act8(const uint16_t* x, int32_t b, int32_t cols, int8_t* qx, uint16_t* sx,
+                       void* stream) {
+    if (!x || !qx || !sx || b <= 0 || cols <= 0) return QMOE_ERR_INVALID_ARG;
+    if (b > 65536 || cols % 512 || cols > 65536) return QMOE_ERR_UNSUPPORTED;
+    if (!aligned16(x) || !aligned16(qx)) return QMOE_ERR_MISALIGNED;
+    return hip_status(qmoe::launch_quantize_act8(x, b, cols, qx, sx, as_stream(stream)));
+}
+
+int qlinear_supergroup_a8(const uint16_t* x, int32_t b, const uint32_t* p4, const uint32_t* p2,
+                          const uint16_t* scales, int32_t rows, int32_t cols, int32_t period,
+                          uint16_t* y, void* stream) {
+    if (!x || !p4 || !scales || !y || b <= 0 || rows <= 0 || cols <= 0 || period <= 0)
+        return QMOE_ERR_INVALID_ARG;
+    if (b > 4096 || period > 64 || rows % period || cols % 512 || cols > 8192) return QMOE_ERR_UNSUPPORTED;
+    if (period > 1 && !p2) return QMOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(y) || !aligned16(p4) || (p2 && !aligned16(p2)))
+        return QMOE_ERR_MISALIGNED;
+    return hip_status(qmoe::launch_qlinear_supergroup_a8(x, b, p4, p2, scales, rows, cols, period,
+                                                         y, as_stream(stream)));
+}
+
 }  // extern "C"

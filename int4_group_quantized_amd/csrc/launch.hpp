@@ -46,4 +46,11 @@ hipError_t launch_qlinear_supergroup(const uint16_t* x, int b, const uint32_t* p
                                      const uint32_t* p2, const uint16_t* scales, int rows,
                                      int cols, int period, uint16_t* y, hipStream_t s);
 
+// supergroup_a8.hip
+hipError_t launch_quantize_act8(const uint16_t* x, int b, int cols, int8_t* qx, uint16_t* sx,
+                                hipStream_t s);
+hipError_t launch_qlinear_supergroup_a8(const uint16_t* x, int b, const uint32_t* p4,
+                                        const uint32_t* p2, const uint16_t* scales, int rows,
+                                        int cols, int period, uint16_t* y, hipStream_t s);
+
 }  // namespace qmoe

@@ -244,3 +244,78 @@ def test_supergroup_gemm_shapes(q, period, rows, cols, b):
     W_ = q.SuperGroupWeight(dev(ref.p4.view(np.int32)), p2, dev(ref.scales), period, rows, cols)
     y = host(q.qlinear_supergroup(dev(x), W_))
     assert_close(y, supergroup.gemm(x, ref), what="supergroup")
+
+
+# ------------------------------------------------------------------------------ super-group, 8-bit activations
+
+def _sg_weight(q, ref, period, rows, cols):
+    p2 = dev(ref.p2.view(np.int32)) if ref.p2.size else torch.empty(0, dtype=torch.int32, device=DEV)
+    return q.SuperGroupWeight(dev(ref.p4.view(np.int32)), p2, dev(ref.scales), period, rows, cols)
+
+
+def _check_a8(y, ref64):
+    """Within one fp16 step of the oracle (the kernel scales in fp32, the oracle in float64:
+    they round to different fp16 values only next to a rounding boundary), and equal almost
+    everywhere."""
+    r16 = ref64.astype(np.float16)
+    assert ulp_distance(y, r16) <= 1
+    assert np.mean(y.view(np.uint16) != r16.view(np.uint16)) < 1e-3
+
+
+@pytest.mark.parametrize("b,cols", [(1, 1024), (5, 512), (64, 1024), (100, 2048), (3, 8192)])
+def test_act8_codes_bit_exact(q, b, cols):
+    """The integer decisions of the activation quantizer: codes and fp16 scales equal the
+    oracle's bit for bit (same fp32 division, ties to even), including an all-zero row (the
+    epsilon scale), a row already on an 8-bit grid and a row with one large outlier."""
+    x = synth.activations(b, cols, synth.Workload.SUPERGROUP, 1, b)
+    x[0, :] = 0
+    if b > 2:
+        x[1, :] = (np.arange(cols) % 255 - 127) * np.float16(2.0 ** -5)
+        x[2, 7] = np.float16(300.0)
+    qx, sx = q.quantize_act8(dev(x))
+    ref_q, ref_s = supergroup.quantize_activations(x)
+    assert np.array_equal(host(sx).view(np.uint16), ref_s.view(np.uint16))
+    assert np.array_equal(host(qx), ref_q)
+
+
+@pytest.mark.parametrize("b", [1, 3, 8, 9, 16, 64, 100])
+def test_supergroup_a8_gemm(q, b):
+    """The integer path at the benchmark shape (3072 x 1024, rho = 1/4): dot4 form (b <= 8)
+    and int8 MFMA form (b > 8; ragged 16-token tiles at 9 and 100)."""
+    rows, cols = 3072, 1024
+    w = synth.normal_f32((rows, cols), 0.02, synth.Workload.SUPERGROUP, 0, synth.Role.SUPERGROUP)
+    ref, _ = supergroup.quantize(w, 4)
+    x = synth.activations(b, cols, synth.Workload.SUPERGROUP, 2, b)
+    y = host(q.qlinear_supergroup_a8(dev(x), _sg_weight(q, ref, 4, rows, cols)))
+    _check_a8(y, supergroup.gemm_a8(x, ref))
+
+
+@pytest.mark.parametrize("period,rows,cols,b", [(1, 128, 2048, 20), (2, 200, 1024, 33), (3, 96, 3072, 17),
+                                                (4, 64, 512, 40), (4, 64, 8192, 2), (4, 192, 4096, 24)])
+def test_supergroup_a8_gemm_shapes(q, period, rows, cols, b):
+    """Other periods (all 4-bit at 1), row counts that are not a multiple of 64, K of two,
+    three and four 1024-input chunks, K = 512 (dot4 form in a batched call) and K = 8192 with
+    two tokens per pass of the dot4 form."""
+    w = synth.normal_f32((rows, cols), 0.02, synth.Workload.TEST, 22, synth.Role.SUPERGROUP, period)
+    ref, _ = supergroup.quantize(w, period)
+    x = synth.activations(b, cols, synth.Workload.TEST, 22, period)
+    y = host(q.qlinear_supergroup_a8(dev(x), _sg_weight(q, ref, period, rows, cols)))
+    _check_a8(y, supergroup.gemm_a8(x, ref))
+
+
+def test_supergroup_a8_integer_case_exact(q):
+    """Activations already on the grid (scale 2^-5: one entry 127 per row, the rest small)
+    and unit weight scales: every output is an integer v times 2^-5 with |v| <= 2048, exact
+    in fp16, so the result is exact."""
+    rows, cols, b = 64, 1024, 12
+    w = synth.normal_f32((rows, cols), 0.02, synth.Workload.TEST, 23, synth.Role.SUPERGROUP)
+    ref, codes = supergroup.quantize(w, 4)
+    ref.scales[:] = np.float16(1.0)
+    k = np.random.default_rng(5).integers(-2, 3, size=(b, cols))
+    k[:, 0] = 127
+    x = (k * 2.0 ** -5).astype(np.float16)
+    y = host(q.qlinear_supergroup_a8(dev(x), _sg_weight(q, ref, 4, rows, cols)))
+    v = k.astype(np.int64) @ codes.astype(np.int64).T
+    assert np.all(np.abs(v) <= 2048)
+    exact = v * 2.0 ** -5
+    assert np.array_equal(y.astype(np.float64), exact)
