@@ -136,9 +136,9 @@ def test_act8_hand_example():
 
 
 def test_act8_codes_nearest_level_and_bounds():
-    """Every code is the nearest level to x / s among -127..127 (ties aside), the largest
-    magnitude of a row maps to +-127, and an all-zero row gets the epsilon scale and zero
-    codes."""
+    """Every code is the integer nearest to the exact quotient x / s (Fraction arithmetic,
+    ties to even), clipped to -127..127; the largest magnitude of a row maps to +-127; an
+    all-zero row gets the epsilon scale and zero codes."""
     x = synth.activations(6, 256, W, 4)
     x[5] = 0
     qx, sx = sg.quantize_activations(x)
@@ -149,10 +149,20 @@ def test_act8_codes_nearest_level_and_bounds():
         assert abs(int(qx[b, i_max])) == 127
         for i in range(256):
             r = Fraction(float(x[b, i])) / S
-            best = min(127, max(-127, round(r)))
-            if int(qx[b, i]) != best:
-                frac = abs(r) - int(abs(r))
-                assert abs(float(frac) - 0.5) < 1e-5 or abs(r) > 127
+            assert int(qx[b, i]) == min(127, max(-127, round(r)))     # round(): ties to even
+
+
+def test_act8_exact_ties_go_to_even():
+    """Planted exact ties: with s = 2^-5 (each row holds 127 * 2^-5), x = (c + 1/2) 2^-5 is
+    exactly halfway and must give the even neighbour: 0.5 -> 0, 1.5 -> 2, 2.5 -> 2, -0.5 -> 0,
+    -1.5 -> -2, 126.5 -> 126, -126.5 -> -126; and 127.4 * 2^-5 (not a tie) -> 127."""
+    halves = [0.5, 1.5, 2.5, -0.5, -1.5, 126.5, -126.5]
+    x = np.zeros((1, 16), np.float16)
+    x[0, 0] = 127 * 2.0 ** -5
+    x[0, 1:1 + len(halves)] = [h * 2.0 ** -5 for h in halves]
+    qx, sx = sg.quantize_activations(x)
+    assert float(sx[0]) == 2.0 ** -5
+    assert qx[0, 1:1 + len(halves)].tolist() == [0, 2, 2, 0, -2, 126, -126]
 
 
 def test_gemm_a8_equals_dequantized_matmul():
