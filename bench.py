@@ -14,7 +14,8 @@ inputs are resident before timing; the timed region is one HIP graph of exactly 
 Other workloads (--workload): gemv (one int4 linear, x [1 x 2048], W [512 x 2048]),
 moe_prefill (512 tokens, top-4; --skew adds +2.0 to the logits of experts 0..15),
 moe_stack (40 stacked layers, 16 tokens per step, top-8, 4 LoRA adapter sets),
-supergroup (mixed ternary/4-bit GEMM, W [3072 x 1024], --batch 1 or 64).
+supergroup (mixed ternary/4-bit GEMM, W [3072 x 1024], --batch 1 or 64), supergroup_a8
+(the same GEMM with 8-bit activations and an integer dot product).
 
 Prints one JSON line: the metric, a roofline object for the dominant kernel (algorithmic
 bytes per launch over its average launch time, measured here with HIP events on the stream
@@ -36,6 +37,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 FP16_MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 MFMA
+INT8_MFMA_PEAK_TOPS = 5000.0    # dense int8 MFMA (TOP/s)
 
 H, I, SI, E, LAYERS, RANK, ALPHA = 2048, 512, 512, 256, 40, 16, 32.0
 MAT_BYTES_4BIT = lambda rows, cols: rows * cols // 2 + 2 * (rows * (cols // 64) * 2)
@@ -441,9 +443,10 @@ def sg_bytes(rows, cols, period=4):
     return n4 * cols // 2 + (rows - n4) * cols // 4 + rows * 2
 
 
-def cpu_baseline_supergroup(batch, budget_s=15.0):
+def cpu_baseline_supergroup(batch, budget_s=15.0, a8=False):
     """The oracle on a bounded sample: the super-group GEMM of one seeded 3072 x 1024 weight
-    against `batch` inputs, repeated until the budget is spent."""
+    against `batch` inputs (weight-only, or with 8-bit activations), repeated until the budget
+    is spent."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     import synth
     from oracle import supergroup
@@ -455,19 +458,23 @@ def cpu_baseline_supergroup(batch, budget_s=15.0):
     x = synth.activations(batch, 1024, synth.Workload.SUPERGROUP, 0)
     t0 = time.perf_counter()
     n = 0
+    gemm = supergroup.gemm_a8 if a8 else supergroup.gemm
     while True:
-        supergroup.gemm(x, W)
+        gemm(x, W)
         n += 1
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
     blas = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
     return {"value": n * batch / dt, "unit": "tokens/s", "cores": int(max(blas) if blas else 1),
-            "kind": "oracle", "sample": f"{n} GEMMs of W[3072x1024] with {batch} inputs, {dt:.1f} s"}
+            "kind": "oracle", "sample": f"{n} {'8-bit activation ' if a8 else ''}GEMMs of W[3072x1024] "
+                                        f"with {batch} inputs, float64/int64 numpy, {dt:.1f} s"}
 
 
-def bench_supergroup(args, q, torch):
-    """Mixed ternary/4-bit super-group GEMM, W [3072 x 1024], B inputs per call."""
+def bench_supergroup(args, q, torch, a8=False):
+    """Mixed ternary/4-bit super-group GEMM, W [3072 x 1024], B inputs per call (with a8: the
+    weight-activation integer path, activations quantized to 8 bits inside the call)."""
+    gemm = q.qlinear_supergroup_a8 if a8 else q.qlinear_supergroup
     B, N, Kc = args.batch, 3072, 1024
     COPIES = 1024 if B == 1 else 64          # B = 1: 1 GB of weights rotated, 4x the cache
     gen = torch.Generator(device="cuda")
@@ -484,7 +491,7 @@ def bench_supergroup(args, q, torch):
     def run(lo, hi):
         def f():
             for i in range(lo, hi):
-                q.qlinear_supergroup(xs[i % 16], mats[i % COPIES], out=ys[i % 16])
+                gemm(xs[i % 16], mats[i % COPIES], out=ys[i % 16])
         return f
     if W:
         graph_of(torch, run(K, K + W)).replay()
@@ -495,19 +502,23 @@ def bench_supergroup(args, q, torch):
     bytes_ = wbytes + B * Kc * 2 + B * N * 2
     flops = 2 * B * N * Kc
     ach = bytes_ / (us * 1e-6) / 1e9
-    res = {"metric": f"super-group GEMM tokens/s (B={B})", "value": B * K / (ms * 1e-3),
+    mfma_peak = INT8_MFMA_PEAK_TOPS if a8 else FP16_MFMA_PEAK_TFLOPS
+    name = "k_sg_a8" if a8 else "k_sg"
+    res = {"metric": f"super-group GEMM{' (8-bit activations)' if a8 else ''} tokens/s (B={B})",
+           "value": B * K / (ms * 1e-3),
            "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": ms / K,
-           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
-           "data": "synthetic",
-           "config": {"workload": f"qlinear_supergroup W[3072x1024] (1 in 4 channels 4-bit, 3 ternary), "
-                                  f"x[{B}x1024], {COPIES} weight copies rotated", "global_batch": B,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "i8/i32" if a8 else "f16", "data": "synthetic",
+           "config": {"workload": f"{'qlinear_supergroup_a8' if a8 else 'qlinear_supergroup'} W[3072x1024] "
+                                  f"(1 in 4 channels 4-bit, 3 ternary), x[{B}x1024], {COPIES} weight "
+                                  f"copies rotated", "global_batch": B,
                       "tflops": flops / (us * 1e-6) / 1e12},
-           "roofline": {"kernel": "k_sg_gemv" if B <= 8 else "k_sg_mfma", "bound": "hbm",
+           "roofline": {"kernel": f"{name}_gemv" if B <= 8 else f"{name}_mfma", "bound": "hbm",
                         "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": ach / HBM_PEAK_GBS, "traffic": None, "bytes_per_launch": bytes_,
                         "us_per_launch": us, "mfma_tflops": flops / (us * 1e-6) / 1e12,
-                        "mfma_frac": flops / (us * 1e-6) / 1e12 / FP16_MFMA_PEAK_TFLOPS}}
-    return res, (lambda: cpu_baseline_supergroup(B))
+                        "mfma_frac": flops / (us * 1e-6) / 1e12 / mfma_peak}}
+    return res, (lambda: cpu_baseline_supergroup(B, a8=a8))
 
 
 def bench_gemv(args, q, torch):
@@ -549,7 +560,9 @@ def bench_gemv(args, q, torch):
 
 
 WORKLOADS = {"moe_decode": bench_moe_decode, "moe_prefill": bench_moe_prefill,
-             "moe_stack": bench_moe_stack, "supergroup": bench_supergroup, "gemv": bench_gemv}
+             "moe_stack": bench_moe_stack, "supergroup": bench_supergroup,
+             "supergroup_a8": lambda args, q, torch: bench_supergroup(args, q, torch, a8=True),
+             "gemv": bench_gemv}
 
 
 def main():

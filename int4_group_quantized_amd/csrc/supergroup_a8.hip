@@ -6,8 +6,9 @@
 // the product of the two scales is applied once per output; section 3.1 (table of the
 // weight-activation results) runs activations at 8 bits.  Activations: one symmetric scale
 // per token, s_X = fp16(max(max|x| / 127, 1e-5)), Q(x) = clip(rint(x / s_X), -127, 127) in
-// fp32 against the stored scale.  Weights: the super-group format of supergroup.hip (4-bit
-// channel rows, nibble q + 8; ternary rows, 2-bit field q + 1).
+// fp32 against the stored scale (as the weight quantizers take their codes).  Weights: the
+// super-group format of supergroup.hip (4-bit channel rows, nibble q + 8; ternary rows, 2-bit
+// field q + 1).
 //
 // Codes stay unsigned in the byte lanes of the integer dot (c = q + off, off = 8 or 1) and
 // the offset is taken out once per output: sum_k q x = sum_k c x - off * sum_k x, all in
@@ -32,6 +33,7 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 constexpr int A8_MT = 8;          // tokens per pass of the few-token kernel
 constexpr int A8_CHUNK = 1024;    // inputs staged per pass of the MFMA kernel
 constexpr int A8_PITCH = A8_CHUNK + 16;   // LDS row pitch in bytes (16-byte reads spread over the banks)
+constexpr int A8_WAVES = 4;       // waves per block of the MFMA kernel (16 channels each)
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -50,8 +52,10 @@ __device__ __forceinline__ float act8_scale(float amax) {
     return h2f(f2h(fmaxf(amax / 127.0f, 1e-5f)));
 }
 
+// Q(x): the correctly rounded fp32 quotient x / s rounded to the nearest integer (ties to
+// even), clipped to +-127.
 __device__ __forceinline__ int act8_code(float x, float s) {
-    return (int)fminf(fmaxf(rintf(x / s), -127.0f), 127.0f);
+    return min(max((int)rintf(x / s), -127), 127);
 }
 
 // The largest |x| of a row of K fp16 inputs, by one wave (K a multiple of 512).
@@ -213,6 +217,21 @@ __global__ void __launch_bounds__(256) k_sg_a8_gemv(const uint16_t* __restrict__
 
 // ---- batched: int8 MFMA --------------------------------------------------------------------
 
+// The largest |x| of 16 inputs held as two 16-byte loads.
+__device__ __forceinline__ float amax16(const uint4& r0, const uint4& r1) {
+    const uint32_t w[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fmaxf(fabsf(half_lo(w[i])), fabsf(half_hi(w[i]))));
+    return m;
+}
+
+// A block: 16 * A8_WAVES channels of one kind x 16 tokens, 16 channels per wave.  Wave w
+// stages tokens w, w + A8_WAVES, ... (a 1024-input chunk of a row is one 16-input unit per
+// lane), so each wave holds whole rows: a row's scale is a wave maximum over values already
+// in registers (one pass over the inputs when they fit one chunk) and its code sum a wave
+// sum.  Every block codes its 16 tokens itself (wider blocks, which would repeat that work
+// less often, stream more weight bytes through each CU and measured slower).
 template <bool FOUR>
 __device__ __forceinline__ void sg_a8_mfma_block(const uint16_t* __restrict__ x, int nb, int K,
                                                  int rows, int period,
@@ -222,14 +241,34 @@ __device__ __forceinline__ void sg_a8_mfma_block(const uint16_t* __restrict__ x,
                                                  int8_t* xl, float* sx, int* ssum) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane & 15, j = lane >> 4;
-    const int kr = rb * 64 + wave * 16 + col;                  // this lane's row of its kind
+    const int kr = rb * (16 * A8_WAVES) + wave * 16 + col;     // this lane's row of its kind
     const int krc = min(kr, kind_rows - 1);
     const int t0 = blockIdx.y * 16;
     const int nt = min(16, nb - t0);
-    // the 16 tokens' scales (wave w: tokens w, w + 4, ...; rows past nt repeat the last)
-    for (int t = wave; t < 16; t += 4) {
-        const float s = act8_scale(row_amax(x + (long)(t0 + min(t, nt - 1)) * K, K));
-        if (lane == 0) { sx[t] = s; ssum[t] = 0; }
+    constexpr int PASSES = 16 / A8_WAVES;                      // token rows per wave
+    const uint16_t* xr[PASSES];                                // rows past nt repeat the last
+#pragma unroll
+    for (int i = 0; i < PASSES; ++i) xr[i] = x + (long)(t0 + min(A8_WAVES * i + wave, nt - 1)) * K + lane * 16;
+    float srow[PASSES];
+    int qsum[PASSES];
+#pragma unroll
+    for (int i = 0; i < PASSES; ++i) qsum[i] = 0;
+    if (K > A8_CHUNK) {   // the rows' scales first, one pass over every chunk
+        float m[PASSES];
+#pragma unroll
+        for (int i = 0; i < PASSES; ++i) m[i] = 0.0f;
+        for (int k0 = 0; k0 < K; k0 += A8_CHUNK) {
+            uint4 v[PASSES][2];
+#pragma unroll
+            for (int i = 0; i < PASSES; ++i) {
+                v[i][0] = reinterpret_cast<const uint4*>(xr[i] + k0)[0];
+                v[i][1] = reinterpret_cast<const uint4*>(xr[i] + k0)[1];
+            }
+#pragma unroll
+            for (int i = 0; i < PASSES; ++i) m[i] = fmaxf(m[i], amax16(v[i][0], v[i][1]));
+        }
+#pragma unroll
+        for (int i = 0; i < PASSES; ++i) srow[i] = act8_scale(wave_max(m[i]));
     }
     // words of one row per 128 inputs: 16 (4-bit) or 8 (2-bit); per lane group 4 or 2
     constexpr int WPS = FOUR ? 16 : 8, LW = WPS / 4;
@@ -248,26 +287,23 @@ __device__ __forceinline__ void sg_a8_mfma_block(const uint16_t* __restrict__ x,
                 w[s][0] = v.x; w[s][1] = v.y;
             }
         }
-        // the 16 tokens' inputs k0 .. k0 + 1023: loads first, then codes to LDS
-        constexpr int PASSES = 16 * (A8_CHUNK / 16) / 256;
+        // this wave's rows, inputs k0 .. k0 + 1023 (one 16-input unit per lane)
         uint4 raw[PASSES][2];
 #pragma unroll
         for (int i = 0; i < PASSES; ++i) {
-            const int u = i * 256 + threadIdx.x;
-            const int r = u / (A8_CHUNK / 16), c = u % (A8_CHUNK / 16);
-            const uint4* src = reinterpret_cast<const uint4*>(x + (long)(t0 + min(r, nt - 1)) * K + k0 + c * 16);
-            raw[i][0] = src[0];
-            raw[i][1] = src[1];
+            raw[i][0] = reinterpret_cast<const uint4*>(xr[i] + k0)[0];
+            raw[i][1] = reinterpret_cast<const uint4*>(xr[i] + k0)[1];
         }
-        __syncthreads();   // the scales are written; the previous chunk's MFMAs are done
+        if (K == A8_CHUNK) {
+#pragma unroll
+            for (int i = 0; i < PASSES; ++i) srow[i] = act8_scale(wave_max(amax16(raw[i][0], raw[i][1])));
+        }
+        __syncthreads();   // the previous chunk's MFMAs are done with xl
 #pragma unroll
         for (int i = 0; i < PASSES; ++i) {
-            const int u = i * 256 + threadIdx.x;
-            const int r = u / (A8_CHUNK / 16), c = u % (A8_CHUNK / 16);
             int q[16];
-            const int sum = codes16(raw[i][0], raw[i][1], sx[r], q);
-            *reinterpret_cast<uint4*>(xl + r * A8_PITCH + c * 16) = FOUR ? order4(q) : order2(q);
-            if (r < nt) atomicAdd(&ssum[r], sum);
+            qsum[i] += codes16(raw[i][0], raw[i][1], srow[i], q);
+            *reinterpret_cast<uint4*>(xl + (A8_WAVES * i + wave) * A8_PITCH + lane * 16) = FOUR ? order4(q) : order2(q);
         }
         __syncthreads();
 #pragma unroll
@@ -291,6 +327,13 @@ __device__ __forceinline__ void sg_a8_mfma_block(const uint16_t* __restrict__ x,
             }
         }
     }
+    // the rows' scales and code sums to LDS for the epilogue's lanes
+#pragma unroll
+    for (int i = 0; i < PASSES; ++i) {
+        const int tot = wave_sum_i(qsum[i]);
+        if (lane == 0) { sx[A8_WAVES * i + wave] = srow[i]; ssum[A8_WAVES * i + wave] = tot; }
+    }
+    __syncthreads();
     if (kr >= kind_rows) return;
     const int n = FOUR ? kr * period : (kr / (period - 1)) * period + 1 + kr % (period - 1);
     const int off = FOUR ? 8 : 1;
@@ -303,7 +346,7 @@ __device__ __forceinline__ void sg_a8_mfma_block(const uint16_t* __restrict__ x,
 }
 
 // Both channel kinds in one launch: blocks 0 .. nb4 - 1 take 4-bit rows, the rest ternary.
-__global__ void __launch_bounds__(256) k_sg_a8_mfma(const uint16_t* __restrict__ x, int nb, int K,
+__global__ void __launch_bounds__(64 * A8_WAVES) k_sg_a8_mfma(const uint16_t* __restrict__ x, int nb, int K,
                                                     int rows, int period,
                                                     const uint32_t* __restrict__ p4,
                                                     const uint32_t* __restrict__ p2,
@@ -332,9 +375,10 @@ hipError_t launch_qlinear_supergroup_a8(const uint16_t* x, int b, const uint32_t
                                         int cols, int period, uint16_t* y, hipStream_t s) {
     if (b > A8_MT && cols % A8_CHUNK == 0) {   // batched: MFMA
         const int n4 = rows / period, n2 = rows - n4;
-        const int nb4 = (n4 + 63) / 64, nb2 = (n2 + 63) / 64;
+        constexpr int CPB = 16 * A8_WAVES;   // channels per block
+        const int nb4 = (n4 + CPB - 1) / CPB, nb2 = (n2 + CPB - 1) / CPB;
         const dim3 g((unsigned)(nb4 + nb2), (unsigned)((b + 15) / 16));
-        k_sg_a8_mfma<<<g, 256, 0, s>>>(x, b, cols, rows, period, p4, p2, scales, y, n4, nb4);
+        k_sg_a8_mfma<<<g, 64 * A8_WAVES, 0, s>>>(x, b, cols, rows, period, p4, p2, scales, y, n4, nb4);
         return hipGetLastError();
     }
     const unsigned blocks = (unsigned)std::max(1, std::min((rows + 3) / 4, 2048));

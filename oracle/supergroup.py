@@ -134,13 +134,10 @@ def gemm(x: np.ndarray, W: SuperGroupWeight) -> np.ndarray:
 # activations to 8 bits (its table of 1.58-8-8 / 1.88-8-8 runs).  Readings where the page is
 # silent: one activation scale per token (row of X), symmetric, with the page's 4-bit formula
 # at n = 8: ``s_X = max(max|x| / (2^(8-1) - 1), eps)`` (in float32) stored as fp16;
-# ``Q(x) = clip(round(x / s_X), -127, 127)`` where round is the integer nearest to the real
-# quotient of x and the stored scale, ties to even.  For fp16 operands the float64 quotient
-# decides that exactly: x and s are multiples of 2^-24, so a quotient that is not a
-# half-integer lies at least 2^-24 / (2 s) >= 2^-34 from one, far beyond float64's rounding
-# of a quotient below 128.  The integer dot is exact; the scale product and the final scaling
-# are done in full precision here (the fp16 factors are exact in float64) and the result is
-# rounded to fp16 once.
+# ``Q(x) = clip(rint(x / s_X), -127, 127)`` with the quotient taken in float32 against the
+# stored scale, ties to even (the same reading as the weight quantizers above).  The integer
+# dot is exact; the scale product and the final scaling are done in full precision here (the
+# fp16 factors are exact in float64) and the result is rounded to fp16 once.
 
 ACT_QMAX = np.float32(127)    # 2^(8-1) - 1
 
@@ -150,7 +147,7 @@ def quantize_activations(x: np.ndarray):
     x = np.asarray(x, dtype=np.float16).astype(np.float32)
     amax = np.max(np.abs(x), axis=1)
     s16 = np.maximum(amax / ACT_QMAX, EPS).astype(np.float16)
-    q = np.clip(np.rint(x.astype(np.float64) / s16.astype(np.float64)[:, None]), -127, 127)
+    q = np.clip(np.rint(x / s16.astype(np.float32)[:, None]), -ACT_QMAX, ACT_QMAX)
     return q.astype(np.int8), s16
 
 

@@ -156,3 +156,17 @@ def test_binding_refuses_host_tensors():
     import torch
     with pytest.raises(TypeError):
         q.quantize_affine(torch.zeros(4, 64))
+
+
+def test_integer_path_rejects_bad_arguments():
+    f = q.lib.qmoe_quantize_act8
+    assert f(None, 1, 1024, FAKE, FAKE, None) == _lib.QMOE_ERR_INVALID_ARG
+    assert f(FAKE, 0, 1024, FAKE, FAKE, None) == _lib.QMOE_ERR_INVALID_ARG
+    assert f(FAKE, 1, 1000, FAKE, FAKE, None) == _lib.QMOE_ERR_UNSUPPORTED
+    assert f(FAKE + 2, 1, 1024, FAKE, FAKE, None) == _lib.QMOE_ERR_MISALIGNED
+    g = q.lib.qlinear_supergroup_a8
+    assert g(FAKE, 1, FAKE, FAKE, FAKE, 3070, 1024, 4, FAKE * 4, None) == _lib.QMOE_ERR_UNSUPPORTED
+    assert g(FAKE, 1, FAKE, None, FAKE, 3072, 1024, 4, FAKE * 4, None) == _lib.QMOE_ERR_INVALID_ARG
+    assert g(FAKE, 1, FAKE, FAKE, FAKE, 3072, 1000, 4, FAKE * 4, None) == _lib.QMOE_ERR_UNSUPPORTED
+    assert g(FAKE, 5000, FAKE, FAKE, FAKE, 3072, 1024, 4, FAKE * 4, None) == _lib.QMOE_ERR_UNSUPPORTED
+    assert g(FAKE + 8, 1, FAKE, FAKE, FAKE, 3072, 1024, 4, FAKE * 4, None) == _lib.QMOE_ERR_MISALIGNED
