@@ -167,3 +167,75 @@ def test_storage_arithmetic_matches_the_page():
     w = np.zeros((512, 2048), dtype=np.float32)
     qw = affine.quantize(w, 4, 64)
     assert qw.packed.nbytes + qw.scales.nbytes + qw.biases.nbytes == m["total_bytes"]
+
+
+# ---- group 32 and bf16 parameters (the port page's own checkpoint format) --------------
+
+def test_bf16_rounding_hand_values_and_library():
+    """Round to nearest even, by hand: 1.0 -> 0x3F80; 1 + 2^-8 is halfway between 0x3F80 and
+    0x3F81 -> even 0x3F80; 1 + 3 * 2^-8 halfway between 0x3F81 and 0x3F82 -> 0x3F82; just
+    above the first tie -> 0x3F81; -2.5 -> 0xC020; and equal to torch's CPU conversion on a
+    random sample that includes exact ties."""
+    x = np.array([1.0, 1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 1 + 2.0 ** -8 + 2.0 ** -20, -2.5], np.float32)
+    assert affine.bf16_bits(x).tolist() == [0x3F80, 0x3F80, 0x3F82, 0x3F81, 0xC020]
+    assert affine.bf16_to_f32(np.array([0x3F80, 0xC020], np.uint16)).tolist() == [1.0, -2.5]
+    import torch
+    g = np.random.default_rng(3)
+    v = (g.standard_normal(20000) * 0.05).astype(np.float32)
+    u = v.view(np.uint32).copy()
+    u[::7] = (u[::7] & 0xFFFF0000) | 0x8000          # exact ties
+    v = u.view(np.float32)
+    ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(affine.bf16_bits(v), ref)
+
+
+@pytest.mark.parametrize("param_dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("bits", [4, 8])
+def test_group32_codes_are_nearest_level_brute_force(bits, param_dtype):
+    """Group 32, fp16 or bf16 parameters: each group has its own scale and bias, and every code
+    is the grid level nearest to w (exact rationals), except at float32 near-ties."""
+    g = np.random.default_rng(31 + bits)
+    w = (g.standard_normal((20, 128)) * 0.02).astype(np.float32)
+    q, s, b = affine.quantize_codes(w, bits, 32, param_dtype)
+    assert s.shape == (20, 4)
+    qw = affine.QWeight(affine.pack(q, bits), s, b, bits, 32, param_dtype)
+    s32, b32 = affine.params_f32(qw)
+    top = 2 ** bits - 1
+    near = 0
+    for r in range(20):
+        for i in range(128):
+            S, B = Fraction(float(s32[r, i // 32])), Fraction(float(b32[r, i // 32]))
+            exact = (Fraction(float(w[r, i])) - B) / S       # nearest level: round the exact quotient
+            if int(q[r, i]) != min(top, max(0, round(exact))):
+                assert abs(float(exact - int(exact)) - 0.5) < 1e-5
+                near += 1
+    assert near <= 2
+    # the stored parameters are the rounded min-max values of each 32-input group
+    v = w.reshape(20, 4, 32)
+    lo, hi = v.min(2), v.max(2)
+    if param_dtype == "bf16":
+        assert np.array_equal(b, affine.bf16_bits(lo))
+        assert np.array_equal(s, affine.bf16_bits((hi - lo) / np.float32(top)))
+    else:
+        assert np.array_equal(b, lo.astype(np.float16))
+
+
+def test_bf16_group32_on_grid_import_is_exact():
+    """The port page's claim for QAT weights: integers plus bf16 parameters taken as given
+    dequantize exactly to scale * q + bias (0.0 error), and quantizing those grid values
+    again reproduces the same codes and parameters."""
+    g = np.random.default_rng(8)
+    n = 500
+    q = g.integers(0, 16, size=(n, 32)).astype(np.uint8)
+    q[:, 0], q[:, 1] = 0, 15
+    s = affine.bf16_bits(np.abs(g.standard_normal(n) * 0.004 + 0.006).astype(np.float32))
+    b = affine.bf16_bits((-7.5 * affine.bf16_to_f32(s) + g.standard_normal(n) * 0.001).astype(np.float32))
+    exact = affine.bf16_to_f32(s).astype(np.float64)[:, None] * q + affine.bf16_to_f32(b).astype(np.float64)[:, None]
+    w = exact.astype(np.float32)
+    keep = np.all(w.astype(np.float64) == exact, axis=1)
+    w, q, s, b = w[keep], q[keep], s[keep], b[keep]
+    imported = affine.QWeight(affine.pack(q, 4), s[:, None], b[:, None], 4, 32, "bf16")
+    assert np.max(np.abs(affine.dequantize(imported) - w.astype(np.float64))) == 0.0
+    again = affine.quantize(w, 4, 32, "bf16")
+    assert np.array_equal(affine.unpack(again.packed, 4), q)
+    assert np.array_equal(again.scales[:, 0], s) and np.array_equal(again.biases[:, 0], b)
