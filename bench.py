@@ -11,7 +11,8 @@ packed experts resident in HBM, 70x the 256 MB last-level cache) and every step 
 different token, so expert weights come from HBM as they do in a deep decode loop.  All
 inputs are resident before timing; the timed region is one HIP graph of exactly K steps.
 
-Other workloads (--workload): gemv (one int4 linear, x [1 x 2048], W [512 x 2048]),
+Other workloads (--workload): gemv (one int4 linear, x [1 x 2048], W [512 x 2048]; --group
+32 and --params bf16 select the port page's checkpoint format),
 moe_prefill (512 tokens, top-4; --skew adds +2.0 to the logits of experts 0..15),
 moe_stack (40 stacked layers, 16 tokens per step, top-8, 4 LoRA adapter sets),
 supergroup (mixed ternary/4-bit GEMM, W [3072 x 1024], --batch 1 or 64), supergroup_a8
@@ -525,13 +526,18 @@ def bench_gemv(args, q, torch):
     gen = torch.Generator(device="cuda")
     gen.manual_seed(1234)
     N, Kc, COPIES = 512, 2048, 2048      # 2048 weight copies = 1.2 GB > 4x the 256 MB cache
+    G, bf = args.group, args.params == "bf16"
     w = torch.randn((COPIES * N, Kc), generator=gen, device="cuda") * 0.02
-    big = q.quantize_affine(w, 4)
+    big = q.quantize_affine(w, 4, group=G)
     del w
+    if bf:   # the port page's format: bf16 parameters (here the fp16 ones re-rounded to bf16)
+        big.scales = big.scales.float().to(torch.bfloat16).view(torch.int16)
+        big.biases = big.biases.float().to(torch.bfloat16).view(torch.int16)
     mats = []
     for c in range(COPIES):
         m = q.QWeight(big.packed[c * N:(c + 1) * N], big.scales[c * N:(c + 1) * N],
-                      big.biases[c * N:(c + 1) * N], 4, N, Kc)
+                      big.biases[c * N:(c + 1) * N], 4, N, Kc, 1, G,
+                      q.PARAM_BF16 if bf else q.PARAM_F16)
         mats.append(m)
     K, W = args.steps, args.warmup
     xs = torch.randn((K + W, 1, Kc), generator=gen, device="cuda").half()
@@ -546,14 +552,15 @@ def bench_gemv(args, q, torch):
         graph_of(torch, run(K, K + W)).replay()
     g = graph_of(torch, run(0, K))
     ms = time_graph(torch, g)
-    bytes_ = MAT_BYTES_4BIT(N, Kc) + Kc * 2 + N * 2
+    bytes_ = N * Kc // 2 + 2 * (N * (Kc // G) * 2) + Kc * 2 + N * 2
     ach = bytes_ / (ms / K * 1e-3) / 1e9
+    fmt = f"int4 g{G}{' bf16 parameters' if bf else ''}"
     res = {"metric": "int4 linear GEMV calls/s (decode)", "value": K / (ms * 1e-3),
            "unit": "calls/s", "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": ms / K,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
            "data": "synthetic",
-           "config": {"workload": "qlinear_int4 x[1x2048] W[512x2048] int4 g64, 2048 weight copies rotated"},
-           "roofline": {"kernel": "k_qgemv_fast<4>", "bound": "hbm", "achieved": ach,
+           "config": {"workload": f"qlinear_int4 x[1x2048] W[512x2048] {fmt}, 2048 weight copies rotated"},
+           "roofline": {"kernel": f"k_qgemv_fast<4,{G},{'bf16' if bf else 'f16'}>", "bound": "hbm", "achieved": ach,
                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
                         "traffic": None, "bytes_per_launch": bytes_, "us_per_launch": ms / K * 1e3}}
     return res, None
@@ -573,6 +580,8 @@ def main():
     ap.add_argument("--workload", default="moe_decode", choices=sorted(WORKLOADS))
     ap.add_argument("--skew", action="store_true", help="moe_prefill: +2.0 on experts 0..15")
     ap.add_argument("--batch", type=int, default=1, choices=(1, 64), help="supergroup: inputs per call")
+    ap.add_argument("--group", type=int, default=64, choices=(32, 64), help="gemv: inputs per group")
+    ap.add_argument("--params", default="f16", choices=("f16", "bf16"), help="gemv: scale/bias type")
     ap.add_argument("--tokens", type=int, default=512,
                     help="moe_prefill: tokens per step (512 is the workload; others are a sweep)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -72,12 +72,19 @@ extern "C" {
  *   packed  uint32 [n_experts][rows][cols*bits/32]; element 8m+j of a row (bits = 4) is
  *           bits [4j, 4j+4) of word m, lowest nibble first; for bits = 8 element 4m+j is
  *           byte j of word m.
- *   scales  fp16 [n_experts][rows][cols/group]
- *   biases  fp16 [n_experts][rows][cols/group]
+ *   scales  fp16 or bf16 [n_experts][rows][cols/group] (param_dtype)
+ *   biases  fp16 or bf16 [n_experts][rows][cols/group]
  *   W[n][k] = scale[n][k/group] * q[n][k] + bias[n][k/group].
  *
- * Supported: bits in {4, 8}; group == 64; cols a multiple of 512; rows >= 1.
+ * Supported: bits in {4, 8}; cols a multiple of 512; rows >= 1; group 64 with fp16
+ * parameters everywhere.  qlinear_int4 and qmoe_dequantize also take group 32 and bf16
+ * parameters (QMOE_PARAM_BF16), the format of the bit-exact port page's QAT checkpoint
+ * ([R3] "4-bit group quantization": 32 weights per group, scale and bias in bf16), whose
+ * packed words and parameters are used as given, without requantization.  The MoE layer
+ * takes group 64, fp16.  param_dtype 0 (the zero-initialised default) is fp16.
  */
+#define QMOE_PARAM_F16 0
+#define QMOE_PARAM_BF16 1
 typedef struct qmoe_qweight {
     const uint32_t* packed;
     const uint16_t* scales;
@@ -86,7 +93,8 @@ typedef struct qmoe_qweight {
     int32_t cols;
     int32_t bits;
     int32_t group;
-    int32_t n_experts; /* 1 for a single matrix */
+    int32_t n_experts;   /* 1 for a single matrix */
+    int32_t param_dtype; /* QMOE_PARAM_F16 or QMOE_PARAM_BF16 */
 } qmoe_qweight;
 
 /*
@@ -163,7 +171,7 @@ const char* qmoe_last_error(void);
  * bias = fp16(min), both from float32 arithmetic; q = clip(rint((w - bias) / scale), 0,
  * 2^bits - 1) in float32 on the stored fp16 scale and bias (q = 0 where scale == 0).
  * Outputs packed [rows][cols*bits/32], scales and biases [rows][cols/group] in the layout
- * of qmoe_qweight.  bits in {4, 8}; group == 64; cols % 64 == 0.
+ * of qmoe_qweight (fp16 parameters).  bits in {4, 8}; group 64 or 32; cols % 64 == 0.
  */
 int qmoe_quantize_affine(const float* w, int32_t rows, int32_t cols, int32_t bits,
                          int32_t group, uint32_t* packed, uint16_t* scales,

@@ -8,6 +8,8 @@ kernels.  Importing the package requires the built library (see build.py).
 from ._lib import LIB_PATH, EXPORTED, QmoeError, lib  # noqa: F401
 from .api import (  # noqa: F401
     Lora,
+    PARAM_BF16,
+    PARAM_F16,
     MoECall,
     STAGE_ALL,
     STAGE_DOWN,

@@ -30,7 +30,7 @@ class QWeightC(ctypes.Structure):
     _fields_ = [("packed", ctypes.c_void_p), ("scales", ctypes.c_void_p),
                 ("biases", ctypes.c_void_p), ("rows", ctypes.c_int32), ("cols", ctypes.c_int32),
                 ("bits", ctypes.c_int32), ("group", ctypes.c_int32),
-                ("n_experts", ctypes.c_int32)]
+                ("n_experts", ctypes.c_int32), ("param_dtype", ctypes.c_int32)]
 
 
 class LoraC(ctypes.Structure):

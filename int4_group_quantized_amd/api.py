@@ -41,8 +41,9 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
 class QWeight:
     """Group-affine quantized matrix (or expert stack) on the device.
 
-    packed int32 [n_experts*rows, cols*bits/32] (uint32 words), scales / biases fp16
-    [n_experts*rows, cols/group]."""
+    packed int32 [n_experts*rows, cols*bits/32] (uint32 words), scales / biases fp16 (or
+    bf16 bit patterns in int16 tensors when param_dtype is PARAM_BF16) [n_experts*rows,
+    cols/group]."""
 
     packed: torch.Tensor
     scales: torch.Tensor
@@ -52,22 +53,28 @@ class QWeight:
     cols: int
     n_experts: int = 1
     group: int = 64
+    param_dtype: int = 0
 
     def c(self) -> QWeightC:
         return QWeightC(self.packed.data_ptr(), self.scales.data_ptr(), self.biases.data_ptr(),
-                        self.rows, self.cols, self.bits, self.group, self.n_experts)
+                        self.rows, self.cols, self.bits, self.group, self.n_experts,
+                        self.param_dtype)
 
     @classmethod
     def from_arrays(cls, packed: np.ndarray, scales: np.ndarray, biases: np.ndarray, bits: int,
-                    device="cuda") -> "QWeight":
-        """From host arrays (uint32 words, fp16 scales and biases), optionally stacked
-        along a leading expert axis."""
+                    device="cuda", group: int = 64, param_dtype: int = 0) -> "QWeight":
+        """From host arrays (uint32 words; fp16 scales and biases, or their bf16 bit patterns
+        as uint16 with param_dtype PARAM_BF16), optionally stacked along a leading expert
+        axis.  The words and parameters are used as given (no requantization)."""
         n_experts = packed.shape[0] if packed.ndim == 3 else 1
-        rows, cols = scales.shape[-2], scales.shape[-1] * 64
+        rows, cols = scales.shape[-2], scales.shape[-1] * group
         p = torch.from_numpy(np.ascontiguousarray(packed).view(np.int32).reshape(n_experts * rows, -1))
-        s = torch.from_numpy(np.ascontiguousarray(scales).reshape(n_experts * rows, -1))
-        b = torch.from_numpy(np.ascontiguousarray(biases).reshape(n_experts * rows, -1))
-        return cls(p.to(device), s.to(device), b.to(device), bits, rows, cols, n_experts)
+        s = torch.from_numpy(np.ascontiguousarray(scales).view(np.int16 if param_dtype else np.float16)
+                             .reshape(n_experts * rows, -1))
+        b = torch.from_numpy(np.ascontiguousarray(biases).view(np.int16 if param_dtype else np.float16)
+                             .reshape(n_experts * rows, -1))
+        return cls(p.to(device), s.to(device), b.to(device), bits, rows, cols, n_experts, group,
+                   param_dtype)
 
     def expert(self, e: int) -> "QWeight":
         r = self.rows
@@ -151,7 +158,7 @@ def quantize_affine(w: torch.Tensor, bits: int = 4, group: int = 64) -> QWeight:
     check(lib.qmoe_quantize_affine(w.data_ptr(), rows, cols, bits, group, packed.data_ptr(),
                                    scales.data_ptr(), biases.data_ptr(), _stream(w)),
           "qmoe_quantize_affine")
-    return QWeight(packed, scales, biases, bits, rows, cols)
+    return QWeight(packed, scales, biases, bits, rows, cols, 1, group)
 
 
 def unpack(qw: QWeight) -> torch.Tensor:
@@ -249,6 +256,7 @@ def moe_switchglu_int4(layer: MoELayer, x: torch.Tensor,
 
 
 STAGE_ALL, STAGE_ROUTE, STAGE_GATE_UP, STAGE_DOWN = 0, 1, 2, 3
+PARAM_F16, PARAM_BF16 = 0, 1
 
 
 class MoECall:

@@ -23,13 +23,16 @@ int hip_status(hipError_t e) {
     return QMOE_ERR_HIP;
 }
 
-// A quantized matrix that the GEMV/GEMM kernels read.
-int check_qweight(const qmoe_qweight* w, int bits_required) {
+// A quantized matrix that the GEMV/GEMM kernels read: group 64 with fp16 parameters, or
+// for the dense linear (`dense`) also group 32 and bf16 parameters.
+int check_qweight(const qmoe_qweight* w, int bits_required, bool dense = false) {
     if (!w || !w->packed || !w->scales || !w->biases) return QMOE_ERR_INVALID_ARG;
     if (w->rows <= 0 || w->cols <= 0 || w->n_experts <= 0) return QMOE_ERR_INVALID_ARG;
     if (w->bits != 4 && w->bits != 8) return QMOE_ERR_UNSUPPORTED;
     if (bits_required && w->bits != bits_required) return QMOE_ERR_UNSUPPORTED;
-    if (w->group != 64) return QMOE_ERR_UNSUPPORTED;
+    if (w->param_dtype != QMOE_PARAM_F16 && w->param_dtype != QMOE_PARAM_BF16) return QMOE_ERR_UNSUPPORTED;
+    if (dense ? (w->group != 64 && w->group != 32) : (w->group != 64 || w->param_dtype != QMOE_PARAM_F16))
+        return QMOE_ERR_UNSUPPORTED;
     if (w->cols % 512 != 0 || w->cols > MAX_COLS) return QMOE_ERR_UNSUPPORTED;
     if (!aligned16(w->packed)) return QMOE_ERR_MISALIGNED;
     return QMOE_OK;
@@ -114,10 +117,10 @@ int qmoe_quantize_affine(const float* w, int32_t rows, int32_t cols, int32_t bit
                          uint16_t* biases, void* stream) {
     if (!w || !packed || !scales || !biases) return QMOE_ERR_INVALID_ARG;
     if (rows <= 0 || cols <= 0) return QMOE_ERR_INVALID_ARG;
-    if ((bits != 4 && bits != 8) || group != 64 || cols % 64) return QMOE_ERR_UNSUPPORTED;
+    if ((bits != 4 && bits != 8) || (group != 64 && group != 32) || cols % 64) return QMOE_ERR_UNSUPPORTED;
     if (!aligned16(w) || !aligned16(packed)) return QMOE_ERR_MISALIGNED;
-    return hip_status(qmoe::launch_quantize_affine(w, rows, cols, bits, packed, scales, biases,
-                                                   as_stream(stream)));
+    return hip_status(qmoe::launch_quantize_affine(w, rows, cols, bits, group, packed, scales,
+                                                   biases, as_stream(stream)));
 }
 
 int qmoe_unpack(const uint32_t* packed, int32_t rows, int32_t cols, int32_t bits, uint8_t* q,
@@ -132,7 +135,9 @@ int qmoe_unpack(const uint32_t* packed, int32_t rows, int32_t cols, int32_t bits
 int qmoe_dequantize(const qmoe_qweight* w, float* out, void* stream) {
     if (!w || !w->packed || !w->scales || !w->biases || !out) return QMOE_ERR_INVALID_ARG;
     if (w->rows <= 0 || w->cols <= 0 || w->n_experts <= 0) return QMOE_ERR_INVALID_ARG;
-    if ((w->bits != 4 && w->bits != 8) || w->group != 64 || w->cols % 64) return QMOE_ERR_UNSUPPORTED;
+    if ((w->bits != 4 && w->bits != 8) || (w->group != 64 && w->group != 32) || w->cols % 64)
+        return QMOE_ERR_UNSUPPORTED;
+    if (w->param_dtype != QMOE_PARAM_F16 && w->param_dtype != QMOE_PARAM_BF16) return QMOE_ERR_UNSUPPORTED;
     if (!aligned16(out)) return QMOE_ERR_MISALIGNED;
     return hip_status(qmoe::launch_dequantize(*w, out, as_stream(stream)));
 }
@@ -141,7 +146,7 @@ int qlinear_int4(const uint16_t* x, int32_t m, const qmoe_qweight* w, const qmoe
                  const int32_t* adapter_idx, uint16_t* y, void* stream) {
     if (!x || !y || m <= 0) return QMOE_ERR_INVALID_ARG;
     if (m > 4096) return QMOE_ERR_UNSUPPORTED;
-    int st = check_qweight(w, 0);
+    int st = check_qweight(w, 0, true);
     if (st) return st;
     if (w->n_experts != 1) return QMOE_ERR_INVALID_ARG;
     if ((st = check_lora(lora, w->cols, w->rows))) return st;

@@ -23,6 +23,9 @@ __device__ __forceinline__ float h2f(uint16_t b) { return (float)__builtin_bit_c
 // fp32 -> fp16, round to nearest even (v_cvt_f16_f32 in the default rounding mode)
 __device__ __forceinline__ uint16_t f2h(float v) { return __builtin_bit_cast(uint16_t, (f16)v); }
 
+// bf16 bits -> fp32 (exact): the upper half of the fp32 pattern
+__device__ __forceinline__ float bf2f(uint16_t b) { return __builtin_bit_cast(float, (uint32_t)b << 16); }
+
 __device__ __forceinline__ f16x2 as_h2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
 __device__ __forceinline__ uint32_t as_u32(f16x2 h) { return __builtin_bit_cast(uint32_t, h); }
 

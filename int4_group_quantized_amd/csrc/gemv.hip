@@ -1,7 +1,8 @@
 // Quantized linear for a few tokens: y = fp16(x W^T + LoRA delta), fp32 accumulation.
 //
 // Every linear layer of the checkpoint is stored as packed integer words plus one fp16
-// scale and one fp16 bias per group of 64 inputs and is dequantized on the fly
+// scale and one fp16 bias per group of 64 inputs (the port page's QAT checkpoint: bf16
+// parameters per 32 inputs, also served here) and is dequantized on the fly
 // ("Recover-LoRA ..." section 1; "Bit-exact MLX 4-bit port ..." "4-bit group
 // quantization"); the recovery LoRA is added as an unmerged parallel delta ("Recover-LoRA"
 // section 2; "Edge0 project review" highlight 3).
@@ -44,7 +45,7 @@ __device__ void lora_down_block(const uint16_t* __restrict__ x, int K, int t0, i
     }
 }
 
-template <int BITS>
+template <int BITS, int G, bool BF>
 __global__ void __launch_bounds__(256) k_qgemv(const uint16_t* __restrict__ x, int m, int K, int N,
                                                const uint32_t* __restrict__ packed,
                                                const uint16_t* __restrict__ scales,
@@ -80,7 +81,7 @@ __global__ void __launch_bounds__(256) k_qgemv(const uint16_t* __restrict__ x, i
             float acc[GEMV_MT];
 #pragma unroll
             for (int t = 0; t < GEMV_MT; ++t) acc[t] = 0.0f;
-            if (row < N) qdot_row<BITS>(packed, scales, biases, K, row, lpr, sl, xs, xsum, mt, acc);
+            if (row < N) qdot_row<BITS, G, BF>(packed, scales, biases, K, row, lpr, sl, xs, xsum, mt, acc);
 #pragma unroll
             for (int t = 0; t < GEMV_MT; ++t) {
                 if (t < mt) {
@@ -103,7 +104,7 @@ __global__ void __launch_bounds__(256) k_qgemv(const uint16_t* __restrict__ x, i
 
 // Fast path (no LoRA, m <= 8, at most two 32-input chunks per lane): each lane segment's
 // weight loads are issued first, then x is staged, so the two memory round trips overlap.
-template <int BITS>
+template <int BITS, int G, bool BF>
 __global__ void __launch_bounds__(256) k_qgemv_fast(const uint16_t* __restrict__ x, int m, int K,
                                                     int N, const uint32_t* __restrict__ packed,
                                                     const uint16_t* __restrict__ scales,
@@ -117,7 +118,7 @@ __global__ void __launch_bounds__(256) k_qgemv_fast(const uint16_t* __restrict__
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lpr = lanes_per_row(K), rpw = 64 / lpr, seg = lane / lpr, sl = lane % lpr;
     const int row = (blockIdx.x * 4 + wave) * rpw + seg;
-    RowRegs<BITS, 2> rr;
+    RowRegs<BITS, 2, G, BF> rr;
     rr.load(packed, scales, biases, K, row < N ? row : 0, lpr, sl, row < N);
     const uint4* x4 = reinterpret_cast<const uint4*>(x);
     stage_rows<BITS, 8>([=](int i) { return x4 + (long)i * (K / 8); }, m, K, xs, xsum);
@@ -135,11 +136,9 @@ __global__ void __launch_bounds__(256) k_qgemv_fast(const uint16_t* __restrict__
     }
 }
 
-}  // namespace
-
-hipError_t launch_qlinear_gemv(const uint16_t* x, int m, const qmoe_qweight& w,
-                               const qmoe_lora* lora, const int32_t* adapter_idx,
-                               uint16_t* y, hipStream_t s) {
+template <int BITS, int G, bool BF>
+hipError_t launch_gemv_t(const uint16_t* x, int m, const qmoe_qweight& w, const qmoe_lora* lora,
+                         const int32_t* adapter_idx, uint16_t* y, hipStream_t s) {
     const int K = w.cols, N = w.rows;
     const int rpw = 64 / lanes_per_row(K);
     const int mt_max = std::min(GEMV_MT, XS_BYTES / (K * 2));
@@ -149,8 +148,7 @@ hipError_t launch_qlinear_gemv(const uint16_t* x, int m, const qmoe_qweight& w,
     const int cpl = (K / 32) / lanes_per_row(K);
     if (!lora && m <= mt_max && cpl <= 2 && m * (K / 8) <= 256 * 8) {
         const unsigned fb = (unsigned)((N + 4 * rpw - 1) / (4 * rpw));
-        if (w.bits == 4) k_qgemv_fast<4><<<fb, 256, smem, s>>>(x, m, K, N, w.packed, w.scales, w.biases, y);
-        else k_qgemv_fast<8><<<fb, 256, smem, s>>>(x, m, K, N, w.packed, w.scales, w.biases, y);
+        k_qgemv_fast<BITS, G, BF><<<fb, 256, smem, s>>>(x, m, K, N, w.packed, w.scales, w.biases, y);
         return hipGetLastError();
     }
     const uint16_t* A = lora ? lora->A : nullptr;
@@ -158,11 +156,29 @@ hipError_t launch_qlinear_gemv(const uint16_t* x, int m, const qmoe_qweight& w,
     const int rank = lora ? lora->rank : 0;
     const int n_ad = lora ? lora->n_adapters : 1;
     const float ls = lora ? lora->scale : 0.0f;
-    if (w.bits == 4)
-        k_qgemv<4><<<blocks, 256, smem, s>>>(x, m, K, N, w.packed, w.scales, w.biases, A, B, rank, n_ad, ls, adapter_idx, y, mt_max);
-    else
-        k_qgemv<8><<<blocks, 256, smem, s>>>(x, m, K, N, w.packed, w.scales, w.biases, A, B, rank, n_ad, ls, adapter_idx, y, mt_max);
+    k_qgemv<BITS, G, BF><<<blocks, 256, smem, s>>>(x, m, K, N, w.packed, w.scales, w.biases, A, B, rank,
+                                                  n_ad, ls, adapter_idx, y, mt_max);
     return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t launch_gemv_bits(const uint16_t* x, int m, const qmoe_qweight& w, const qmoe_lora* lora,
+                            const int32_t* adapter_idx, uint16_t* y, hipStream_t s) {
+    const bool bf = w.param_dtype == QMOE_PARAM_BF16;
+    if (w.group == 32)
+        return bf ? launch_gemv_t<BITS, 32, true>(x, m, w, lora, adapter_idx, y, s)
+                  : launch_gemv_t<BITS, 32, false>(x, m, w, lora, adapter_idx, y, s);
+    return bf ? launch_gemv_t<BITS, 64, true>(x, m, w, lora, adapter_idx, y, s)
+              : launch_gemv_t<BITS, 64, false>(x, m, w, lora, adapter_idx, y, s);
+}
+
+}  // namespace
+
+hipError_t launch_qlinear_gemv(const uint16_t* x, int m, const qmoe_qweight& w,
+                               const qmoe_lora* lora, const int32_t* adapter_idx,
+                               uint16_t* y, hipStream_t s) {
+    return w.bits == 4 ? launch_gemv_bits<4>(x, m, w, lora, adapter_idx, y, s)
+                       : launch_gemv_bits<8>(x, m, w, lora, adapter_idx, y, s);
 }
 
 }  // namespace qmoe

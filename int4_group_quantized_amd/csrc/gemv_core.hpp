@@ -111,8 +111,14 @@ struct StageRegs {
     }
 };
 
-// acc[t] += this lane's share of row `row` . x_t for t < mt (segment-partial sums).
-template <int BITS>
+// A stored group parameter as fp32: fp16 bits, or bf16 bits when BF.
+template <bool BF>
+__device__ __forceinline__ float param_f32(uint16_t v) { return BF ? bf2f(v) : h2f(v); }
+
+// acc[t] += this lane's share of row `row` . x_t for t < mt (segment-partial sums).  G is
+// the group size (64, or 32: then every 32-input chunk has its own parameters), BF selects
+// bf16 parameters.
+template <int BITS, int G = 64, bool BF = false>
 __device__ __forceinline__ void qdot_row(const uint32_t* __restrict__ packed,
                                          const uint16_t* __restrict__ scales,
                                          const uint16_t* __restrict__ biases, int K, long row,
@@ -130,8 +136,8 @@ __device__ __forceinline__ void qdot_row(const uint32_t* __restrict__ packed,
             const uint4 v = src[i];
             wd[4 * i] = v.x; wd[4 * i + 1] = v.y; wd[4 * i + 2] = v.z; wd[4 * i + 3] = v.w;
         }
-        const long gi = row * (K / 64) + c / 2;
-        const float s = h2f(scales[gi]), b = h2f(biases[gi]);
+        const long gi = row * (K / G) + c / (G / 32);
+        const float s = param_f32<BF>(scales[gi]), b = param_f32<BF>(biases[gi]);
         const float sC = s * C, bb = b - sC;
 #pragma unroll
         for (int t = 0; t < GEMV_MT; ++t) {
@@ -151,11 +157,11 @@ __device__ __forceinline__ void qdot_row(const uint32_t* __restrict__ packed,
 
 // One row's chunks for this lane (the chunk set of qdot_row, at most MAXC of them), loaded
 // into registers by load() so that every load of a wave is in flight before any dot.
-template <int BITS, int MAXC>
+template <int BITS, int MAXC, int G = 64, bool BF = false>
 struct RowRegs {
     static constexpr int WPC = BITS == 4 ? 4 : 8;
     uint32_t w[MAXC][WPC];
-    uint16_t s[MAXC], b[MAXC];   // raw fp16 bits: converted only when used
+    uint16_t s[MAXC], b[MAXC];   // raw parameter bits: converted only when used
     int n;
     // Loads are unconditional (chunk index clamped into the row, `valid == false` reads the
     // same row and marks nothing usable) so the compiler issues them without branches and
@@ -176,7 +182,7 @@ struct RowRegs {
                 const uint4 v = src[j];
                 w[i][4 * j] = v.x; w[i][4 * j + 1] = v.y; w[i][4 * j + 2] = v.z; w[i][4 * j + 3] = v.w;
             }
-            const long gi = row * (K / 64) + c / 2;
+            const long gi = row * (K / G) + c / (G / 32);
             s[i] = scales[gi];
             b[i] = biases[gi];
             if (valid && sl + i * lpr < chunks) n = i + 1;
@@ -205,7 +211,7 @@ struct RowRegs {
         for (int i = 0; i < MAXC; ++i) {
             if (i < n) {
                 const int c = sl + i * lpr;
-                const float sC = h2f(s[i]) * C, bb = h2f(b[i]) - sC;
+                const float sC = param_f32<BF>(s[i]) * C, bb = param_f32<BF>(b[i]) - sC;
 #pragma unroll
                 for (int t = 0; t < GEMV_MT; ++t) {
                     if (t < mt) {

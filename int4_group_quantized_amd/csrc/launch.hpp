@@ -12,7 +12,7 @@
 namespace qmoe {
 
 // quant.hip
-hipError_t launch_quantize_affine(const float* w, int rows, int cols, int bits,
+hipError_t launch_quantize_affine(const float* w, int rows, int cols, int bits, int group,
                                   uint32_t* packed, uint16_t* scales, uint16_t* biases,
                                   hipStream_t s);
 hipError_t launch_unpack(const uint32_t* packed, long n_words, int bits, uint8_t* q,

@@ -1,8 +1,8 @@
 // Affine group quantization, unpacking and dequantization; super-group quantization.
 //
 // Affine format ("Recover-LoRA ..." section 1; "Bit-exact MLX 4-bit port ..." section
-// "4-bit group quantization"): per row and group of 64 inputs one fp16 scale and one fp16
-// bias, codes in packed uint32 words (lowest field first); w = scale * q + bias.
+// "4-bit group quantization"): per row and group of 64 (or 32) inputs one fp16 scale and
+// one fp16 bias, codes in packed uint32 words (lowest field first); w = scale * q + bias.
 // Super-group format ("EDGERAZOR deep dive" section 2.1): one 4-bit symmetric channel per
 // block of `period` output channels, the others ternary.
 //
@@ -14,31 +14,31 @@
 
 namespace qmoe {
 
-// One thread per (row, group of 64).
-template <int BITS>
+// One thread per (row, group of G inputs).
+template <int BITS, int G>
 __global__ void __launch_bounds__(256) k_quantize_affine(const float* __restrict__ w,
-                                                         long n_groups, int groups_per_row,
+                                                         long n_groups,
                                                          uint32_t* __restrict__ packed,
                                                          uint16_t* __restrict__ scales,
                                                          uint16_t* __restrict__ biases) {
     const long g = (long)blockIdx.x * blockDim.x + threadIdx.x;
     if (g >= n_groups) return;
-    const float4* src = reinterpret_cast<const float4*>(w + g * 64);
-    float v[64];
+    const float4* src = reinterpret_cast<const float4*>(w + g * G);
+    float v[G];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < G / 4; ++i) {
         float4 t = src[i];
         v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
     }
     float lo = v[0], hi = v[0];
 #pragma unroll
-    for (int i = 1; i < 64; ++i) { lo = fminf(lo, v[i]); hi = fmaxf(hi, v[i]); }
+    for (int i = 1; i < G; ++i) { lo = fminf(lo, v[i]); hi = fmaxf(hi, v[i]); }
     constexpr float top = BITS == 4 ? 15.0f : 255.0f;
     const f16 sh = (f16)__fdiv_rn(__fsub_rn(hi, lo), top);
     const f16 bh = (f16)lo;
     const float s = (float)sh, b = (float)bh;
     constexpr int PER = 32 / BITS;          // codes per word
-    constexpr int NW = 64 / PER;            // words per group
+    constexpr int NW = G / PER;             // words per group
     uint32_t words[NW];
 #pragma unroll
     for (int m = 0; m < NW; ++m) {
@@ -58,15 +58,18 @@ __global__ void __launch_bounds__(256) k_quantize_affine(const float* __restrict
     biases[g] = __builtin_bit_cast(uint16_t, bh);
 }
 
-hipError_t launch_quantize_affine(const float* w, int rows, int cols, int bits,
+hipError_t launch_quantize_affine(const float* w, int rows, int cols, int bits, int group,
                                   uint32_t* packed, uint16_t* scales, uint16_t* biases,
                                   hipStream_t s) {
-    const long n_groups = (long)rows * (cols / 64);
+    const long n_groups = (long)rows * (cols / group);
     const unsigned blocks = (unsigned)((n_groups + 255) / 256);
-    if (bits == 4)
-        k_quantize_affine<4><<<blocks, 256, 0, s>>>(w, n_groups, cols / 64, packed, scales, biases);
-    else
-        k_quantize_affine<8><<<blocks, 256, 0, s>>>(w, n_groups, cols / 64, packed, scales, biases);
+    if (group == 32) {
+        if (bits == 4) k_quantize_affine<4, 32><<<blocks, 256, 0, s>>>(w, n_groups, packed, scales, biases);
+        else k_quantize_affine<8, 32><<<blocks, 256, 0, s>>>(w, n_groups, packed, scales, biases);
+    } else {
+        if (bits == 4) k_quantize_affine<4, 64><<<blocks, 256, 0, s>>>(w, n_groups, packed, scales, biases);
+        else k_quantize_affine<8, 64><<<blocks, 256, 0, s>>>(w, n_groups, packed, scales, biases);
+    }
     return hipGetLastError();
 }
 
@@ -98,17 +101,20 @@ hipError_t launch_unpack(const uint32_t* packed, long n_words, int bits, uint8_t
     return hipGetLastError();
 }
 
-// One thread per word: fp32(s * q + b) with one rounding (fmaf of an exact product).
+// One thread per word: fp32(s * q + b) with one rounding (fmaf of an exact product); the
+// parameters fp16 or bf16 (bf16 of the port page's checkpoint), the group 64 or 32.
 template <int BITS>
 __global__ void __launch_bounds__(256) k_dequantize(const uint32_t* __restrict__ packed,
                                                     const uint16_t* __restrict__ scales,
                                                     const uint16_t* __restrict__ biases,
-                                                    long n_words, float* __restrict__ out) {
+                                                    long n_words, int group, int bf16,
+                                                    float* __restrict__ out) {
     const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n_words) return;
     constexpr int PER = 32 / BITS;
-    const long grp = i / (64 / PER);      // words of a group are consecutive
-    const float sc = h2f(scales[grp]), bi = h2f(biases[grp]);
+    const long grp = i / (group / PER);   // words of a group are consecutive
+    const float sc = bf16 ? bf2f(scales[grp]) : h2f(scales[grp]);
+    const float bi = bf16 ? bf2f(biases[grp]) : h2f(biases[grp]);
     const uint32_t w = packed[i];
     float r[PER];
 #pragma unroll
@@ -121,8 +127,9 @@ __global__ void __launch_bounds__(256) k_dequantize(const uint32_t* __restrict__
 hipError_t launch_dequantize(const qmoe_qweight& w, float* out, hipStream_t s) {
     const long n_words = (long)w.n_experts * w.rows * (w.cols * w.bits / 32);
     const unsigned blocks = (unsigned)((n_words + 255) / 256);
-    if (w.bits == 4) k_dequantize<4><<<blocks, 256, 0, s>>>(w.packed, w.scales, w.biases, n_words, out);
-    else k_dequantize<8><<<blocks, 256, 0, s>>>(w.packed, w.scales, w.biases, n_words, out);
+    const int bf = w.param_dtype == QMOE_PARAM_BF16;
+    if (w.bits == 4) k_dequantize<4><<<blocks, 256, 0, s>>>(w.packed, w.scales, w.biases, n_words, w.group, bf, out);
+    else k_dequantize<8><<<blocks, 256, 0, s>>>(w.packed, w.scales, w.biases, n_words, w.group, bf, out);
     return hipGetLastError();
 }
 

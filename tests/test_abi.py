@@ -48,8 +48,8 @@ def test_version_status_and_struct_layout():
 FAKE = 0x100000  # a 16-byte aligned fake device address; never dereferenced (validation fails first)
 
 
-def qw(rows=512, cols=2048, bits=4, n_experts=1, packed=FAKE):
-    return _lib.QWeightC(packed, FAKE, FAKE, rows, cols, bits, 64, n_experts)
+def qw(rows=512, cols=2048, bits=4, n_experts=1, packed=FAKE, group=64, param_dtype=0):
+    return _lib.QWeightC(packed, FAKE, FAKE, rows, cols, bits, group, n_experts, param_dtype)
 
 
 def test_quantize_rejects_bad_arguments():
@@ -57,7 +57,7 @@ def test_quantize_rejects_bad_arguments():
     assert f(None, 4, 64, 4, 64, FAKE, FAKE, FAKE, None) == _lib.QMOE_ERR_INVALID_ARG
     assert f(FAKE, 0, 64, 4, 64, FAKE, FAKE, FAKE, None) == _lib.QMOE_ERR_INVALID_ARG
     assert f(FAKE, 4, 64, 3, 64, FAKE, FAKE, FAKE, None) == _lib.QMOE_ERR_UNSUPPORTED
-    assert f(FAKE, 4, 64, 4, 32, FAKE, FAKE, FAKE, None) == _lib.QMOE_ERR_UNSUPPORTED
+    assert f(FAKE, 4, 64, 4, 16, FAKE, FAKE, FAKE, None) == _lib.QMOE_ERR_UNSUPPORTED
     assert f(FAKE, 4, 96, 4, 64, FAKE, FAKE, FAKE, None) == _lib.QMOE_ERR_UNSUPPORTED
     assert f(FAKE + 4, 4, 64, 4, 64, FAKE, FAKE, FAKE, None) == _lib.QMOE_ERR_MISALIGNED
 
@@ -81,6 +81,9 @@ def test_qlinear_rejects_bad_arguments():
     assert f(FAKE, 1, ctypes.byref(w), ctypes.byref(lo), None, FAKE * 8, None) == _lib.QMOE_ERR_INVALID_ARG
     # output overlapping the input
     assert f(FAKE, 1, ctypes.byref(w), None, None, FAKE + 16, None) == _lib.QMOE_ERR_INVALID_ARG
+    # group 32 / bf16 parameters are accepted by the dense linear's validation, other values not
+    for bad in (qw(group=16), qw(group=128), qw(param_dtype=2)):
+        assert f(FAKE, 1, ctypes.byref(bad), None, None, FAKE * 8, None) == _lib.QMOE_ERR_UNSUPPORTED
 
 
 def test_router_topk_rejects_bad_arguments():
@@ -126,7 +129,8 @@ def test_moe_workspace_and_validation():
     assert f(ctypes.byref(L), X, 1, None, X, None, None, FAKE * 64, ws1, None) == _lib.QMOE_ERR_INVALID_ARG
     for bad in (layer_c(top_k=0), layer_c(top_k=300), layer_c(hidden=1000),
                 layer_c(router=qw(256, 2048, 4)), layer_c(exp_down=qw(512, 2048, 4, 256)),
-                layer_c(n_experts=2000)):
+                layer_c(n_experts=2000), layer_c(exp_gate=qw(512, 2048, 4, 256, group=32)),
+                layer_c(sh_up=qw(512, 2048, param_dtype=1))):
         st = f(ctypes.byref(bad), X, 1, None, Y, None, None, FAKE * 64, 1 << 30, None)
         assert st in (_lib.QMOE_ERR_INVALID_ARG, _lib.QMOE_ERR_UNSUPPORTED), st
     lo = _lib.LoraC(FAKE, FAKE, 16, 4, 2048, 1024, 2.0)  # wrong out_dim for the shared gate

@@ -319,3 +319,69 @@ def test_supergroup_a8_integer_case_exact(q):
     assert np.all(np.abs(v) <= 2048)
     exact = v * 2.0 ** -5
     assert np.array_equal(y.astype(np.float64), exact)
+
+
+# ------------------------------------------------------------------------------ group 32, bf16 parameters
+
+_PD = {"f16": 0, "bf16": 1}
+
+
+def _qw_g(rows, cols, bits, group, pdt, idx):
+    w = synth.normal_f32((rows, cols), 0.02, W, 5, synth.Role.DENSE, idx)
+    w[0, :group] = 0.25                          # a constant group: scale 0
+    w[1, 3] = 2.0                                # an outlier
+    return affine.quantize(w, bits, group, pdt)
+
+
+def _dev_qw(q, ref):
+    return q.QWeight.from_arrays(ref.packed, ref.scales, ref.biases, ref.bits, DEV, group=ref.group,
+                                 param_dtype=_PD[ref.param_dtype])
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("shape", [(64, 2048), (7, 512), (33, 1536)])
+def test_quantize_group32_bit_exact(q, bits, shape):
+    w = special_matrix(*shape, seed=shape[0] + bits)
+    ref = affine.quantize(w, bits, 32)
+    got = q.quantize_affine(dev(w), bits, group=32)
+    assert np.array_equal(host(got.packed).view(np.uint32), ref.packed)
+    assert np.array_equal(host(got.scales).view(np.uint16), ref.scales.view(np.uint16))
+    assert np.array_equal(host(got.biases).view(np.uint16), ref.biases.view(np.uint16))
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("group,pdt", [(32, "f16"), (32, "bf16"), (64, "bf16")])
+def test_dequantize_group32_bf16_bit_exact(q, bits, group, pdt):
+    """Packed words and parameters taken as given (the import path): the fp32 dequantized
+    weights equal the oracle's single rounding of s * q + b bit for bit."""
+    ref = _qw_g(96, 1024, bits, group, pdt, 1)
+    got = host(q.dequantize(_dev_qw(q, ref)))
+    assert np.array_equal(got.view(np.uint32), affine.dequantize_f32(ref).view(np.uint32))
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("group,pdt", [(32, "f16"), (32, "bf16"), (64, "bf16")])
+@pytest.mark.parametrize("m,rows,cols", [(1, 512, 2048), (5, 96, 1024), (12, 130, 4096)])
+def test_qlinear_group32_bf16(q, bits, group, pdt, m, rows, cols):
+    """The dense linear on group-32 and/or bf16-parameter weights (the GEMV fast path at
+    m <= 8, the general path above), to the float bar; 4-bit within one fp16 step of the
+    correctly rounded oracle (8-bit codes enter as 1 + q/256, whose per-group affine terms
+    cancel more of the fp32 sum, as with fp16 parameters)."""
+    ref = _qw_g(rows, cols, bits, group, pdt, m + rows)
+    x = synth.activations(m, cols, W, 5, m)
+    y = host(q.qlinear_int4(dev(x), _dev_qw(q, ref)))
+    exact = moe.qlinear(x, ref)
+    assert_close(y, exact, what="qlinear g32/bf16")
+    if bits == 4:
+        assert ulp_distance(y, moe.to_f16(exact)) <= 1
+
+
+def test_qlinear_group32_bf16_with_lora(q):
+    rows, cols, T, n_ad, r = 512, 2048, 8, 4, 16
+    ref = _qw_g(rows, cols, 4, 32, "bf16", 9)
+    A = synth.normal_f16((n_ad, r, cols), 0.01, W, 6, synth.Role.LORA_A_GATE)
+    B = synth.normal_f16((n_ad, rows, r), 0.01, W, 6, synth.Role.LORA_B_GATE)
+    ad = synth.adapter_index(T, 2)
+    x = synth.activations(T, cols, W, 6)
+    y = host(q.qlinear_int4(dev(x), _dev_qw(q, ref), q.Lora(dev(A), dev(B), 2.0), dev(ad)))
+    assert_close(y, moe.qlinear(x, ref, moe.Lora(A, B, 2.0), ad), what="qlinear g32/bf16 + lora")
