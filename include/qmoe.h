@@ -295,6 +295,42 @@ int qlinear_supergroup_a8(const uint16_t* x, int32_t b, const uint32_t* p4, cons
                           const uint16_t* scales, int32_t rows, int32_t cols, int32_t period,
                           uint16_t* y, void* stream);
 
+/*
+ * Prerouter head of one layer ("Edge0 project review", highlight 1): f = [h (hidden),
+ * one-hot of the token's executed top-k (n_experts), one-hot of the previous token's top-k
+ * (n_experts)]; logits = linear_init(f) + fc2(gelu_erf(fc1(f))), every layer's output
+ * rounded to fp16 (fp32 accumulation).  Weights fp16, row-major [out][in], with biases:
+ *   w_init [n_experts][hidden + 2 n_experts], b_init [n_experts]
+ *   w1     [ffn][hidden + 2 n_experts],       b1 [ffn]
+ *   w2     [n_experts][ffn],                  b2 [n_experts]
+ */
+typedef struct qmoe_prerouter {
+    const uint16_t* w_init;
+    const uint16_t* b_init;
+    const uint16_t* w1;
+    const uint16_t* b1;
+    const uint16_t* w2;
+    const uint16_t* b2;
+    int32_t hidden;
+    int32_t n_experts;
+    int32_t ffn;
+} qmoe_prerouter;
+
+/*
+ * The head's forward for t tokens: h fp16 [t][hidden]; topk_now and topk_prev int32 [t][k]
+ * (the executed routing of each token and of its previous token; indices outside
+ * [0, n_experts) are clamped).  Outputs: act fp16 [t][ffn] = fp16(gelu_erf(fp16(fc1 f)))
+ * and logits fp32 [t][n_experts] holding the fp16-rounded head logits; when pred_idx is
+ * not NULL, also the predicted routing of the next layer: the top-k of the logits with
+ * router_topk's rule (lower index on ties) into pred_idx int32 [t][k] and pred_w fp32
+ * [t][k] (softmax over the k).  Supported: hidden % 512 == 0, hidden <= 8192,
+ * ffn % 512 == 0, n_experts % 4 == 0, n_experts <= 1024, 1 <= k <= 32, k <= n_experts,
+ * 1 <= t <= 4096; h, act and every weight 16-byte aligned.
+ */
+int prerouter_forward(const qmoe_prerouter* P, const uint16_t* h, int32_t t, int32_t k,
+                      const int32_t* topk_now, const int32_t* topk_prev, uint16_t* act,
+                      float* logits, int32_t* pred_idx, float* pred_w, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -17,6 +17,8 @@ from .api import (  # noqa: F401
     STAGE_ROUTE,
     MoELayer,
     QWeight,
+    PrerouterHead,
+    prerouter_forward,
     SuperGroupWeight,
     dequantize,
     lora_apply,

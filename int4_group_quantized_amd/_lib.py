@@ -33,6 +33,12 @@ class QWeightC(ctypes.Structure):
                 ("n_experts", ctypes.c_int32), ("param_dtype", ctypes.c_int32)]
 
 
+class PrerouterC(ctypes.Structure):
+    _fields_ = [("w_init", ctypes.c_void_p), ("b_init", ctypes.c_void_p), ("w1", ctypes.c_void_p),
+                ("b1", ctypes.c_void_p), ("w2", ctypes.c_void_p), ("b2", ctypes.c_void_p),
+                ("hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32), ("ffn", ctypes.c_int32)]
+
+
 class LoraC(ctypes.Structure):
     _fields_ = [("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("rank", ctypes.c_int32),
                 ("n_adapters", ctypes.c_int32), ("in_dim", ctypes.c_int32),
@@ -71,6 +77,7 @@ _SIGS = {
     "qmoe_quantize_supergroup": (ctypes.c_int, [_P, _I, _I, _I, _P, _P, _P, _P]),
     "qlinear_supergroup": (ctypes.c_int, [_P, _I, _P, _P, _P, _I, _I, _I, _P, _P]),
     "qmoe_quantize_act8": (ctypes.c_int, [_P, _I, _I, _P, _P, _P]),
+    "prerouter_forward": (ctypes.c_int, [ctypes.POINTER(PrerouterC), _P, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
     "qlinear_supergroup_a8": (ctypes.c_int, [_P, _I, _P, _P, _P, _I, _I, _I, _P, _P]),
 }
 EXPORTED = tuple(_SIGS)

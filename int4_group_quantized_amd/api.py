@@ -14,7 +14,7 @@ from typing import Optional
 import numpy as np
 import torch
 
-from ._lib import LoraC, MoELayerC, QWeightC, check, lib
+from ._lib import LoraC, MoELayerC, PrerouterC, QWeightC, check, lib
 
 
 def _stream(t: torch.Tensor) -> ctypes.c_void_p:
@@ -333,3 +333,43 @@ def qlinear_supergroup_a8(x: torch.Tensor, W: SuperGroupWeight,
                                     W.rows, W.cols, W.period, y.data_ptr(), _stream(x)),
           "qlinear_supergroup_a8")
     return y
+
+
+@dataclass
+class PrerouterHead:
+    """One layer's prerouter head on the device: fp16 weights [out, in] and biases;
+    w_init [E, D + 2E], w1 [F, D + 2E], w2 [E, F]."""
+
+    w_init: torch.Tensor
+    b_init: torch.Tensor
+    w1: torch.Tensor
+    b1: torch.Tensor
+    w2: torch.Tensor
+    b2: torch.Tensor
+
+    def c(self) -> PrerouterC:
+        E, F = self.w_init.shape[0], self.w1.shape[0]
+        D = self.w_init.shape[1] - 2 * E
+        for name in ("w_init", "b_init", "w1", "b1", "w2", "b2"):
+            _dev(getattr(self, name), torch.float16, name)
+        return PrerouterC(self.w_init.data_ptr(), self.b_init.data_ptr(), self.w1.data_ptr(),
+                          self.b1.data_ptr(), self.w2.data_ptr(), self.b2.data_ptr(), D, E, F)
+
+
+def prerouter_forward(P: PrerouterHead, h: torch.Tensor, topk_now: torch.Tensor,
+                      topk_prev: torch.Tensor, predict: bool = True):
+    """(act fp16 [t, F], logits fp32 [t, E], pred_idx int32 [t, k] or None, pred_w fp32 or
+    None) of the prerouter head for t tokens."""
+    _dev(h, torch.float16, "h")
+    _dev(topk_now, torch.int32, "topk_now")
+    _dev(topk_prev, torch.int32, "topk_prev")
+    t, k = topk_now.shape
+    c = P.c()
+    act = torch.empty((t, c.ffn), dtype=torch.float16, device=h.device)
+    logits = torch.empty((t, c.n_experts), dtype=torch.float32, device=h.device)
+    idx = torch.empty((t, k), dtype=torch.int32, device=h.device) if predict else None
+    w = torch.empty((t, k), dtype=torch.float32, device=h.device) if predict else None
+    check(lib.prerouter_forward(ctypes.byref(c), h.data_ptr(), t, k, topk_now.data_ptr(),
+                                topk_prev.data_ptr(), act.data_ptr(), logits.data_ptr(), _ptr(idx),
+                                _ptr(w), _stream(h)), "prerouter_forward")
+    return act, logits, idx, w

@@ -108,6 +108,7 @@ size_t qmoe_abi_struct_size(int which) {
         case 0: return sizeof(qmoe_qweight);
         case 1: return sizeof(qmoe_lora);
         case 2: return sizeof(qmoe_moe_layer);
+        case 3: return sizeof(qmoe_prerouter);
         default: return 0;
     }
 }
@@ -224,6 +225,24 @@ int qlinear_supergroup(const uint16_t* x, int32_t b, const uint32_t* p4, const u
         return QMOE_ERR_MISALIGNED;
     return hip_status(qmoe::launch_qlinear_supergroup(x, b, p4, p2, scales, rows, cols, period, y,
                                                       as_stream(stream)));
+}
+
+int prerouter_forward(const qmoe_prerouter* P, const uint16_t* h, int32_t t, int32_t k,
+                      const int32_t* topk_now, const int32_t* topk_prev, uint16_t* act,
+                      float* logits, int32_t* pred_idx, float* pred_w, void* stream) {
+    if (!P || !h || !topk_now || !topk_prev || !act || !logits || t <= 0 || k <= 0)
+        return QMOE_ERR_INVALID_ARG;
+    if (!P->w_init || !P->b_init || !P->w1 || !P->b1 || !P->w2 || !P->b2) return QMOE_ERR_INVALID_ARG;
+    if (P->hidden <= 0 || P->n_experts <= 0 || P->ffn <= 0) return QMOE_ERR_INVALID_ARG;
+    if ((pred_idx == nullptr) != (pred_w == nullptr)) return QMOE_ERR_INVALID_ARG;
+    if (P->hidden % 512 || P->hidden > 8192 || P->ffn % 512 || P->n_experts % 4 ||
+        P->n_experts > 1024 || k > 32 || k > P->n_experts || t > 4096)
+        return QMOE_ERR_UNSUPPORTED;
+    if (!aligned16(h) || !aligned16(act) || !aligned16(P->w_init) || !aligned16(P->w1) ||
+        !aligned16(P->w2))
+        return QMOE_ERR_MISALIGNED;
+    return hip_status(qmoe::launch_prerouter(*P, h, t, k, topk_now, topk_prev, act, logits,
+                                             pred_idx, pred_w, as_stream(stream)));
 }
 
 int qmoe_quantize_act8(const uint16_t* x, int32_t b, int32_t cols, int8_t* qx, uint16_t* sx,

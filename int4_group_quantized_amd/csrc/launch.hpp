@@ -46,6 +46,11 @@ hipError_t launch_qlinear_supergroup(const uint16_t* x, int b, const uint32_t* p
                                      const uint32_t* p2, const uint16_t* scales, int rows,
                                      int cols, int period, uint16_t* y, hipStream_t s);
 
+// prerouter.hip
+hipError_t launch_prerouter(const qmoe_prerouter& P, const uint16_t* h, int t, int k,
+                            const int32_t* now, const int32_t* prev, uint16_t* act,
+                            float* logits, int32_t* pred_idx, float* pred_w, hipStream_t s);
+
 // supergroup_a8.hip
 hipError_t launch_quantize_act8(const uint16_t* x, int b, int cols, int8_t* qx, uint16_t* sx,
                                 hipStream_t s);

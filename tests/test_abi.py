@@ -29,7 +29,7 @@ def test_header_declares_the_four_calls():
 def test_every_declared_function_is_exported():
     lib = ctypes.CDLL(q.LIB_PATH)
     names = declared_functions()
-    assert len(names) == 17
+    assert len(names) == 18
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.EXPORTED)
@@ -42,6 +42,7 @@ def test_version_status_and_struct_layout():
     assert q.lib.qmoe_abi_struct_size(0) == ctypes.sizeof(_lib.QWeightC)
     assert q.lib.qmoe_abi_struct_size(1) == ctypes.sizeof(_lib.LoraC)
     assert q.lib.qmoe_abi_struct_size(2) == ctypes.sizeof(_lib.MoELayerC)
+    assert q.lib.qmoe_abi_struct_size(3) == ctypes.sizeof(_lib.PrerouterC)
     assert q.lib.qmoe_abi_struct_size(7) == 0
 
 
@@ -174,3 +175,18 @@ def test_integer_path_rejects_bad_arguments():
     assert g(FAKE, 1, FAKE, FAKE, FAKE, 3072, 1000, 4, FAKE * 4, None) == _lib.QMOE_ERR_UNSUPPORTED
     assert g(FAKE, 5000, FAKE, FAKE, FAKE, 3072, 1024, 4, FAKE * 4, None) == _lib.QMOE_ERR_UNSUPPORTED
     assert g(FAKE + 8, 1, FAKE, FAKE, FAKE, 3072, 1024, 4, FAKE * 4, None) == _lib.QMOE_ERR_MISALIGNED
+
+
+def test_prerouter_rejects_bad_arguments():
+    f = q.lib.prerouter_forward
+    P = _lib.PrerouterC(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2048, 256, 512)
+    X, A, L = FAKE * 2, FAKE * 4, FAKE * 8
+    assert f(None, X, 1, 4, FAKE, FAKE, A, L, None, None, None) == _lib.QMOE_ERR_INVALID_ARG
+    assert f(ctypes.byref(P), X, 0, 4, FAKE, FAKE, A, L, None, None, None) == _lib.QMOE_ERR_INVALID_ARG
+    assert f(ctypes.byref(P), X, 1, 4, FAKE, FAKE, A, L, FAKE, None, None) == _lib.QMOE_ERR_INVALID_ARG
+    assert f(ctypes.byref(P), X, 1, 33, FAKE, FAKE, A, L, None, None, None) == _lib.QMOE_ERR_UNSUPPORTED
+    for bad in (_lib.PrerouterC(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2000, 256, 512),
+                _lib.PrerouterC(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2048, 254, 512),
+                _lib.PrerouterC(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2048, 256, 500)):
+        assert f(ctypes.byref(bad), X, 1, 4, FAKE, FAKE, A, L, None, None, None) == _lib.QMOE_ERR_UNSUPPORTED
+    assert f(ctypes.byref(P), X + 2, 1, 4, FAKE, FAKE, A, L, None, None, None) == _lib.QMOE_ERR_MISALIGNED
