@@ -16,7 +16,8 @@ Other workloads (--workload): gemv (one int4 linear, x [1 x 2048], W [512 x 2048
 moe_prefill (512 tokens, top-4; --skew adds +2.0 to the logits of experts 0..15),
 moe_stack (40 stacked layers, 16 tokens per step, top-8, 4 LoRA adapter sets),
 supergroup (mixed ternary/4-bit GEMM, W [3072 x 1024], --batch 1 or 64), supergroup_a8
-(the same GEMM with 8-bit activations and an integer dot product).
+(the same GEMM with 8-bit activations and an integer dot product), prerouter (one prerouter
+head forward per token).
 
 Prints one JSON line: the metric, a roofline object for the dominant kernel (algorithmic
 bytes per launch over its average launch time, measured here with HIP events on the stream
@@ -566,10 +567,64 @@ def bench_gemv(args, q, torch):
     return res, None
 
 
+def bench_prerouter(args, q, torch):
+    """One prerouter head forward per decode token (hidden 2048, 256 experts, head width 512,
+    top-4), rotating over 128 independently drawn heads (540 MB, twice the 256 MB cache)."""
+    D, E, F, k, HEADS = 2048, 256, 512, 4, 128
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4242)
+    n = D + 2 * E
+    rnd = lambda *s: (torch.randn(s, generator=gen, device="cuda") * 0.02).half()
+    heads = [q.PrerouterHead(rnd(E, n), rnd(E), rnd(F, n), rnd(F), rnd(E, F), rnd(E)) for _ in range(HEADS)]
+    K, W = args.steps, args.warmup
+    hs = torch.randn((K + W, 1, D), generator=gen, device="cuda").half()
+    rt = torch.stack([torch.randperm(E, generator=gen, device="cuda")[:2 * k] for _ in range(K + W)]).int()
+    now, prev = rt[:, None, :k].contiguous(), rt[:, None, k:].contiguous()
+    cs = [heads[i % HEADS].c() for i in range(HEADS)]
+    act = torch.empty((K + W, 1, F), dtype=torch.float16, device="cuda")
+    logits = torch.empty((K + W, 1, E), dtype=torch.float32, device="cuda")
+    idx = torch.empty((K + W, 1, k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((K + W, 1, k), dtype=torch.float32, device="cuda")
+    import ctypes
+    from int4_group_quantized_amd._lib import check
+
+    def run(lo, hi):
+        def f():
+            st = torch.cuda.current_stream().cuda_stream
+            for i in range(lo, hi):
+                check(q.lib.prerouter_forward(ctypes.byref(cs[i % HEADS]), hs[i].data_ptr(), 1, k,
+                                              now[i].data_ptr(), prev[i].data_ptr(), act[i].data_ptr(),
+                                              logits[i].data_ptr(), idx[i].data_ptr(), wts[i].data_ptr(),
+                                              st), "prerouter_forward")
+        return f
+    if W:
+        graph_of(torch, run(K, K + W)).replay()
+    g = graph_of(torch, run(0, K))
+    ms = time_graph(torch, g)
+    us = ms / K * 1e3
+    # algorithmic bytes: the dense parts of the fc1 and linear_init rows, the 2k gathered
+    # one-hot columns of each, fc2, the biases, h in, act out and in, logits out and in, the
+    # routing in and out
+    bytes_ = ((F + E) * D * 2 + (F + E) * 2 * k * 2 + E * F * 2 + (F + 2 * E) * 2 + D * 2
+              + 2 * F * 2 + 3 * E * 4 + 2 * k * 4 + 2 * k * 4)
+    ach = bytes_ / (us * 1e-6) / 1e9
+    res = {"metric": "prerouter head forwards/s (decode, 1 token)", "value": K / (ms * 1e-3),
+           "unit": "calls/s", "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": ms / K,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+           "data": "synthetic",
+           "config": {"workload": f"prerouter_forward h[1x{D}], {E} experts, head width {F}, top-{k}, "
+                                  f"{HEADS} heads rotated"},
+           "roofline": {"kernel": "whole call (k_pr_fc1, k_pr_fc2, k_router_topk)", "bound": "hbm",
+                        "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": ach / HBM_PEAK_GBS, "traffic": None, "bytes_per_launch": bytes_,
+                        "us_per_launch": us}}
+    return res, None
+
+
 WORKLOADS = {"moe_decode": bench_moe_decode, "moe_prefill": bench_moe_prefill,
              "moe_stack": bench_moe_stack, "supergroup": bench_supergroup,
              "supergroup_a8": lambda args, q, torch: bench_supergroup(args, q, torch, a8=True),
-             "gemv": bench_gemv}
+             "gemv": bench_gemv, "prerouter": bench_prerouter}
 
 
 def main():

@@ -49,7 +49,11 @@ __device__ __forceinline__ float dot8(const uint4& w, const uint4& x, float acc)
 
 __device__ __forceinline__ float gelu_erf(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
 
+constexpr int PR_U = 4;    // 16-byte weight units per lane held in registers (D <= 2048)
+
 // P1: rows [0, F) are fc1, rows [F, F + E) linear_init.  h of up to PR_MT tokens in LDS.
+// For D <= 2048 (one pass of tokens at a time) the row's weights and the first tokens'
+// routing indices are loaded before h is staged, so those round trips overlap.
 __global__ void __launch_bounds__(256) k_pr_fc1(PrArgs a) {
     __shared__ __align__(16) uint4 hs[1024];   // mt_max tokens x D inputs <= 8192 halves
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -61,6 +65,11 @@ __global__ void __launch_bounds__(256) k_pr_fc1(PrArgs a) {
     const int rr = min(row, rows - 1);
     const uint16_t* wrow = fc1 ? a.w1 + (long)rr * n : a.wi + (long)(rr - a.F) * n;
     const float bias = h2f(fc1 ? a.b1[rr] : a.bi[rr - a.F]);
+    const bool held = units <= 64 * PR_U;
+    uint4 wr[PR_U];
+#pragma unroll
+    for (int i = 0; i < PR_U; ++i)   // unconditional (clamped) loads: no branch around them
+        wr[i] = reinterpret_cast<const uint4*>(wrow)[min(lane + 64 * i, units - 1)];
     for (int t0 = 0; t0 < a.T; t0 += mt_max) {
         const int mt = min(mt_max, a.T - t0);
         __syncthreads();
@@ -70,11 +79,23 @@ __global__ void __launch_bounds__(256) k_pr_fc1(PrArgs a) {
         float acc[PR_MT];
 #pragma unroll
         for (int t = 0; t < PR_MT; ++t) acc[t] = 0.0f;
-        for (int c = lane; c < units; c += 64) {
-            const uint4 w = reinterpret_cast<const uint4*>(wrow)[c];
+        if (held) {
 #pragma unroll
-            for (int t = 0; t < PR_MT; ++t)
-                if (t < mt) acc[t] = dot8(w, hs[t * units + c], acc[t]);
+            for (int i = 0; i < PR_U; ++i) {
+                const int c = lane + 64 * i;
+                if (c < units) {
+#pragma unroll
+                    for (int t = 0; t < PR_MT; ++t)
+                        if (t < mt) acc[t] = dot8(wr[i], hs[t * units + c], acc[t]);
+                }
+            }
+        } else {
+            for (int c = lane; c < units; c += 64) {
+                const uint4 w = reinterpret_cast<const uint4*>(wrow)[c];
+#pragma unroll
+                for (int t = 0; t < PR_MT; ++t)
+                    if (t < mt) acc[t] = dot8(w, hs[t * units + c], acc[t]);
+            }
         }
         // the one-hot parts: lane j < K gathers this token's expert j, K <= j < 2K the
         // previous token's (indices clamped into [0, E))
