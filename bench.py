@@ -127,6 +127,19 @@ def time_graph(torch, g, reps=1):
 
 # ------------------------------------------------------------------------------ CPU baseline
 
+def host_desc():
+    """The host CPU model and the number of CPUs this process may run on."""
+    model = "unknown CPU"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return f"{model}, {len(os.sched_getaffinity(0))} CPUs available"
+
+
 def cpu_baseline_moe_decode(n_tokens=600, budget_s=20.0):
     """The oracle (float64 numpy) on a bounded sample: n_tokens single-token decodes of one
     seeded layer of the same shapes; only the experts those tokens reach are quantized."""
@@ -150,7 +163,7 @@ def cpu_baseline_moe_decode(n_tokens=600, budget_s=20.0):
     dt = time.perf_counter() - t0
     blas = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
     cores = max(blas) if blas else 1
-    return {"value": done / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+    return {"value": done / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle", "host": host_desc(),
             "sample": f"{done} single-token decodes of one layer (hidden 2048, 256 experts, "
                       f"top-4, shared expert, LoRA r16), float64 numpy, {dt:.1f} s"}
 
@@ -251,7 +264,7 @@ def cpu_baseline_moe_prefill(n_tokens=64, budget_s=20.0):
     dt = time.perf_counter() - t0
     blas = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
     cores = max(blas) if blas else 1
-    return {"value": done / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+    return {"value": done / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle", "host": host_desc(),
             "sample": f"{done} prefill tokens in batches of 16 through one layer (hidden 2048, "
                       f"256 experts, top-4, shared expert, LoRA r16), float64 numpy, {dt:.1f} s"}
 
@@ -370,7 +383,7 @@ def cpu_baseline_moe_stack(n_layers=2, budget_s=25.0):
     blas = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
     cores = max(blas) if blas else 1
     per_step = spent / done * LAYERS
-    return {"value": 16 / per_step, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+    return {"value": 16 / per_step, "unit": "tokens/s", "cores": int(cores), "kind": "oracle", "host": host_desc(),
             "sample": f"16 tokens (4 adapters) through {done} of the 40 layers, float64 numpy, "
                       f"{spent:.1f} s, scaled to 40 layers"}
 
@@ -469,7 +482,7 @@ def cpu_baseline_supergroup(batch, budget_s=15.0, a8=False):
     dt = time.perf_counter() - t0
     blas = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
     return {"value": n * batch / dt, "unit": "tokens/s", "cores": int(max(blas) if blas else 1),
-            "kind": "oracle", "sample": f"{n} {'8-bit activation ' if a8 else ''}GEMMs of W[3072x1024] "
+            "kind": "oracle", "host": host_desc(), "sample": f"{n} {'8-bit activation ' if a8 else ''}GEMMs of W[3072x1024] "
                                         f"with {batch} inputs, float64/int64 numpy, {dt:.1f} s"}
 
 
