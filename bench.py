@@ -536,6 +536,62 @@ def bench_supergroup(args, q, torch, a8=False):
     return res, (lambda: cpu_baseline_supergroup(B, a8=a8))
 
 
+def _threads():
+    from threadpoolctl import threadpool_info
+    blas = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+    return int(max(blas) if blas else 1)
+
+
+def cpu_baseline_gemv(group=64, bf16=False, budget_s=10.0):
+    """The oracle (float64 numpy) on a bounded sample: int4 linears x[1x2048] W[512x2048] of one
+    seeded weight, repeated until the budget is spent."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import synth
+    from oracle import affine, moe
+
+    w = synth.normal_f32((512, 2048), synth.WEIGHT_SIGMA, synth.Workload.GEMV, 0, synth.Role.DENSE)
+    W_ = affine.quantize(w, 4, group, "bf16" if bf16 else "f16")
+    x = synth.activations(1, 2048, synth.Workload.GEMV)
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < budget_s:
+        moe.to_f16(moe.qlinear(x, W_))
+        n += 1
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "calls/s", "cores": _threads(), "kind": "oracle", "host": host_desc(),
+            "sample": f"{n} calls of x[1x2048] W[512x2048] int4 g{group}, float64 numpy, {dt:.1f} s"}
+
+
+def cpu_baseline_prerouter(budget_s=10.0):
+    """The oracle on a bounded sample: prerouter head forwards of one token (hidden 2048, 256
+    experts, head width 512, top-4) with one seeded head."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import numpy as np
+    import synth
+    from oracle import moe
+    from oracle import prerouter as pr
+
+    D, E, F, k = 2048, 256, 512, 4
+    R_ = synth.Role.MISC
+    W_ = synth.Workload.TEST
+    n_in = D + 2 * E
+    P = pr.PrerouterHead(synth.normal_f16((E, n_in), 0.02, W_, 0, R_, 0), synth.normal_f16((E,), 0.02, W_, 0, R_, 1),
+                         synth.normal_f16((F, n_in), 0.02, W_, 0, R_, 2), synth.normal_f16((F,), 0.02, W_, 0, R_, 3),
+                         synth.normal_f16((E, F), 0.05, W_, 0, R_, 4), synth.normal_f16((E,), 0.02, W_, 0, R_, 5))
+    h = synth.activations(1, D, W_, 0)
+    g = np.random.default_rng(0)
+    now, prev = g.choice(E, (1, k), replace=False), g.choice(E, (1, k), replace=False)
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < budget_s:
+        _, lg = pr.forward(P, h, now, prev)
+        moe.topk(lg.astype(np.float64), k)
+        n += 1
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "calls/s", "cores": _threads(), "kind": "oracle", "host": host_desc(),
+            "sample": f"{n} one-token head forwards + top-4, float64 numpy, {dt:.1f} s"}
+
+
 def bench_gemv(args, q, torch):
     gen = torch.Generator(device="cuda")
     gen.manual_seed(1234)
@@ -577,7 +633,7 @@ def bench_gemv(args, q, torch):
            "roofline": {"kernel": f"k_qgemv_fast<4,{G},{'bf16' if bf else 'f16'}>", "bound": "hbm", "achieved": ach,
                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
                         "traffic": None, "bytes_per_launch": bytes_, "us_per_launch": ms / K * 1e3}}
-    return res, None
+    return res, (lambda: cpu_baseline_gemv(G, bf))
 
 
 def bench_prerouter(args, q, torch):
@@ -631,7 +687,7 @@ def bench_prerouter(args, q, torch):
                         "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": ach / HBM_PEAK_GBS, "traffic": None, "bytes_per_launch": bytes_,
                         "us_per_launch": us}}
-    return res, None
+    return res, cpu_baseline_prerouter
 
 
 WORKLOADS = {"moe_decode": bench_moe_decode, "moe_prefill": bench_moe_prefill,
