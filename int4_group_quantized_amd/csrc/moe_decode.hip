@@ -9,11 +9,12 @@
 //   D1 x-side  : router logits (8-bit), shared-gate logit (8-bit), the shared expert's raw
 //                gate/up projections (int4), LoRA z = A x.  Each wave issues its weight
 //                loads before staging x, so the two memory round trips overlap.
-//   D2 gate/up : one block per (row block, routed pair (t, k) or the shared expert).  Wave
-//                0 reads token t's logits and takes its top-K (the same deterministic
-//                selection in every block); the other waves stage x meanwhile.  Then the
-//                gate and up rows of expert idx[t][k] are streamed and h = silu(g) * u is
-//                stored (fp16).  Shared blocks add the LoRA up-projections and store h_s.
+//   D2 gate/up : one block per (row block, routed pair (t, k) or the shared expert).  Every
+//                wave reads token t's logits and takes the selection up to round k (the
+//                same deterministic selection in every block), so it issues the gate and up
+//                rows of expert idx[t][k] before x is staged and the block synchronises;
+//                then h = silu(g) * u is stored (fp16).  Shared blocks add the LoRA
+//                up-projections and store h_s.
 //   D3 down    : one block per (row block, token).  It recomputes the token's top-K,
 //                stages the token's K expert activations h and h_s, computes the shared
 //                expert's LoRA z_down, streams the K + 1 down matrices' rows, and combines
@@ -143,23 +144,16 @@ __global__ void __launch_bounds__(256) k_dec_gate_up(MoeArgs a) {
     __shared__ int sel[MAX_K];
     __shared__ float selw[MAX_K];
     TopkKeys<PER> keys;
-    if (wave == 0) keys.load(a.logits + (long)t * a.Ep, a.rbias, a.E);
+    keys.load(a.logits + (long)t * a.Ep, a.rbias, a.E);
     const uint4* xt = reinterpret_cast<const uint4*>(a.x + (long)t * H);
     StageRegs<4, 2> st;
     st.load([=](int) { return xt; }, 1, H);
     __builtin_amdgcn_sched_barrier(0);
-    // phase 2: wave 0 takes the top-K while the others write x to LDS
-    if (wave == 0) keys.select(a.E, K, sel, selw);
-    st.commit(1, H, xs, xsum);
-    __syncthreads();
-    const int e = sel[k];
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-        // publish the decision for the down stage and the caller
-        a.idx[pair] = e;
-        a.wts[pair] = selw[k];
-        if (a.idx_out) a.idx_out[pair] = e;
-        if (a.w_out) a.w_out[pair] = selw[k];
-    }
+    // phase 2: every wave takes the selection up to its pair's round k itself and issues its
+    // weight loads at once, before x goes to LDS and the barrier; the first row block's wave 0
+    // also takes the whole top-K, to publish it
+    if (blockIdx.x == 0 && wave == 0) keys.select(a.E, K, sel, selw);
+    const int e = keys.pick(a.E, k);
     RowRegs<4, 2> rg[GU_RPW], ru[GU_RPW];
     int n[GU_RPW];
 #pragma unroll
@@ -169,6 +163,15 @@ __global__ void __launch_bounds__(256) k_dec_gate_up(MoeArgs a) {
         const long row = (long)e * I + (ok ? n[j] : 0);
         rg[j].load(a.eg.p, a.eg.s, a.eg.b, H, row, lpr, sl, ok);
         ru[j].load(a.eu.p, a.eu.s, a.eu.b, H, row, lpr, sl, ok);
+    }
+    st.commit(1, H, xs, xsum);
+    __syncthreads();
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        // publish the decision for the down stage and the caller
+        a.idx[pair] = e;
+        a.wts[pair] = selw[k];
+        if (a.idx_out) a.idx_out[pair] = e;
+        if (a.w_out) a.w_out[pair] = selw[k];
     }
 #pragma unroll
     for (int j = 0; j < GU_RPW; ++j) {

@@ -59,10 +59,10 @@ struct TopkKeys {
     // index with that key, and lane l holds indices l*PER .. l*PER + PER - 1, so the round picks
     // the lowest index of the largest key.  The winner drops its head.  Lane r keeps round r's
     // expert and key, and the k weights are taken in parallel at the end.
-    __device__ void select(int e, int k, int* sel, float* w) const {
+    // This lane's keys sorted descending (order-preserving float bits, 0: no entry) with
+    // their indices.
+    __device__ __forceinline__ void sorted(int e, uint32_t (&kv)[PER], int (&ki)[PER]) const {
         const int lane = threadIdx.x & 63;
-        uint32_t kv[PER];   // keys (order-preserving float bits; 0: no entry)
-        int ki[PER];        // their indices
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const bool ok = lane * PER + i < e;
@@ -79,28 +79,55 @@ struct TopkKeys {
                 kv[i] = sw ? kb : ka; kv[i + 1] = sw ? ka : kb;
                 ki[i] = sw ? ib : ia; ki[i + 1] = sw ? ia : ib;
             }
+    }
+
+    // One round: the lowest index holding the largest head key (returned in every lane, its
+    // key in `best`); the winning lane drops its head.
+    __device__ __forceinline__ int round(uint32_t (&kv)[PER], int (&ki)[PER], uint32_t& best) const {
+        const int lane = threadIdx.x & 63;
+        uint32_t m = kv[0];
+        m = max(m, dpp_u<DPP_XOR1>(m));
+        m = max(m, dpp_u<DPP_XOR2>(m));
+        m = max(m, dpp_u<DPP_HALF_MIRROR>(m));
+        m = max(m, dpp_u<DPP_MIRROR>(m));
+        const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)m, 0);
+        const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)m, 16);
+        const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)m, 32);
+        const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)m, 48);
+        best = max(max(r0, r1), max(r2, r3));
+        const int lw = __builtin_ctzll(__ballot(kv[0] == best));   // the lowest lane holding it
+        const int idx = __builtin_amdgcn_readlane(ki[0], lw);
+        const bool win = lane == lw;
+#pragma unroll
+        for (int i = 0; i + 1 < PER; ++i) {
+            kv[i] = win ? kv[i + 1] : kv[i];
+            ki[i] = win ? ki[i + 1] : ki[i];
+        }
+        kv[PER - 1] = win ? 0u : kv[PER - 1];
+        return idx;
+    }
+
+    // The expert chosen in round k alone (the same in every lane): rounds 0 .. k, no weights.
+    __device__ int pick(int e, int k) const {
+        uint32_t kv[PER];
+        int ki[PER];
+        sorted(e, kv, ki);
+        int idx = 0;
+        uint32_t best;
+        for (int r = 0; r <= k; ++r) idx = round(kv, ki, best);
+        return idx;
+    }
+
+    __device__ void select(int e, int k, int* sel, float* w) const {
+        const int lane = threadIdx.x & 63;
+        uint32_t kv[PER];
+        int ki[PER];
+        sorted(e, kv, ki);
         int my_idx = 0;
         uint32_t my_key = 0u;
         for (int r = 0; r < k; ++r) {
-            uint32_t m = kv[0];
-            m = max(m, dpp_u<DPP_XOR1>(m));
-            m = max(m, dpp_u<DPP_XOR2>(m));
-            m = max(m, dpp_u<DPP_HALF_MIRROR>(m));
-            m = max(m, dpp_u<DPP_MIRROR>(m));
-            const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)m, 0);
-            const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)m, 16);
-            const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)m, 32);
-            const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)m, 48);
-            const uint32_t best = max(max(r0, r1), max(r2, r3));
-            const int lw = __builtin_ctzll(__ballot(kv[0] == best));   // the lowest lane holding it
-            const int idx = __builtin_amdgcn_readlane(ki[0], lw);
-            const bool win = lane == lw;
-#pragma unroll
-            for (int i = 0; i + 1 < PER; ++i) {
-                kv[i] = win ? kv[i + 1] : kv[i];
-                ki[i] = win ? ki[i + 1] : ki[i];
-            }
-            kv[PER - 1] = win ? 0u : kv[PER - 1];
+            uint32_t best;
+            const int idx = round(kv, ki, best);
             if (lane == r) { my_idx = idx; my_key = best; }
         }
         // softmax over the k chosen keys, relative to the largest (round 0's, held by lane 0)
