@@ -11,7 +11,8 @@ Precision policy
 ----------------
 * Matmuls, LoRA deltas, activations and routing weights are evaluated in float64 from the
   exact dequantized weights (``scale * q + bias`` is exact in float64 for fp16 scale/bias
-  and integer codes), so the oracle is the definition of the layer up to float64 rounding.
+  and integer codes, and for bf16 ones checked per matrix), so the oracle is the definition
+  of the layer up to float64 rounding; integer dot products are exact (int64).
 * Where a floating-point value *decides an integer* (a quantized code, a scale that later
   decides codes), the oracle takes that decision in float32, the precision of the kernel,
   with every operation spelled out in IEEE float32 (numpy float32 arrays, no contraction).
@@ -19,11 +20,14 @@ Precision policy
 
 Modules
 -------
-``affine``      group-wise affine quantize / pack / unpack / dequantize (4- and 8-bit).
+``affine``      group-wise affine quantize / pack / unpack / dequantize (4- and 8-bit; group
+                64 or 32; fp16 or bf16 scale and bias).
 ``moe``         quantized linear, LoRA delta, router + top-K, experts, shared expert, layer,
                 layer stack.
-``supergroup``  mixed ternary / 4-bit super-group quantizer, packing and weight-only GEMM.
+``supergroup``  mixed ternary / 4-bit super-group quantizer, packing, the weight-only GEMM
+                and the 8-bit-activation integer path.
+``prerouter``   the prerouter head's forward (the next layer's predicted routing).
 
 Functions with no independent pin are marked "parity unpinned" in their docstrings.
 """
-from . import affine, moe, supergroup  # noqa: F401
+from . import affine, moe, prerouter, supergroup  # noqa: F401
