@@ -190,3 +190,20 @@ def test_prerouter_rejects_bad_arguments():
                 _lib.PrerouterC(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2048, 256, 500)):
         assert f(ctypes.byref(bad), X, 1, 4, FAKE, FAKE, A, L, None, None, None) == _lib.QMOE_ERR_UNSUPPORTED
     assert f(ctypes.byref(P), X + 2, 1, 4, FAKE, FAKE, A, L, None, None, None) == _lib.QMOE_ERR_MISALIGNED
+
+
+def test_header_is_plain_c(tmp_path):
+    """include/qmoe.h is a C header: a C99 translation unit that includes it and takes the
+    address of every declared function compiles with gcc (no C++ or HIP types leak in)."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    src = tmp_path / "abi.c"
+    refs = "\n".join(f"    (entry)&{n}," for n in declared_functions())
+    src.write_text('#include "qmoe.h"\ntypedef void (*entry)(void);\nentry qmoe_entry_points[] = {\n'
+                   + refs + "\n};\n")
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-pedantic", "-I",
+                        os.path.dirname(HEADER), "-c", str(src), "-o", str(tmp_path / "abi.o")],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
