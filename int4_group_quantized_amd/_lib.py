@@ -91,7 +91,7 @@ def _load():
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
-    for which, cls in enumerate((QWeightC, LoraC, MoELayerC)):
+    for which, cls in enumerate((QWeightC, LoraC, MoELayerC, PrerouterC)):
         if lib.qmoe_abi_struct_size(which) != ctypes.sizeof(cls):
             raise ImportError(f"ABI struct {cls.__name__} size mismatch with {LIB_PATH}")
     return lib

@@ -207,3 +207,20 @@ def test_header_is_plain_c(tmp_path):
                         os.path.dirname(HEADER), "-c", str(src), "-o", str(tmp_path / "abi.o")],
                        capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
+
+
+def test_package_fails_loudly_without_the_library(tmp_path):
+    """With the built library absent the package does not import (no CPU or oracle fallback):
+    a copy of the Python sources without libqmoe.so raises ImportError on import."""
+    import shutil
+    import subprocess
+    import sys
+    pkg = os.path.dirname(q.__file__)
+    dst = tmp_path / "int4_group_quantized_amd"
+    dst.mkdir()
+    for f in os.listdir(pkg):
+        if f.endswith(".py"):
+            shutil.copy(os.path.join(pkg, f), dst / f)
+    r = subprocess.run([sys.executable, "-c", "import int4_group_quantized_amd"], cwd=tmp_path,
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0 and "ImportError" in r.stderr and "not built" in r.stderr
