@@ -17,7 +17,7 @@
 // inputs 1, 3, 5, 7; 2-bit: (w >> 2e) & 0x03030303 holds inputs e, e + 4, e + 8, e + 12).
 //   * few tokens (<= 8): one wave per output channel, v_dot4_i32_i8 over 4-byte groups;
 //   * more tokens, inputs a multiple of 1024: v_mfma_i32_16x16x64_i8 with 16 tokens as A
-//     (from LDS) and 16 channels of one kind as B (unpacked in registers), 64 channels and
+//     (from LDS) and 16 channels of one kind as B (unpacked in registers), 128 channels and
 //     16 tokens per block.
 #include <algorithm>
 
@@ -33,7 +33,7 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 constexpr int A8_MT = 8;          // tokens per pass of the few-token kernel
 constexpr int A8_CHUNK = 1024;    // inputs staged per pass of the MFMA kernel
 constexpr int A8_PITCH = A8_CHUNK + 16;   // LDS row pitch in bytes (16-byte reads spread over the banks)
-constexpr int A8_WAVES = 4;       // waves per block of the MFMA kernel (16 channels each)
+constexpr int A8_WAVES = 8;       // waves per block of the MFMA kernel (16 channels each)
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -230,8 +230,8 @@ __device__ __forceinline__ float amax16(const uint4& r0, const uint4& r1) {
 // stages tokens w, w + A8_WAVES, ... (a 1024-input chunk of a row is one 16-input unit per
 // lane), so each wave holds whole rows: a row's scale is a wave maximum over values already
 // in registers (one pass over the inputs when they fit one chunk) and its code sum a wave
-// sum.  Every block codes its 16 tokens itself (wider blocks, which would repeat that work
-// less often, stream more weight bytes through each CU and measured slower).
+// sum.  Every block codes its 16 tokens itself; 8 waves halve that repeated work against 4
+// (7.9 -> 7.6 us at 64 tokens), 16 waves stream too many weight bytes through one CU.
 template <bool FOUR>
 __device__ __forceinline__ void sg_a8_mfma_block(const uint16_t* __restrict__ x, int nb, int K,
                                                  int rows, int period,
