@@ -241,7 +241,7 @@ def bench_moe_decode(args, q, torch):
     return res, cpu_baseline_moe_decode
 
 
-def cpu_baseline_moe_prefill(n_tokens=64, budget_s=20.0):
+def cpu_baseline_moe_prefill(n_tokens=448, budget_s=20.0):
     """The oracle (float64 numpy) on a bounded sample: batches of 16 prefill tokens through
     one seeded layer of the same shapes (every expert the sample reaches is quantized)."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
