@@ -28,6 +28,12 @@ Modules
                 and the 8-bit-activation integer path.
 ``prerouter``   the prerouter head's forward (the next layer's predicted routing).
 
-Functions with no independent pin are marked "parity unpinned" in their docstrings.
+Every function here is pinned by a CPU test that does not take its expected value from the
+function itself (closed forms, hand-worked values, exact integer arithmetic, brute force,
+library routines, or the same function written another way).  The pages print no worked
+value of a whole layer, so the layer's composition is pinned through its parts: the shared
+expert and its gate by hand-worked constant-matrix examples and torch modules with the
+adapters merged in (``tests/test_oracle_shared_expert.py``), the routed part by the dense
+SwiGLU, identical-expert and per-pair recomputation identities.
 """
 from . import affine, moe, prerouter, supergroup  # noqa: F401

@@ -291,3 +291,24 @@ def test_residual_rounds_once():
     b = np.array([[2.0 ** -11, 1.0, 0.25]], np.float16)
     # 1 + 2^-11 is a tie -> even (1.0); 2048 + 1 is a tie -> even (2048); exact otherwise
     assert moe.residual(a, b).tolist() == [[1.0, 2048.0, -0.25]]
+
+
+def test_given_selection_equal_to_topk_reproduces_topk_weights():
+    """moe_layer(idx=...) with the router's own top-K as the given selection reproduces
+    topk's indices, weights and output exactly; another given set gets the full softmax
+    (scipy) restricted to that set and renormalized."""
+    L = small_layer(E=8, K=3)
+    x = synth.activations(6, 128, W)
+    own = moe.moe_layer(x, L)
+    given = moe.moe_layer(x, L, idx=own["idx"])
+    assert np.array_equal(given["idx"], own["idx"])
+    assert np.array_equal(given["w"], own["w"])
+    assert np.array_equal(given["y64"], own["y64"])
+    alt = np.array([[7, 0, 3]] * 6, np.int32)
+    out = moe.moe_layer(x, L, idx=alt)
+    p = scipy.special.softmax(out["logits"], axis=1)[:, [7, 0, 3]]
+    np.testing.assert_allclose(out["w"], p / p.sum(axis=1, keepdims=True), rtol=1e-13)
+    for t in range(6):
+        acc = sum(out["w"][t, k] * moe.expert_mlp(x[t:t + 1], L.exp_gate.expert(e), L.exp_up.expert(e),
+                                                   L.exp_down.expert(e))[0] for k, e in enumerate([7, 0, 3]))
+        np.testing.assert_allclose(out["routed"][t], acc, rtol=1e-12, atol=1e-15)
