@@ -43,8 +43,10 @@
  *    NaN/Inf inputs give undefined (but memory-safe) results.
  *  - Determinism: no atomics on any reduction path; identical inputs give bit-identical
  *    outputs on the same device.
- *  - Alignment: every weight, activation and output pointer must be 16-byte aligned
- *    (QMOE_ERR_MISALIGNED otherwise).
+ *  - Alignment (QMOE_ERR_MISALIGNED otherwise): the packed words, scales and biases of
+ *    every quantized matrix handed to a GEMV/GEMM entry point, LoRA A and B, activations
+ *    and fp16 outputs must be 16-byte aligned; the MoE workspace 256-byte aligned; int32 and
+ *    fp32 index, weight and bias arrays 4-byte aligned.
  */
 #ifndef QMOE_H
 #define QMOE_H
@@ -61,7 +63,7 @@ extern "C" {
 #define QMOE_OK 0
 #define QMOE_ERR_INVALID_ARG (-1) /* NULL pointer, non-positive or inconsistent size   */
 #define QMOE_ERR_UNSUPPORTED (-2) /* bits/group/shape outside what the kernels support */
-#define QMOE_ERR_MISALIGNED (-3)  /* a pointer is not 16-byte aligned                  */
+#define QMOE_ERR_MISALIGNED (-3)  /* a pointer is not aligned as required below       */
 #define QMOE_ERR_WORKSPACE (-4)   /* workspace NULL or smaller than required           */
 #define QMOE_ERR_HIP (-5)         /* a kernel launch failed                            */
 
@@ -158,7 +160,8 @@ int qmoe_abi_version(void);
 const char* qmoe_status_string(int status);
 
 /* sizeof of the ABI structs as compiled into the library, for bindings to check their
- * own layout: which = 0 qmoe_qweight, 1 qmoe_lora, 2 qmoe_moe_layer; 0 otherwise. */
+ * own layout: which = 0 qmoe_qweight, 1 qmoe_lora, 2 qmoe_moe_layer, 3 qmoe_prerouter;
+ * 0 otherwise. */
 size_t qmoe_abi_struct_size(int which);
 
 /* Text of the HIP error behind the calling thread's most recent QMOE_ERR_HIP ("" if none).

@@ -8,7 +8,7 @@ there is no CPU path.
 from __future__ import annotations
 
 import ctypes
-from dataclasses import dataclass, field
+from dataclasses import dataclass
 from typing import Optional
 
 import numpy as np
@@ -55,7 +55,24 @@ class QWeight:
     group: int = 64
     param_dtype: int = 0
 
+    def check(self) -> None:
+        """The tensors must hold exactly the shapes the fields describe (the C layer cannot
+        see buffer sizes)."""
+        if self.bits not in (4, 8) or self.group not in (32, 64) or self.cols % self.group:
+            raise ValueError(f"unsupported format: bits {self.bits}, group {self.group}, cols {self.cols}")
+        if self.rows <= 0 or self.n_experts <= 0:
+            raise ValueError("rows and n_experts must be positive")
+        pdt = torch.int16 if self.param_dtype == PARAM_BF16 else torch.float16
+        R = self.n_experts * self.rows
+        for name, t, dt, cols in (("packed", self.packed, torch.int32, self.cols * self.bits // 32),
+                                  ("scales", self.scales, pdt, self.cols // self.group),
+                                  ("biases", self.biases, pdt, self.cols // self.group)):
+            _dev(t, dt, name)
+            if tuple(t.shape) != (R, cols):
+                raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {(R, cols)}")
+
     def c(self) -> QWeightC:
+        self.check()
         return QWeightC(self.packed.data_ptr(), self.scales.data_ptr(), self.biases.data_ptr(),
                         self.rows, self.cols, self.bits, self.group, self.n_experts,
                         self.param_dtype)
@@ -79,7 +96,8 @@ class QWeight:
     def expert(self, e: int) -> "QWeight":
         r = self.rows
         return QWeight(self.packed[e * r:(e + 1) * r], self.scales[e * r:(e + 1) * r],
-                       self.biases[e * r:(e + 1) * r], self.bits, self.rows, self.cols, 1)
+                       self.biases[e * r:(e + 1) * r], self.bits, self.rows, self.cols, 1,
+                       self.group, self.param_dtype)
 
 
 @dataclass
@@ -92,7 +110,11 @@ class Lora:
     scale: float
 
     def c(self) -> LoraC:
+        _dev(self.A, torch.float16, "lora A")
+        _dev(self.B, torch.float16, "lora B")
         n, r, i = self.A.shape
+        if self.B.dim() != 3 or self.B.shape[0] != n or self.B.shape[2] != r:
+            raise ValueError(f"lora B has shape {tuple(self.B.shape)}, expected ({n}, out_dim, {r})")
         return LoraC(self.A.data_ptr(), self.B.data_ptr(), r, n, i, self.B.shape[1],
                      float(self.scale))
 
@@ -117,19 +139,17 @@ class MoELayer:
     lora_down: Optional[Lora] = None
     router_bias: Optional[torch.Tensor] = None
     add_residual: bool = False
-    _keep: list = field(default_factory=list, repr=False)
 
     def c(self) -> MoELayerC:
+        """The C struct of the layer.  The LoRA structs it points to are owned by the
+        returned struct (ctypes keeps a pointer field's target alive with the struct)."""
         loras = []
         for l in (self.lora_gate, self.lora_up, self.lora_down):
-            if l is None:
-                loras.append(ctypes.POINTER(LoraC)())
-            else:
-                lc = l.c()
-                self._keep.append(lc)
-                loras.append(ctypes.pointer(lc))
+            loras.append(ctypes.POINTER(LoraC)() if l is None else ctypes.pointer(l.c()))
         if self.router_bias is not None:
             _dev(self.router_bias, torch.float32, "router_bias")
+            if self.router_bias.numel() != self.n_experts:
+                raise ValueError(f"router_bias must hold {self.n_experts} values")
         return MoELayerC(self.hidden, self.inter, self.shared_inter, self.n_experts, self.top_k,
                          int(self.add_residual), self.router.c(), self.shared_gate.c(),
                          self.exp_gate.c(), self.exp_up.c(), self.exp_down.c(), self.sh_gate.c(),
@@ -231,6 +251,28 @@ def moe_workspace(layer: MoELayer, max_tokens: int, device="cuda") -> torch.Tens
     return torch.empty(moe_workspace_bytes(layer, max_tokens), dtype=torch.uint8, device=device)
 
 
+def _moe_io(layer: MoELayer, x: torch.Tensor, y: torch.Tensor,
+            adapter_idx: Optional[torch.Tensor], idx_out: Optional[torch.Tensor],
+            w_out: Optional[torch.Tensor]) -> int:
+    """Check the per-call tensors of a layer call (the C layer cannot see buffer sizes) and
+    return the token count."""
+    _dev(x, torch.float16, "x")
+    _dev(y, torch.float16, "y")
+    if x.dim() != 2 or x.shape[1] != layer.hidden or tuple(y.shape) != tuple(x.shape):
+        raise ValueError(f"x and y must be [t, {layer.hidden}], got {tuple(x.shape)} and {tuple(y.shape)}")
+    t = x.shape[0]
+    for name, v, dt, n in (("adapter_idx", adapter_idx, torch.int32, t),
+                           ("idx_out", idx_out, torch.int32, t * layer.top_k),
+                           ("w_out", w_out, torch.float32, t * layer.top_k)):
+        if v is not None:
+            _dev(v, dt, name)
+            if v.numel() != n:
+                raise ValueError(f"{name} must hold {n} elements, got {v.numel()}")
+            if v.device != x.device:
+                raise ValueError(f"{name} is on {v.device}, x on {x.device}")
+    return t
+
+
 def moe_switchglu_int4(layer: MoELayer, x: torch.Tensor,
                        adapter_idx: Optional[torch.Tensor] = None,
                        ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
@@ -241,13 +283,11 @@ def moe_switchglu_int4(layer: MoELayer, x: torch.Tensor,
         ws = moe_workspace(layer, t, x.device)
     _dev(ws, torch.uint8, "ws")
     y = out if out is not None else torch.empty_like(x)
-    _dev(y, torch.float16, "out")
-    if adapter_idx is not None:
-        _dev(adapter_idx, torch.int32, "adapter_idx")
     idx = w = None
     if return_routing:
         idx = torch.empty((t, layer.top_k), dtype=torch.int32, device=x.device)
         w = torch.empty((t, layer.top_k), dtype=torch.float32, device=x.device)
+    _moe_io(layer, x, y, adapter_idx, idx, w)
     c = layer.c()
     check(lib.moe_switchglu_int4(ctypes.byref(c), x.data_ptr(), t, _ptr(adapter_idx),
                                  y.data_ptr(), _ptr(idx), _ptr(w), ws.data_ptr(), ws.numel(),
@@ -266,13 +306,11 @@ class MoECall:
     def __init__(self, layer: MoELayer, x: torch.Tensor, y: torch.Tensor, ws: torch.Tensor,
                  adapter_idx: Optional[torch.Tensor] = None,
                  idx_out: Optional[torch.Tensor] = None, w_out: Optional[torch.Tensor] = None):
-        _dev(x, torch.float16, "x")
-        _dev(y, torch.float16, "y")
+        self.t = _moe_io(layer, x, y, adapter_idx, idx_out, w_out)
         _dev(ws, torch.uint8, "ws")
         self.layer, self.x, self.y, self.ws = layer, x, y, ws
         self.adapter_idx, self.idx_out, self.w_out = adapter_idx, idx_out, w_out
         self.c = layer.c()
-        self.t = x.shape[0]
 
     def __call__(self, stage: int = STAGE_ALL, stream: Optional[int] = None) -> None:
         s = ctypes.c_void_p(stream if stream is not None

@@ -14,6 +14,7 @@ constexpr int MAX_COLS = 16384;
 constexpr int MAX_MOE_DIM = 4096;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 thread_local const char* g_last_error = "";
 
@@ -34,7 +35,7 @@ int check_qweight(const qmoe_qweight* w, int bits_required, bool dense = false) 
     if (dense ? (w->group != 64 && w->group != 32) : (w->group != 64 || w->param_dtype != QMOE_PARAM_F16))
         return QMOE_ERR_UNSUPPORTED;
     if (w->cols % 512 != 0 || w->cols > MAX_COLS) return QMOE_ERR_UNSUPPORTED;
-    if (!aligned16(w->packed)) return QMOE_ERR_MISALIGNED;
+    if (!aligned16(w->packed) || !aligned16(w->scales) || !aligned16(w->biases)) return QMOE_ERR_MISALIGNED;
     return QMOE_OK;
 }
 
@@ -80,6 +81,7 @@ int check_layer(const qmoe_moe_layer* L) {
     if ((st = check_lora(L->lora_gate, H, SI))) return st;
     if ((st = check_lora(L->lora_up, H, SI))) return st;
     if ((st = check_lora(L->lora_down, SI, H))) return st;
+    if (!aligned4(L->router_bias)) return QMOE_ERR_MISALIGNED;
     return QMOE_OK;
 }
 
@@ -94,7 +96,7 @@ const char* qmoe_status_string(int status) {
         case QMOE_OK: return "ok";
         case QMOE_ERR_INVALID_ARG: return "invalid argument";
         case QMOE_ERR_UNSUPPORTED: return "unsupported shape or format";
-        case QMOE_ERR_MISALIGNED: return "pointer not 16-byte aligned";
+        case QMOE_ERR_MISALIGNED: return "pointer not aligned (16 bytes; 4 for int32/fp32 arrays)";
         case QMOE_ERR_WORKSPACE: return "workspace missing or too small";
         case QMOE_ERR_HIP: return "kernel launch failed";
         default: return "unknown status";
@@ -139,7 +141,7 @@ int qmoe_dequantize(const qmoe_qweight* w, float* out, void* stream) {
     if ((w->bits != 4 && w->bits != 8) || (w->group != 64 && w->group != 32) || w->cols % 64)
         return QMOE_ERR_UNSUPPORTED;
     if (w->param_dtype != QMOE_PARAM_F16 && w->param_dtype != QMOE_PARAM_BF16) return QMOE_ERR_UNSUPPORTED;
-    if (!aligned16(out)) return QMOE_ERR_MISALIGNED;
+    if (!aligned16(out) || !aligned16(w->packed)) return QMOE_ERR_MISALIGNED;
     return hip_status(qmoe::launch_dequantize(*w, out, as_stream(stream)));
 }
 
@@ -196,6 +198,7 @@ int moe_switchglu_int4_stage(const qmoe_moe_layer* L, int32_t stage, const uint1
     int st = check_layer(L);
     if (st) return st;
     if (!aligned16(x) || !aligned16(y)) return QMOE_ERR_MISALIGNED;
+    if (!aligned4(adapter_idx) || !aligned4(idx_out) || !aligned4(w_out)) return QMOE_ERR_MISALIGNED;
     const size_t xb = (size_t)t * L->hidden * 2;
     if (overlap(x, xb, y, xb)) return QMOE_ERR_INVALID_ARG;
     if (!ws || ws_bytes < qmoe::moe_workspace_bytes(*L, t)) return QMOE_ERR_WORKSPACE;

@@ -1,5 +1,6 @@
 // Decode path of the MoE SwitchGLU layer (a few tokens per call): three launches, no sort,
-// no atomics, top-K recomputed where it is needed.
+// no atomics, top-K taken once per token in the gate/up launch and published to the down
+// launch through the workspace.
 //
 // The layer is the one described in moe.hip (pages: "Edge0-35B-A3B Preview model repository
 // guide" model spec; "Recover-LoRA ..." sections 1-2; "Edge0 project review" highlights 2-3).
@@ -15,7 +16,7 @@
 //                rows of expert idx[t][k] before x is staged and the block synchronises;
 //                then h = silu(g) * u is stored (fp16).  Shared blocks add the LoRA
 //                up-projections and store h_s.
-//   D3 down    : one block per (row block, token).  It recomputes the token's top-K,
+//   D3 down    : one block per (row block, token).  It reads the token's published routing,
 //                stages the token's K expert activations h and h_s, computes the shared
 //                expert's LoRA z_down, streams the K + 1 down matrices' rows, and combines
 //                y = sum_k w_k o_k + sigmoid(gate) (o_s + LoRA) (+ residual) in-block.

@@ -224,3 +224,21 @@ def test_package_fails_loudly_without_the_library(tmp_path):
     r = subprocess.run([sys.executable, "-c", "import int4_group_quantized_amd"], cwd=tmp_path,
                        capture_output=True, text=True, timeout=300)
     assert r.returncode != 0 and "ImportError" in r.stderr and "not built" in r.stderr
+
+
+def test_moe_rejects_misaligned_parameters_and_index_arrays():
+    """Scales and biases are read with 16-byte loads and are checked like the packed words;
+    the int32/fp32 routing outputs, adapter indices and router bias must be 4-byte aligned."""
+    f = q.lib.moe_switchglu_int4
+    X, Y, WS = FAKE, FAKE * 16, FAKE * 64
+    ok = layer_c()
+    ws1 = q.lib.moe_switchglu_int4_workspace_bytes(ctypes.byref(ok), 1)
+    mis_s = _lib.QWeightC(FAKE, FAKE + 8, FAKE, 512, 2048, 4, 64, 256, 0)
+    mis_b = _lib.QWeightC(FAKE, FAKE, FAKE + 2, 2048, 512, 4, 64, 256, 0)
+    for bad in (layer_c(exp_gate=mis_s), layer_c(exp_down=mis_b), layer_c(router_bias=FAKE + 2)):
+        assert f(ctypes.byref(bad), X, 1, None, Y, None, None, WS, ws1, None) == _lib.QMOE_ERR_MISALIGNED
+    for idx, w, ad in ((FAKE + 2, None, None), (None, FAKE + 1, None), (None, None, FAKE + 3)):
+        assert f(ctypes.byref(ok), X, 1, ad, Y, idx, w, WS, ws1, None) == _lib.QMOE_ERR_MISALIGNED
+    g = q.lib.qlinear_int4
+    w = _lib.QWeightC(FAKE, FAKE + 4, FAKE, 512, 2048, 4, 64, 1, 0)
+    assert g(FAKE, 1, ctypes.byref(w), None, None, FAKE * 8, None) == _lib.QMOE_ERR_MISALIGNED
