@@ -50,18 +50,35 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def measured_traffic(kernel):
-    """HBM bytes per launch of `kernel` from the committed counter runs (profiles/traffic.json),
-    or None when the kernel's sources changed since the counters were taken."""
+def counter_entry(key):
+    """A committed counter record (profiles/traffic.json) for `key` ("workload/kernel"), or
+    None when it is absent or the kernel's sources changed since the counters were taken."""
     import hashlib
     try:
-        entry = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))[kernel]
+        entry = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))[key]
         h = hashlib.sha256()
         for src in entry["sources"]:
             h.update(open(os.path.join(ROOT, src), "rb").read())
     except (OSError, KeyError, ValueError):
         return None
-    return entry["traffic_bytes_per_launch"] if h.hexdigest() == entry["source_sha256"] else None
+    return entry if h.hexdigest() == entry["source_sha256"] else None
+
+
+def measured_traffic(key):
+    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE runs, or None."""
+    e = counter_entry(key)
+    return None if e is None else e.get("traffic_bytes_per_launch")
+
+
+class CacheFlush:
+    """Writes 1 GiB (4x the 256 MB last-level cache, 250x an XCD's L2) on the current stream,
+    so that a timed region that follows starts with no benchmark data in any cache."""
+
+    def __init__(self, torch):
+        self.buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+
+    def __call__(self):
+        self.buf.fill_(1)
 
 
 # ------------------------------------------------------------------------------ device data
@@ -112,17 +129,29 @@ def graph_of(torch, fn):
     return g
 
 
-def time_graph(torch, g, reps=1):
-    """Average ms of one replay: HIP events on the stream the graph runs on."""
+def time_graph(torch, g, reps=1, flush=None):
+    """Average ms of one replay: HIP events on the stream the graph runs on.  With `flush`,
+    the caches are flushed before each replay, outside the timed span."""
     st = torch.cuda.current_stream()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    a.record(st)
+    total = 0.0
+    if flush is None:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        for _ in range(reps):
+            g.replay()
+        b.record(st)
+        b.synchronize()
+        return a.elapsed_time(b) / reps
     for _ in range(reps):
+        flush()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(st)
         g.replay()
-    b.record(st)
-    b.synchronize()
-    return a.elapsed_time(b) / reps
+        b.record(st)
+        b.synchronize()
+        total += a.elapsed_time(b)
+    return total / reps
 
 
 # ------------------------------------------------------------------------------ CPU baseline
@@ -170,11 +199,48 @@ def cpu_baseline_moe_decode(n_tokens=600, budget_s=20.0):
 
 # ------------------------------------------------------------------------------ workloads
 
+def kernel_row(name, key, us, nbytes=None, flops=None, peak=HBM_PEAK_GBS):
+    """One per-kernel entry: average launch time and its algorithmic rate against the peak."""
+    r = {"kernel": name, "us_per_launch": us}
+    if nbytes is not None:
+        gbs = nbytes / (us * 1e-6) / 1e9
+        r.update(bytes_per_launch=nbytes, gbps=gbs, hbm_frac=gbs / HBM_PEAK_GBS,
+                 traffic=measured_traffic(key))
+    if flops is not None:
+        tf = flops / (us * 1e-6) / 1e12
+        r.update(flops_per_launch=flops, tflops=tf, mfma_frac=tf / FP16_MFMA_PEAK_TFLOPS)
+    return r
+
+
+def roofline_of(row, bound="hbm"):
+    """The bench line's roofline object for one per-kernel entry."""
+    if bound == "hbm":
+        return {"kernel": row["kernel"], "bound": "hbm", "achieved": row["gbps"], "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": row["gbps"] / HBM_PEAK_GBS, "traffic": row.get("traffic"),
+                "bytes_per_launch": row["bytes_per_launch"], "us_per_launch": row["us_per_launch"]}
+    return {"kernel": row["kernel"], "bound": "mfma", "achieved": row["tflops"],
+            "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": row["tflops"] / FP16_MFMA_PEAK_TFLOPS,
+            "traffic": row.get("traffic"), "flops_per_launch": row["flops_per_launch"],
+            "us_per_launch": row["us_per_launch"]}
+
+
+# algorithmic bytes of the decode layer at one token (config 1 shapes, top-4, LoRA r16)
+DEC_XSIDE_BYTES = (MAT_BYTES_8BIT(E, H) + MAT_BYTES_8BIT(1, H) + 2 * MAT_BYTES_4BIT(SI, H)
+                   + 2 * RANK * H * 2 + H * 2 + (E + 1 + 2 * SI + 2 * RANK) * 4)
+DEC_GATE_UP_BYTES = (4 * 2 * MAT_BYTES_4BIT(I, H) + H * 2 + 2 * SI * RANK * 2 + 2 * SI * 4
+                     + (4 * I + SI) * 2)
+DEC_DOWN_BYTES = (4 * MAT_BYTES_4BIT(H, I) + MAT_BYTES_4BIT(H, SI) + RANK * SI * 2 + H * RANK * 2
+                  + (4 * I + SI) * 2 + H * 2)
+DEC_STEP_BYTES = (MAT_BYTES_8BIT(E, H) + MAT_BYTES_8BIT(1, H) + 4 * 3 * MAT_BYTES_4BIT(I, H)
+                  + 3 * MAT_BYTES_4BIT(SI, H) + 3 * RANK * (H + SI) * 2 + 2 * H * 2)
+
+
 def bench_moe_decode(args, q, torch):
     gen = torch.Generator(device="cuda")
     gen.manual_seed(1234)
     t0 = time.perf_counter()
     layers = [make_layer(q, torch, gen) for _ in range(LAYERS)]
+    flush = CacheFlush(torch)
     torch.cuda.synchronize()
     log(f"built {LAYERS} layers in {time.perf_counter() - t0:.1f} s")
     K, W = args.steps, args.warmup
@@ -195,31 +261,28 @@ def bench_moe_decode(args, q, torch):
     g_main = graph_of(torch, run(0, K))
     if g_warm is not None:
         g_warm.replay()
-    torch.cuda.synchronize()
     t_wall = time.perf_counter()
-    ms_total = time_graph(torch, g_main)
+    ms_total = time_graph(torch, g_main, flush=flush)
     t_wall = time.perf_counter() - t_wall
-    log(f"main: {K} steps in {ms_total:.3f} ms (wall {t_wall * 1e3:.3f} ms)")
+    log(f"main: {K} steps in {ms_total:.3f} ms (wall {t_wall * 1e3:.3f} ms, caches flushed first)")
 
-    # dominant kernel: the gate/up stage alone, over R (layer, token) pairs routed beforehand
+    # each launch alone, over R (layer, token) pairs routed beforehand, caches flushed first
     R = 512
     wss = torch.empty((R, ws_bytes), dtype=torch.uint8, device="cuda")
     rx = (torch.randn((R, 1, H), generator=gen, device="cuda")).half()
     ry = torch.empty_like(rx)
     rcalls = [q.MoECall(layers[r % LAYERS], rx[r], ry[r], wss[r]) for r in range(R)]
     for c in rcalls:
-        c(q.STAGE_ROUTE)
+        c()
     torch.cuda.synchronize()
-
-    def gate_up():
-        for c in rcalls:
-            c(q.STAGE_GATE_UP)
-    g_gu = graph_of(torch, gate_up)
-    ms_gu = time_graph(torch, g_gu, reps=3) / R
-    gu_bytes = 4 * 2 * MAT_BYTES_4BIT(I, H) + H * 2 + 2 * SI * RANK * 2 + 2 * SI * 4 + (4 * I + SI) * 2
-    step_bytes = (MAT_BYTES_8BIT(E, H) + MAT_BYTES_8BIT(1, H) + 4 * 3 * MAT_BYTES_4BIT(I, H)
-                  + 3 * MAT_BYTES_4BIT(SI, H) + 3 * RANK * (H + SI) * 2 + 2 * H * 2)
-    achieved = gu_bytes / (ms_gu * 1e-3) / 1e9
+    rows = []
+    for name, st, nbytes in (("k_dec_xside", q.STAGE_ROUTE, DEC_XSIDE_BYTES),
+                             ("k_dec_gate_up", q.STAGE_GATE_UP, DEC_GATE_UP_BYTES),
+                             ("k_dec_down", q.STAGE_DOWN, DEC_DOWN_BYTES)):
+        g = graph_of(torch, lambda st=st: [c(st) for c in rcalls])
+        us = time_graph(torch, g, reps=3, flush=flush) / R * 1e3
+        rows.append(kernel_row(name, f"moe_decode/{name}", us, nbytes))
+    dom = max(rows, key=lambda r: r["us_per_launch"])
     ms_step = ms_total / K
     res = {
         "metric": "int4 MoE layer tokens/s (decode, 1 token per step)",
@@ -228,15 +291,14 @@ def bench_moe_decode(args, q, torch):
         "vs_baseline": None, "dtype": "f16", "data": "synthetic",
         "config": {"workload": "moe_switchglu_int4 decode: 1 token/step, hidden 2048, 256 "
                                "experts int4 g64, top-4, shared expert + 8-bit gate, LoRA r16 "
-                               "a32, 40 independently seeded layers rotated",
+                               "a32, 40 independently seeded layers rotated, caches flushed "
+                               "before the timed region",
                    "global_batch": 1, "layers_rotated": LAYERS,
-                   "step_algorithmic_bytes": step_bytes,
-                   "step_hbm_gbps": step_bytes / (ms_step * 1e-3) / 1e9},
-        "roofline": {"kernel": "k_dec_gate_up (top-K, routed + shared gate/up, silu*up)",
-                     "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic("k_dec_gate_up"),
-                     "bytes_per_launch": gu_bytes, "us_per_launch": ms_gu * 1e3},
+                   "step_algorithmic_bytes": DEC_STEP_BYTES,
+                   "step_hbm_gbps": DEC_STEP_BYTES / (ms_step * 1e-3) / 1e9,
+                   "step_hbm_frac": DEC_STEP_BYTES / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                   "kernels": rows},
+        "roofline": roofline_of(dom),
     }
     return res, cpu_baseline_moe_decode
 
@@ -279,6 +341,7 @@ def bench_moe_prefill(args, q, torch):
     gen.manual_seed(4321)
     t0 = time.perf_counter()
     layers = [make_layer(q, torch, gen, skew=args.skew) for _ in range(NL)]
+    flush = CacheFlush(torch)
     xs = torch.randn((NX, T, H), generator=gen, device="cuda").half()
     ys = torch.empty_like(xs)
     ws_bytes = q.moe_workspace_bytes(layers[0], T)
@@ -296,9 +359,9 @@ def bench_moe_prefill(args, q, torch):
     if W:
         graph_of(torch, run(K, K + W)).replay()
     g_main = graph_of(torch, run(0, K))
-    ms_total = time_graph(torch, g_main)
+    ms_total = time_graph(torch, g_main, flush=flush)
     ms_step = ms_total / K
-    log(f"main: {K} steps in {ms_total:.3f} ms")
+    log(f"main: {K} steps in {ms_total:.3f} ms (caches flushed first)")
 
     # stages over NL routed workspaces (one per layer, distinct inputs)
     wss = torch.empty((NL, ws_bytes), dtype=torch.uint8, device="cuda")
@@ -312,7 +375,7 @@ def bench_moe_prefill(args, q, torch):
         def f(st=st):
             for c in scalls:
                 c(st)
-        stage_us[name] = time_graph(torch, graph_of(torch, f), reps=5) / NL * 1e3
+        stage_us[name] = time_graph(torch, graph_of(torch, f), reps=5, flush=flush) / NL * 1e3
     ih = idx.cpu().numpy()
     used = np.mean([len(np.unique(ih[i])) for i in range(NL)])
     pairs = T * 4
@@ -324,18 +387,24 @@ def bench_moe_prefill(args, q, torch):
     step_bytes = (MAT_BYTES_8BIT(E, H) + MAT_BYTES_8BIT(1, H) + used * 3 * MAT_BYTES_4BIT(I, H)
                   + 3 * MAT_BYTES_4BIT(SI, H) + 3 * RANK * (H + SI) * 2 + 2 * T * H * 2)
     step_flops = 2 * T * (E * H + H + 3 * SI * H + 4 * 3 * I * H)
+    key = f"moe_prefill{'' if T == 512 else f'_{T}'}{'_skew' if args.skew else ''}/k_pf_gemm"
+    ctr = counter_entry(key) or {}
+    counted = {k: ctr[k] for k in ("traffic_bytes_per_launch", "mfma_flops_per_launch",
+                                   "mfma_busy_frac") if k in ctr}
     if sweep:
         roofline = {"kernel": "k_pf_gemm grouped gate/up (silu*up epilogue)",
                     "bound": "mfma", "achieved": tflops, "peak": FP16_MFMA_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": tflops / FP16_MFMA_PEAK_TFLOPS, "traffic": None,
+                    "unit": "TFLOP/s", "frac": tflops / FP16_MFMA_PEAK_TFLOPS,
+                    "traffic": ctr.get("traffic_bytes_per_launch"),
                     "flops_per_launch": gu_flops, "us_per_launch": us,
-                    "hbm_gbps": achieved, "hbm_frac": achieved / HBM_PEAK_GBS}
+                    "hbm_gbps": achieved, "hbm_frac": achieved / HBM_PEAK_GBS, "counters": counted}
     else:
         roofline = {"kernel": "k_pf_gemm grouped gate/up (silu*up epilogue)",
                     "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                    "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                    "traffic": ctr.get("traffic_bytes_per_launch"),
                     "bytes_per_launch": gu_bytes, "us_per_launch": us,
-                    "mfma_tflops": tflops, "mfma_frac": tflops / FP16_MFMA_PEAK_TFLOPS}
+                    "mfma_tflops": tflops, "mfma_frac": tflops / FP16_MFMA_PEAK_TFLOPS, "counters": counted}
     res = {
         "metric": f"int4 MoE layer tokens/s (prefill, {T} tokens per step)",
         "value": T * K / (ms_total * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": K,
@@ -409,11 +478,12 @@ def bench_moe_stack(args, q, torch):
         for c in calls:
             c()
     acts[0].copy_(x0)
+    flush = CacheFlush(torch)
     if W:
         gw = graph_of(torch, lambda: [step() for _ in range(W)])
         gw.replay()
     g = graph_of(torch, lambda: [step() for _ in range(K)])
-    ms = time_graph(torch, g)
+    ms = time_graph(torch, g, flush=flush)
     ms_step = ms / K
 
     # dominant kernel: gate/up of one layer over routed workspaces (one per layer)
@@ -425,7 +495,7 @@ def bench_moe_stack(args, q, torch):
         c(q.STAGE_ROUTE)
     torch.cuda.synchronize()
     g_gu = graph_of(torch, lambda: [c(q.STAGE_GATE_UP) for c in rcalls])
-    us_gu = time_graph(torch, g_gu, reps=3) / LAYERS * 1e3
+    us_gu = time_graph(torch, g_gu, reps=3, flush=flush) / LAYERS * 1e3
     ih = idx.cpu().numpy()
     used = float(np.mean([len(np.unique(ih[l])) for l in range(LAYERS)]))
     # 128 (token, k) pairs take the token-sorted path: the grouped gate/up GEMM reads each
@@ -447,7 +517,7 @@ def bench_moe_stack(args, q, torch):
                    "step_hbm_gbps": step_bytes / (ms_step * 1e-3) / 1e9},
         "roofline": {"kernel": "k_pf_gemm grouped gate/up (16 tokens, top-8; silu*up epilogue)",
                      "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic("moe_stack/k_pf_gemm"),
                      "bytes_per_launch": gu_bytes, "us_per_launch": us_gu},
     }
     return res, cpu_baseline_moe_stack
@@ -491,7 +561,7 @@ def bench_supergroup(args, q, torch, a8=False):
     weight-activation integer path, activations quantized to 8 bits inside the call)."""
     gemm = q.qlinear_supergroup_a8 if a8 else q.qlinear_supergroup
     B, N, Kc = args.batch, 3072, 1024
-    COPIES = 1024 if B == 1 else 64          # B = 1: 1 GB of weights rotated, 4x the cache
+    COPIES = 1024                            # 1 GB of weights rotated, 4x the last-level cache
     gen = torch.Generator(device="cuda")
     gen.manual_seed(97)
     mats = []
@@ -511,7 +581,7 @@ def bench_supergroup(args, q, torch, a8=False):
     if W:
         graph_of(torch, run(K, K + W)).replay()
     g = graph_of(torch, run(0, K))
-    ms = time_graph(torch, g)
+    ms = time_graph(torch, g, flush=CacheFlush(torch))
     us = ms / K * 1e3
     wbytes = sg_bytes(N, Kc)
     bytes_ = wbytes + B * Kc * 2 + B * N * 2
@@ -621,7 +691,7 @@ def bench_gemv(args, q, torch):
     if W:
         graph_of(torch, run(K, K + W)).replay()
     g = graph_of(torch, run(0, K))
-    ms = time_graph(torch, g)
+    ms = time_graph(torch, g, flush=CacheFlush(torch))
     bytes_ = N * Kc // 2 + 2 * (N * (Kc // G) * 2) + Kc * 2 + N * 2
     ach = bytes_ / (ms / K * 1e-3) / 1e9
     fmt = f"int4 g{G}{' bf16 parameters' if bf else ''}"
@@ -669,7 +739,7 @@ def bench_prerouter(args, q, torch):
     if W:
         graph_of(torch, run(K, K + W)).replay()
     g = graph_of(torch, run(0, K))
-    ms = time_graph(torch, g)
+    ms = time_graph(torch, g, flush=CacheFlush(torch))
     us = ms / K * 1e3
     # algorithmic bytes: the dense parts of the fc1 and linear_init rows, the 2k gathered
     # one-hot columns of each, fc2, the biases, h in, act out and in, logits out and in, the
