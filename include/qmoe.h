@@ -35,7 +35,8 @@
  *    array members are device pointers.
  *  - fp16 data is passed as uint16_t bit patterns (IEEE binary16).
  *  - The caller owns every buffer, workspaces included.  The library allocates and frees
- *    no device memory, keeps no state between calls, never copies to the host and never
+ *    no device memory, keeps no state between calls (apart from the fixed per-device
+ *    scratch of moe_switchglu_int4_noalloc), never copies to the host and never
  *    synchronises: work is enqueued on `stream` and the call returns.
  *  - Errors: 0 on success, a negative QMOE_ERR_* code otherwise.  Arguments are validated
  *    before anything is enqueued; on error nothing is enqueued and outputs are untouched.
@@ -253,6 +254,24 @@ int moe_switchglu_int4_stage(const qmoe_moe_layer* L, int32_t stage, const uint1
                              int32_t t, const int32_t* adapter_idx, uint16_t* y,
                              int32_t* idx_out, float* w_out, void* ws, size_t ws_bytes,
                              void* stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): moe_switchglu_int4 with its workspace in
+ * a fixed scratch array inside the library instead of a caller buffer.  Same arguments,
+ * outputs, limits and results as moe_switchglu_int4 without ws / ws_bytes.  The scratch
+ * holds QMOE_NOALLOC_SCRATCH_BYTES per device and is kept from the first call on a device
+ * until the process ends; a call whose workspace (moe_switchglu_int4_workspace_bytes of the
+ * layer at t tokens) exceeds it fails with QMOE_ERR_WORKSPACE before anything is enqueued
+ * (hidden 2048, 256 experts, top-4: up to 512 tokens).  The call allocates and frees
+ * nothing.  All calls on one device share that device's scratch, which keeps the last
+ * call's contents (nothing in it needs to start at zero): calls that overlap in time on one
+ * device (two streams, two host threads) race, and the caller must serialise them.
+ */
+#define QMOE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int moe_switchglu_int4_noalloc(const qmoe_moe_layer* L, const uint16_t* x, int32_t t,
+                               const int32_t* adapter_idx, uint16_t* y, int32_t* idx_out,
+                               float* w_out, void* stream);
 
 /*
  * Mixed ternary / 4-bit super-group quantization of fp32 w [rows x cols] ([R5] 2.1).

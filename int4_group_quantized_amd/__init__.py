@@ -23,6 +23,7 @@ from .api import (  # noqa: F401
     dequantize,
     lora_apply,
     moe_switchglu_int4,
+    moe_switchglu_int4_noalloc,
     moe_workspace,
     moe_workspace_bytes,
     qlinear_int4,

@@ -24,6 +24,7 @@ QMOE_ERR_UNSUPPORTED = -2
 QMOE_ERR_MISALIGNED = -3
 QMOE_ERR_WORKSPACE = -4
 QMOE_ERR_HIP = -5
+NOALLOC_SCRATCH_BYTES = 32 << 20   # QMOE_NOALLOC_SCRATCH_BYTES of include/qmoe.h
 
 
 class QWeightC(ctypes.Structure):
@@ -74,6 +75,7 @@ _SIGS = {
                                           ctypes.c_size_t, _P]),
     "moe_switchglu_int4_stage": (ctypes.c_int, [ctypes.POINTER(MoELayerC), _I, _P, _I, _P, _P, _P,
                                                 _P, _P, ctypes.c_size_t, _P]),
+    "moe_switchglu_int4_noalloc": (ctypes.c_int, [ctypes.POINTER(MoELayerC), _P, _I, _P, _P, _P, _P, _P]),
     "qmoe_quantize_supergroup": (ctypes.c_int, [_P, _I, _I, _I, _P, _P, _P, _P]),
     "qlinear_supergroup": (ctypes.c_int, [_P, _I, _P, _P, _P, _I, _I, _I, _P, _P]),
     "qmoe_quantize_act8": (ctypes.c_int, [_P, _I, _I, _P, _P, _P]),

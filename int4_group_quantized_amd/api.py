@@ -295,6 +295,22 @@ def moe_switchglu_int4(layer: MoELayer, x: torch.Tensor,
     return (y, idx, w) if return_routing else y
 
 
+def moe_switchglu_int4_noalloc(layer: MoELayer, x: torch.Tensor,
+                               adapter_idx: Optional[torch.Tensor] = None,
+                               out: Optional[torch.Tensor] = None,
+                               idx_out: Optional[torch.Tensor] = None,
+                               w_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The layer with the library's fixed per-device scratch as its workspace (the entry
+    point for callers that cannot allocate; overlapping calls on one device race)."""
+    y = out if out is not None else torch.empty_like(x)
+    t = _moe_io(layer, x, y, adapter_idx, idx_out, w_out)
+    c = layer.c()
+    check(lib.moe_switchglu_int4_noalloc(ctypes.byref(c), x.data_ptr(), t, _ptr(adapter_idx),
+                                         y.data_ptr(), _ptr(idx_out), _ptr(w_out), _stream(x)),
+          "moe_switchglu_int4_noalloc")
+    return y
+
+
 STAGE_ALL, STAGE_ROUTE, STAGE_GATE_UP, STAGE_DOWN = 0, 1, 2, 3
 PARAM_F16, PARAM_BF16 = 0, 1
 

@@ -11,6 +11,8 @@
 namespace {
 
 constexpr int MAX_COLS = 16384;
+static_assert(qmoe::MOE_NOALLOC_SCRATCH_BYTES == QMOE_NOALLOC_SCRATCH_BYTES,
+              "the header states the allocation-free call's scratch size");
 constexpr int MAX_MOE_DIM = 4096;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -205,6 +207,29 @@ int moe_switchglu_int4_stage(const qmoe_moe_layer* L, int32_t stage, const uint1
     if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return QMOE_ERR_MISALIGNED;
     return hip_status(qmoe::launch_moe(*L, stage, x, t, adapter_idx, y, idx_out, w_out, ws,
                                        as_stream(stream)));
+}
+
+int moe_switchglu_int4_noalloc(const qmoe_moe_layer* L, const uint16_t* x, int32_t t,
+                               const int32_t* adapter_idx, uint16_t* y, int32_t* idx_out,
+                               float* w_out, void* stream) {
+    if (!x || !y || t <= 0) return QMOE_ERR_INVALID_ARG;
+    if (t > 65536) return QMOE_ERR_UNSUPPORTED;
+    int st = check_layer(L);
+    if (st) return st;
+    if (!aligned16(x) || !aligned16(y)) return QMOE_ERR_MISALIGNED;
+    if (!aligned4(adapter_idx) || !aligned4(idx_out) || !aligned4(w_out)) return QMOE_ERR_MISALIGNED;
+    const size_t xb = (size_t)t * L->hidden * 2;
+    if (overlap(x, xb, y, xb)) return QMOE_ERR_INVALID_ARG;
+    if (qmoe::moe_workspace_bytes(*L, t) > qmoe::MOE_NOALLOC_SCRATCH_BYTES) {
+        g_last_error = "the layer needs more workspace for this token count than the "
+                       "allocation-free call's fixed scratch holds";
+        return QMOE_ERR_WORKSPACE;
+    }
+    void* ws = nullptr;
+    st = hip_status(qmoe::moe_noalloc_scratch(as_stream(stream), &ws));
+    if (st) return st;
+    return hip_status(qmoe::launch_moe(*L, QMOE_STAGE_ALL, x, t, adapter_idx, y, idx_out, w_out,
+                                       ws, as_stream(stream)));
 }
 
 int qmoe_quantize_supergroup(const float* w, int32_t rows, int32_t cols, int32_t period,

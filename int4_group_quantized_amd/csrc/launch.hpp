@@ -37,6 +37,10 @@ hipError_t launch_lora_apply(const uint16_t* x, int t, const qmoe_lora& l,
 
 // moe.hip
 size_t moe_workspace_bytes(const qmoe_moe_layer& L, int max_tokens);
+// the allocation-free call's workspace: a static device array of this size per device, its
+// device address looked up on the first call on the stream's device
+constexpr size_t MOE_NOALLOC_SCRATCH_BYTES = (size_t)32 << 20;
+hipError_t moe_noalloc_scratch(hipStream_t s, void** ptr);
 hipError_t launch_moe(const qmoe_moe_layer& L, int stage, const uint16_t* x, int t,
                       const int32_t* adapter_idx, uint16_t* y, int32_t* idx_out,
                       float* w_out, void* ws, hipStream_t s);

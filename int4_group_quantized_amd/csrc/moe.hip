@@ -18,6 +18,7 @@
 //     stable sort of the (token, k) pairs by expert, grouped expert GEMMs, combine.
 // This file owns the workspace layout and the choice between the two.
 #include <algorithm>
+#include <mutex>
 
 #include "gemv_core.hpp"
 #include "launch.hpp"
@@ -69,6 +70,46 @@ Layout layout_of(const qmoe_moe_layer& L, int T) {
 
 size_t moe_workspace_bytes(const qmoe_moe_layer& L, int max_tokens) {
     return layout_of(L, max_tokens).total;
+}
+
+}  // namespace qmoe
+
+// Workspace of the allocation-free layer call: one copy per device, held from the first
+// call on that device until the process ends.  Host code never uses this name as an
+// address (on the host it is a stand-in, not device memory); it uses the device address
+// that moe_noalloc_scratch() looks up once per device.
+static __device__ __align__(256) unsigned char scratch[qmoe::MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace qmoe {
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[MAX_DEVICES];
+}  // namespace
+
+hipError_t moe_noalloc_scratch(hipStream_t s, void** ptr) {
+    int dev = 0;
+    hipError_t e = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        int cur = 0;
+        if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch[dev] = p;
+    }
+    *ptr = g_scratch[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_moe(const qmoe_moe_layer& L, int stage, const uint16_t* x, int T,

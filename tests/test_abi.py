@@ -29,7 +29,7 @@ def test_header_declares_the_four_calls():
 def test_every_declared_function_is_exported():
     lib = ctypes.CDLL(q.LIB_PATH)
     names = declared_functions()
-    assert len(names) == 18
+    assert len(names) == 19
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.EXPORTED)
@@ -242,3 +242,19 @@ def test_moe_rejects_misaligned_parameters_and_index_arrays():
     g = q.lib.qlinear_int4
     w = _lib.QWeightC(FAKE, FAKE + 4, FAKE, 512, 2048, 4, 64, 1, 0)
     assert g(FAKE, 1, ctypes.byref(w), None, None, FAKE * 8, None) == _lib.QMOE_ERR_MISALIGNED
+
+
+def test_noalloc_rejects_what_its_scratch_cannot_hold():
+    """The allocation-free call validates like the layer call and rejects a token count whose
+    workspace exceeds the fixed scratch (QMOE_NOALLOC_SCRATCH_BYTES) before any device work."""
+    f = q.lib.moe_switchglu_int4_noalloc
+    L = layer_c()
+    X, Y = FAKE, FAKE * 4096
+    assert q.lib.moe_switchglu_int4_workspace_bytes(ctypes.byref(L), 512) <= _lib.NOALLOC_SCRATCH_BYTES
+    assert q.lib.moe_switchglu_int4_workspace_bytes(ctypes.byref(L), 1024) > _lib.NOALLOC_SCRATCH_BYTES
+    assert f(ctypes.byref(L), X, 1024, None, Y, None, None, None) == _lib.QMOE_ERR_WORKSPACE
+    assert b"scratch" in q.lib.qmoe_last_error()
+    assert f(ctypes.byref(L), None, 1, None, Y, None, None, None) == _lib.QMOE_ERR_INVALID_ARG
+    assert f(ctypes.byref(L), X, 1, None, X, None, None, None) == _lib.QMOE_ERR_INVALID_ARG
+    assert f(ctypes.byref(L), X + 2, 1, None, Y, None, None, None) == _lib.QMOE_ERR_MISALIGNED
+    assert f(ctypes.byref(layer_c(top_k=0)), X, 1, None, Y, None, None, None) == _lib.QMOE_ERR_INVALID_ARG
