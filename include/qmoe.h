@@ -256,6 +256,22 @@ int moe_switchglu_int4_stage(const qmoe_moe_layer* L, int32_t stage, const uint1
                              void* stream);
 
 /*
+ * The same layer under a routing given by the caller instead of the router's top-K: token
+ * t runs experts route_idx[t][0 .. top_k-1] (device int32 [t x top_k]).  This is the
+ * prerouter's use ("Edge0 project review", highlight 1): the head of layer N predicts, at
+ * token t-1, the experts of layer N+1 for token t, and that prediction is the route itself
+ * (the staged experts are exactly the predicted set), so the expert loads need not wait for
+ * the router.  The router still runs: the routing weights are the softmax of its logits
+ * (+ router_bias) over the given set, w_k = exp(l_k - m) / sum_j exp(l_j - m), written to
+ * w_out (fp32 [t x top_k]) when it is not NULL.  Entries outside [0, n_experts) are clamped
+ * into it; an expert given twice counts twice.  Workspace, limits and the rest of the
+ * output as moe_switchglu_int4.  Up to 32 (token, expert) pairs this is two launches.
+ */
+int moe_switchglu_int4_routed(const qmoe_moe_layer* L, const uint16_t* x, int32_t t,
+                              const int32_t* adapter_idx, const int32_t* route_idx, uint16_t* y,
+                              float* w_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * For callers that cannot allocate device memory (code under HIP graph capture, tight
  * serving loops, harnesses that forbid hipMalloc): moe_switchglu_int4 with its workspace in
  * a fixed scratch array inside the library instead of a caller buffer.  Same arguments,

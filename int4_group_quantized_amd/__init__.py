@@ -24,6 +24,7 @@ from .api import (  # noqa: F401
     lora_apply,
     moe_switchglu_int4,
     moe_switchglu_int4_noalloc,
+    moe_switchglu_int4_routed,
     moe_workspace,
     moe_workspace_bytes,
     qlinear_int4,

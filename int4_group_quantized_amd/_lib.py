@@ -76,6 +76,8 @@ _SIGS = {
     "moe_switchglu_int4_stage": (ctypes.c_int, [ctypes.POINTER(MoELayerC), _I, _P, _I, _P, _P, _P,
                                                 _P, _P, ctypes.c_size_t, _P]),
     "moe_switchglu_int4_noalloc": (ctypes.c_int, [ctypes.POINTER(MoELayerC), _P, _I, _P, _P, _P, _P, _P]),
+    "moe_switchglu_int4_routed": (ctypes.c_int, [ctypes.POINTER(MoELayerC), _P, _I, _P, _P, _P, _P, _P,
+                                                 ctypes.c_size_t, _P]),
     "qmoe_quantize_supergroup": (ctypes.c_int, [_P, _I, _I, _I, _P, _P, _P, _P]),
     "qlinear_supergroup": (ctypes.c_int, [_P, _I, _P, _P, _P, _I, _I, _I, _P, _P]),
     "qmoe_quantize_act8": (ctypes.c_int, [_P, _I, _I, _P, _P, _P]),

@@ -253,7 +253,7 @@ def moe_workspace(layer: MoELayer, max_tokens: int, device="cuda") -> torch.Tens
 
 def _moe_io(layer: MoELayer, x: torch.Tensor, y: torch.Tensor,
             adapter_idx: Optional[torch.Tensor], idx_out: Optional[torch.Tensor],
-            w_out: Optional[torch.Tensor]) -> int:
+            w_out: Optional[torch.Tensor], idx_name: str = "idx_out") -> int:
     """Check the per-call tensors of a layer call (the C layer cannot see buffer sizes) and
     return the token count."""
     _dev(x, torch.float16, "x")
@@ -262,7 +262,7 @@ def _moe_io(layer: MoELayer, x: torch.Tensor, y: torch.Tensor,
         raise ValueError(f"x and y must be [t, {layer.hidden}], got {tuple(x.shape)} and {tuple(y.shape)}")
     t = x.shape[0]
     for name, v, dt, n in (("adapter_idx", adapter_idx, torch.int32, t),
-                           ("idx_out", idx_out, torch.int32, t * layer.top_k),
+                           (idx_name, idx_out, torch.int32, t * layer.top_k),
                            ("w_out", w_out, torch.float32, t * layer.top_k)):
         if v is not None:
             _dev(v, dt, name)
@@ -293,6 +293,26 @@ def moe_switchglu_int4(layer: MoELayer, x: torch.Tensor,
                                  y.data_ptr(), _ptr(idx), _ptr(w), ws.data_ptr(), ws.numel(),
                                  _stream(x)), "moe_switchglu_int4")
     return (y, idx, w) if return_routing else y
+
+
+def moe_switchglu_int4_routed(layer: MoELayer, x: torch.Tensor, route: torch.Tensor,
+                              adapter_idx: Optional[torch.Tensor] = None,
+                              ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                              w_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The layer under a given routing route int32 [t, top_k] (e.g. the prerouter head's
+    prediction); w_out (fp32 [t, top_k]) receives the routing weights when given."""
+    y = out if out is not None else torch.empty_like(x)
+    if route is None:
+        raise ValueError("route is required")
+    t = _moe_io(layer, x, y, adapter_idx, route, w_out, "route")
+    if ws is None:
+        ws = moe_workspace(layer, t, x.device)
+    _dev(ws, torch.uint8, "ws")
+    c = layer.c()
+    check(lib.moe_switchglu_int4_routed(ctypes.byref(c), x.data_ptr(), t, _ptr(adapter_idx),
+                                        route.data_ptr(), y.data_ptr(), _ptr(w_out), ws.data_ptr(),
+                                        ws.numel(), _stream(x)), "moe_switchglu_int4_routed")
+    return y
 
 
 def moe_switchglu_int4_noalloc(layer: MoELayer, x: torch.Tensor,

@@ -209,6 +209,23 @@ int moe_switchglu_int4_stage(const qmoe_moe_layer* L, int32_t stage, const uint1
                                        as_stream(stream)));
 }
 
+int moe_switchglu_int4_routed(const qmoe_moe_layer* L, const uint16_t* x, int32_t t,
+                              const int32_t* adapter_idx, const int32_t* route_idx, uint16_t* y,
+                              float* w_out, void* ws, size_t ws_bytes, void* stream) {
+    if (!x || !y || !route_idx || t <= 0) return QMOE_ERR_INVALID_ARG;
+    if (t > 65536) return QMOE_ERR_UNSUPPORTED;
+    int st = check_layer(L);
+    if (st) return st;
+    if (!aligned16(x) || !aligned16(y)) return QMOE_ERR_MISALIGNED;
+    if (!aligned4(adapter_idx) || !aligned4(route_idx) || !aligned4(w_out)) return QMOE_ERR_MISALIGNED;
+    const size_t xb = (size_t)t * L->hidden * 2;
+    if (overlap(x, xb, y, xb)) return QMOE_ERR_INVALID_ARG;
+    if (!ws || ws_bytes < qmoe::moe_workspace_bytes(*L, t)) return QMOE_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return QMOE_ERR_MISALIGNED;
+    return hip_status(qmoe::launch_moe(*L, QMOE_STAGE_ALL, x, t, adapter_idx, y, nullptr, w_out, ws,
+                                       as_stream(stream), route_idx));
+}
+
 int moe_switchglu_int4_noalloc(const qmoe_moe_layer* L, const uint16_t* x, int32_t t,
                                const int32_t* adapter_idx, uint16_t* y, int32_t* idx_out,
                                float* w_out, void* stream) {

@@ -41,9 +41,10 @@ size_t moe_workspace_bytes(const qmoe_moe_layer& L, int max_tokens);
 // device address looked up on the first call on the stream's device
 constexpr size_t MOE_NOALLOC_SCRATCH_BYTES = (size_t)32 << 20;
 hipError_t moe_noalloc_scratch(hipStream_t s, void** ptr);
+// route: a given selection [t][top_k] (the caller's routing) in place of the top-K, or null
 hipError_t launch_moe(const qmoe_moe_layer& L, int stage, const uint16_t* x, int t,
                       const int32_t* adapter_idx, uint16_t* y, int32_t* idx_out,
-                      float* w_out, void* ws, hipStream_t s);
+                      float* w_out, void* ws, hipStream_t s, const int32_t* route = nullptr);
 
 // supergroup.hip
 hipError_t launch_qlinear_supergroup(const uint16_t* x, int b, const uint32_t* p4,

@@ -13,7 +13,7 @@
 //
 // Two launch sequences on the caller's stream, neither with a host synchronisation:
 //   decode (moe_decode.hip, up to 32 tokens): three launches, top-K once per token inside
-//     the gate/up kernel;
+//     the gate/up kernel; with a routing given by the caller, two;
 //   prefill (moe_prefill.hip, any count): router / shared-expert GEMMs on MFMA, top-K, a
 //     stable sort of the (token, k) pairs by expert, grouped expert GEMMs, combine.
 // This file owns the workspace layout and the choice between the two.
@@ -114,7 +114,7 @@ hipError_t moe_noalloc_scratch(hipStream_t s, void** ptr) {
 
 hipError_t launch_moe(const qmoe_moe_layer& L, int stage, const uint16_t* x, int T,
                       const int32_t* adapter_idx, uint16_t* y, int32_t* idx_out,
-                      float* w_out, void* ws, hipStream_t s) {
+                      float* w_out, void* ws, hipStream_t s, const int32_t* route) {
     const Layout lo = layout_of(L, T);
     char* base = static_cast<char*>(ws);
     MoeArgs a{};
@@ -148,6 +148,7 @@ hipError_t launch_moe(const qmoe_moe_layer& L, int stage, const uint16_t* x, int
     a.os = reinterpret_cast<float*>(base + lo.os);
     a.idx_out = idx_out;
     a.w_out = w_out;
+    a.route = route;
     if (decode_path_fits(L, T)) return launch_moe_decode(a, stage, s);
     return launch_moe_prefill(a, stage, s);
 }

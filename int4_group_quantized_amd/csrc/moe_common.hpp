@@ -33,6 +33,7 @@ struct MoeArgs {
     int nag, nau, nad;  // adapters per projection
     float lsg, lsu, lsd;
     const float* rbias;
+    const int32_t* route;   // given selection [T][K] (the caller's routing), or null: top-K
     // workspace
     float *logits, *gate, *zg, *zu, *zd, *gs, *us;
     int32_t* idx;
@@ -100,6 +101,24 @@ __device__ __forceinline__ float lora_b_dot(const uint16_t* __restrict__ B, int 
     return d;
 }
 
+
+// LoRA-B term of one output row from 16 rank entries held as two uint4 (entries r < rank
+// count), z from LDS.
+__device__ __forceinline__ float bdot16(const uint4 (&v)[2], const float* z, int rank) {
+    float d = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        if (8 * i < rank) {
+            const uint32_t w4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                d = fmaf(half_lo(w4[j]), z[8 * i + 2 * j], d);
+                d = fmaf(half_hi(w4[j]), z[8 * i + 2 * j + 1], d);
+            }
+        }
+    }
+    return d;
+}
 
 // z[r] = A[r] . v for r < rank (A fp16 [rank][K] row-major, v fp16 [K]), whole block: one
 // 16-lane DPP row per rank row, each lane a K/16 slice (K a multiple of 128), so all loads

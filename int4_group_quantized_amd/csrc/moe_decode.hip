@@ -69,21 +69,22 @@ __device__ __forceinline__ void xside_rows(const MoeArgs& a, const QW& w, int n,
     }
 }
 
-__global__ void __launch_bounds__(256) k_dec_xside(MoeArgs a) {
-    __shared__ __align__(16) f16x2 xs[8192];   // 32 KB: 8192 / (hidden / 2) tokens per pass
-    __shared__ float xsum[MT * 128];
-    // every argument field of the kernel in one batch of scalar loads (one round trip)
-    asm volatile("" ::"s"(a.router.p), "s"(a.router.s), "s"(a.router.b), "s"(a.x), "s"(a.shg.p),
-                 "s"(a.shg.s), "s"(a.shg.b), "s"(a.logits), "s"(a.shu.p), "s"(a.shu.s), "s"(a.shu.b),
-                 "s"(a.gs), "s"(a.us), "s"(a.T), "s"(a.H), "s"(a.E), "s"(a.SI), "s"(a.Ep), "s"(a.Ag),
-                 "s"(a.Au), "s"(a.rg), "s"(a.ru), "s"(a.gate), "s"(a.sgate.p), "s"(a.sgate.s),
-                 "s"(a.sgate.b), "s"(a.zg), "s"(a.zu));
+// Every argument field of the x side in one batch of scalar loads (one round trip).
+#define QMOE_XSIDE_ARGS()                                                                        \
+    asm volatile("" ::"s"(a.router.p), "s"(a.router.s), "s"(a.router.b), "s"(a.x), "s"(a.shg.p), \
+                 "s"(a.shg.s), "s"(a.shg.b), "s"(a.logits), "s"(a.shu.p), "s"(a.shu.s),         \
+                 "s"(a.shu.b), "s"(a.gs), "s"(a.us), "s"(a.T), "s"(a.H), "s"(a.E), "s"(a.SI),   \
+                 "s"(a.Ep), "s"(a.Ag), "s"(a.Au), "s"(a.rg), "s"(a.ru), "s"(a.gate),            \
+                 "s"(a.sgate.p), "s"(a.sgate.s), "s"(a.sgate.b), "s"(a.zg), "s"(a.zu))
+
+// Block b of the x side: router rows, the shared-gate row, the shared expert's raw gate/up
+// rows, or LoRA z jobs.
+__device__ __forceinline__ void xside_block(const MoeArgs& a, int b, f16x2* xs, float* xsum) {
     const int H = a.H;
     const int zjobs = (a.Ag ? a.T * a.rg : 0) + (a.Au ? a.T * a.ru : 0);
     const XsideGrid g = xside_grid(a.T, H, a.E, a.SI, zjobs);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lpr = lanes_per_row(H), rpw = 64 / lpr, seg = lane / lpr;
-    const int b = blockIdx.x;
 
     if (b >= g.nb_router + g.nb_gate + g.nb_shared) {
         xside_lora_z(a, (b - g.nb_router - g.nb_gate - g.nb_shared) * 4 + wave, zjobs);
@@ -104,6 +105,19 @@ __global__ void __launch_bounds__(256) k_dec_xside(MoeArgs a) {
         const bool up = rr >= a.SI;
         xside_rows<4>(a, up ? a.shu : a.shg, up ? rr - a.SI : rr, ok, up ? a.us : a.gs, a.SI, xs, xsum, 8192);
     }
+}
+
+__global__ void __launch_bounds__(256) k_dec_xside(MoeArgs a) {
+    __shared__ __align__(16) f16x2 xs[8192];   // 32 KB: 8192 / (hidden / 2) tokens per pass
+    __shared__ float xsum[MT * 128];
+    QMOE_XSIDE_ARGS();
+    xside_block(a, blockIdx.x, xs, xsum);
+}
+
+int xside_blocks(const MoeArgs& a) {
+    const int zjobs = (a.Ag ? a.T * a.rg : 0) + (a.Au ? a.T * a.ru : 0);
+    const XsideGrid g = xside_grid(a.T, a.H, a.E, a.SI, zjobs);
+    return g.nb_router + g.nb_gate + g.nb_shared + g.nb_z;
 }
 
 // ------------------------------------------------------------------------------ D2 gate/up
@@ -185,16 +199,80 @@ __global__ void __launch_bounds__(256) k_dec_gate_up(MoeArgs a) {
     }
 }
 
+// The x side and the routed gate/up of a GIVEN routing in one launch (the caller's selection,
+// e.g. the prerouter head's prediction, which is then the route itself: "Edge0 project
+// review", highlight 1).  Blocks below nx are x-side blocks; every other block is one
+// (row block, pair) of the routed gate/up: it reads its expert from the given routing at
+// entry and issues that expert's gate and up rows at once, so no block waits for another
+// and the router's logits are needed only by the down launch (the routing weights).  The
+// shared expert's h_s, which needs the x side's LoRA z's, is finished by the down launch.
+__global__ void __launch_bounds__(256) k_dec_rt_gate_up(MoeArgs a, int nx) {
+    __shared__ __align__(16) f16x2 xs[8192];
+    __shared__ float xsum[MT * 128];
+    if ((int)blockIdx.x < nx) {
+        QMOE_XSIDE_ARGS();
+        xside_block(a, blockIdx.x, xs, xsum);
+        return;
+    }
+    QMOE_SGPR_USE4(a.route, a.x, a.eg.p, a.eg.s);
+    QMOE_SGPR_USE4(a.eg.b, a.eu.p, a.eu.s, a.eu.b);
+    QMOE_SGPR_USE4(a.h, a.H, a.I, a.E);
+    const int H = a.H, I = a.I;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lpr = lanes_per_row(H), rpw = 64 / lpr, seg = lane / lpr, sl = lane % lpr;
+    const int rows_per_block = 4 * rpw * GU_RPW;
+    const int nrb = (I + rows_per_block - 1) / rows_per_block;
+    const int b = blockIdx.x - nx;
+    const int pair = b / nrb, bx = b % nrb;
+    const int t = pair / a.K;
+    const int e = clamp_expert(a.route[pair], a.E);
+    const uint4* xt = reinterpret_cast<const uint4*>(a.x + (long)t * H);
+    StageRegs<4, 2> st;
+    st.load([=](int) { return xt; }, 1, H);
+    RowRegs<4, 2> rg[GU_RPW], ru[GU_RPW];
+    int n[GU_RPW];
+#pragma unroll
+    for (int j = 0; j < GU_RPW; ++j) {
+        n[j] = bx * rows_per_block + (j * 4 + wave) * rpw + seg;
+        const bool ok = n[j] < I;
+        const long row = (long)e * I + (ok ? n[j] : 0);
+        rg[j].load(a.eg.p, a.eg.s, a.eg.b, H, row, lpr, sl, ok);
+        ru[j].load(a.eu.p, a.eu.s, a.eu.b, H, row, lpr, sl, ok);
+    }
+    st.commit(1, H, xs, xsum);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < GU_RPW; ++j) {
+        float ag[MT], au[MT];
+        ag[0] = au[0] = 0.0f;
+        rg[j].dot(H, lpr, sl, xs, xsum, 1, ag);
+        ru[j].dot(H, lpr, sl, xs, xsum, 1, au);
+        const float gv = segment_sum(ag[0], lpr), uv = segment_sum(au[0], lpr);
+        if (sl == 0 && n[j] < I) a.h[(long)pair * I + n[j]] = f2h(silu(gv) * uv);
+    }
+}
+
 // ------------------------------------------------------------------------------ D3 down
 
 constexpr int DN_ROWS = 8;     // output rows per block
 constexpr int DN_ITEMS = 4;    // (matrix, row) items per lane segment per pass
 constexpr int DN_STAGE = 3;    // 16-byte staging loads per thread: (K + 1) * inter / 8 <= 768
 
+// ROUTED: the routing is the caller's (a.route): the experts come from it, the weights are
+// the softmax of the router logits over it, and h_s is finished here from the x side's raw
+// shared gate/up sums and LoRA z's (k_dec_rt_gate_up leaves them), not loaded.
+template <bool ROUTED>
 __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
     // staged activations: the token's K routed h rows and h_s (as matrix K), pair layout
     __shared__ __align__(16) f16x2 hs_l[(MAX_DEC_K + 1) * 1024];   // inter <= 2048
-    QMOE_SGPR_USE4(a.idx, a.wts, a.h, a.hs);
+    __shared__ __align__(16) uint16_t hsc[ROUTED ? 2048 : 8];      // h_s in input order (ROUTED)
+    if constexpr (ROUTED) {
+        QMOE_SGPR_USE4(a.route, a.logits, a.h, a.gs);
+        QMOE_SGPR_USE4(a.us, a.zg, a.zu, a.Bg);
+        QMOE_SGPR_USE4(a.Bu, a.E, a.Ep, a.rbias);
+    } else {
+        QMOE_SGPR_USE4(a.idx, a.wts, a.h, a.hs);
+    }
     QMOE_SGPR_USE4(a.ed.p, a.ed.s, a.ed.b, a.shd.p);
     QMOE_SGPR_USE4(a.shd.s, a.shd.b, a.Ad, a.Bd);
     QMOE_SGPR_USE4(a.gate, a.x, a.y, a.adapter);
@@ -207,7 +285,13 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
     const int t = blockIdx.y;
     const int n0 = blockIdx.x * DN_ROWS;
     const int lpr = lanes_per_row(Kd), rpw = 64 / lpr, seg = lane / lpr, sl = lane % lpr;
-    const bool one_pass = (K + 1) * (Kd / 8) <= 256 * DN_STAGE;
+    const int n_staged = ROUTED ? K : K + 1;   // rows staged from memory
+    const bool one_pass = n_staged * (Kd / 8) <= 256 * DN_STAGE;
+    // expert of routing entry m (< K) of token t
+    auto expert_of = [&](int m) {
+        if constexpr (ROUTED) return clamp_expert(a.route[(long)t * K + m], a.E);
+        else return a.idx[(long)t * K + m];
+    };
 
     // phase 1: the routing decision (published by the gate/up stage), the K + 1 activation
     // rows and the LoRA A_down slices in flight together.  Each lane loads the expert of its
@@ -223,17 +307,52 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
 #pragma unroll
     for (int i = 0; i < DN_ITEMS; ++i) {
         const int m = min(i * slots + slot, n_items - 1) / DN_ROWS;
-        eit[i] = a.idx[(long)t * K + min(m, K - 1)];
+        eit[i] = expert_of(min(m, K - 1));
     }
     float selw[MAX_DEC_K];
+    if constexpr (ROUTED) {
+        float lg[MAX_DEC_K];
 #pragma unroll
-    for (int r = 0; r < MAX_DEC_K; ++r) selw[r] = a.wts[(long)t * K + min(r, K - 1)];
-    const uint16_t* hsrow = a.hs + (long)t * Kd;
+        for (int r = 0; r < MAX_DEC_K; ++r) {
+            const int e = expert_of(min(r, K - 1));
+            lg[r] = a.logits[(long)t * a.Ep + e];
+            if (a.rbias) lg[r] += a.rbias[e];
+        }
+        given_softmax<MAX_DEC_K>(K, lg, selw);
+    } else {
+#pragma unroll
+        for (int r = 0; r < MAX_DEC_K; ++r) selw[r] = a.wts[(long)t * K + min(r, K - 1)];
+    }
+    const uint16_t* hsrow = ROUTED ? hsc : a.hs + (long)t * Kd;
     const uint4* hbase4 = reinterpret_cast<const uint4*>(a.h + (long)t * K * Kd);
     const uint4* hsrow4 = reinterpret_cast<const uint4*>(hsrow);
     auto rowp = [=](int m) { return m < K ? hbase4 + (long)m * (Kd / 8) : hsrow4; };
     StageRegs<4, DN_STAGE> st;
-    if (one_pass) st.load(rowp, K + 1, Kd);
+    if (one_pass) st.load(rowp, n_staged, Kd);
+    // ROUTED: the raw shared gate/up sums of this thread's h_s outputs and, for ranks of at
+    // most 16 in multiples of 8, their LoRA-B rows, loaded before the expert rows
+    constexpr int HSN = ROUTED ? 2 : 1;    // h_s outputs per thread loaded here (the rest later)
+    float gsv[HSN], usv[HSN];
+    uint4 bgv[HSN][2], buv[HSN][2];
+    const int adg = ROUTED ? adapter_of(a.adapter, t, a.nag) : 0;
+    const int adu = ROUTED ? adapter_of(a.adapter, t, a.nau) : 0;
+    const bool bgf = ROUTED && a.Bg && (a.rg & 7) == 0 && a.rg <= 16;
+    const bool buf = ROUTED && a.Bu && (a.ru & 7) == 0 && a.ru <= 16;
+    if constexpr (ROUTED) {
+#pragma unroll
+        for (int j = 0; j < HSN; ++j) {
+            const int n = min((int)threadIdx.x + j * NT, Kd - 1);
+            gsv[j] = a.gs[(long)t * Kd + n];
+            usv[j] = a.us[(long)t * Kd + n];
+            const uint16_t* gb = bgf ? a.Bg + ((long)adg * Kd + n) * a.rg : a.x;
+            const uint16_t* ub = buf ? a.Bu + ((long)adu * Kd + n) * a.ru : a.x;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                bgv[j][i] = *reinterpret_cast<const uint4*>(gb + (bgf ? min(8 * i, a.rg - 8) : 0));
+                buv[j][i] = *reinterpret_cast<const uint4*>(ub + (buf ? min(8 * i, a.ru - 8) : 0));
+            }
+        }
+    }
     constexpr int ZI = 4;                      // A_down slice: Kd/16 <= 32 inputs per lane
     const int lane16 = threadIdx.x & 15, zrow = threadIdx.x >> 4;
     const int zper = Kd / 16;
@@ -274,7 +393,7 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
             const int m = ic / DN_ROWS, r = ic % DN_ROWS;
             const bool ok = item < n_items && n0 + r < H;
             const int nn = ok ? n0 + r : 0;
-            const int e = base == 0 ? eit[i] : a.idx[(long)t * K + min(m, K - 1)];
+            const int e = base == 0 ? eit[i] : expert_of(min(m, K - 1));
             mi[i] = ok ? m : -1;
             ri[i] = r;
             const bool routed = m < K;
@@ -285,8 +404,37 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
     };
     load_items(0);
     // phase 3: activations to LDS
-    if (one_pass) st.commit(K + 1, Kd, hs_l, hsum);
-    else stage_rows<4, 4>(rowp, K + 1, Kd, hs_l, hsum);
+    if constexpr (ROUTED) {
+        // h_s = silu(g_s + LoRA_g) * (u_s + LoRA_u), as the shared gate/up blocks of the
+        // top-K path take it
+        const float* zg = a.zg + (long)t * MAX_RANK;
+        const float* zu = a.zu + (long)t * MAX_RANK;
+#pragma unroll
+        for (int j = 0; j < HSN; ++j) {
+            const int n = threadIdx.x + j * NT;
+            if (n < Kd) {
+                float gv = gsv[j], uv = usv[j];
+                if (a.Bg) gv = fmaf(a.lsg, bgf ? bdot16(bgv[j], zg, a.rg) : lora_b_dot(a.Bg, adg, Kd, n, a.rg, zg), gv);
+                if (a.Bu) uv = fmaf(a.lsu, buf ? bdot16(buv[j], zu, a.ru) : lora_b_dot(a.Bu, adu, Kd, n, a.ru, zu), uv);
+                hsc[n] = f2h(silu(gv) * uv);
+            }
+        }
+        for (int n = threadIdx.x + HSN * NT; n < Kd; n += NT) {   // inter above 512
+            float gv = a.gs[(long)t * Kd + n], uv = a.us[(long)t * Kd + n];
+            if (a.Bg) gv = fmaf(a.lsg, lora_b_dot(a.Bg, adg, Kd, n, a.rg, zg), gv);
+            if (a.Bu) uv = fmaf(a.lsu, lora_b_dot(a.Bu, adu, Kd, n, a.ru, zu), uv);
+            hsc[n] = f2h(silu(gv) * uv);
+        }
+    }
+    if (one_pass) st.commit(n_staged, Kd, hs_l, hsum);
+    else stage_rows<4, 4>(rowp, n_staged, Kd, hs_l, hsum);
+    if constexpr (ROUTED) {
+        __syncthreads();
+        // h_s as staged row K (Kd / 8 <= NT units: one per thread)
+        const int u = threadIdx.x;
+        const uint4 raw = reinterpret_cast<const uint4*>(hsc)[min(u, Kd / 8 - 1)];
+        commit_unit<4>(raw, K * (Kd / 8) + u, u < Kd / 8, hs_l, hsum);
+    }
     __syncthreads();
     // z_down = A_down[ad] . h_s[t], from the staged h_s in the pair order of A's registers
     if (zfast) {
@@ -355,6 +503,11 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
             a.y[(long)t * H + n] = outv;
         }
     }
+    if (ROUTED && a.w_out && blockIdx.x == 0 && threadIdx.x == 0) {
+#pragma unroll
+        for (int k = 0; k < MAX_DEC_K; ++k)
+            if (k < K) a.w_out[(long)t * K + k] = selw[k];
+    }
 }
 
 }  // namespace
@@ -374,10 +527,17 @@ bool decode_path_fits(const qmoe_moe_layer& L, int T) {
 }
 
 hipError_t launch_moe_decode(const MoeArgs& a, int stage, hipStream_t s) {
-    const int zjobs = (a.Ag ? a.T * a.rg : 0) + (a.Au ? a.T * a.ru : 0);
-    const XsideGrid g = xside_grid(a.T, a.H, a.E, a.SI, zjobs);
+    const int nx = xside_blocks(a);
+    if (a.route) {   // the caller's routing: two launches
+        const int rpb = 4 * (64 / lanes_per_row(a.H)) * GU_RPW;
+        const int nrb = (a.I + rpb - 1) / rpb;
+        k_dec_rt_gate_up<<<(unsigned)(nx + nrb * a.T * a.K), 256, 0, s>>>(a, nx);
+        dim3 grid((unsigned)((a.H + DN_ROWS - 1) / DN_ROWS), (unsigned)a.T);
+        k_dec_down<true><<<grid, 256, 0, s>>>(a);
+        return hipGetLastError();
+    }
     if (stage == QMOE_STAGE_ALL || stage == QMOE_STAGE_ROUTE)
-        k_dec_xside<<<g.nb_router + g.nb_gate + g.nb_shared + g.nb_z, 256, 0, s>>>(a);
+        k_dec_xside<<<nx, 256, 0, s>>>(a);
     const int per = topk_per_lane(a.E);
     if (stage == QMOE_STAGE_ALL || stage == QMOE_STAGE_GATE_UP) {
         const int rpb = 4 * (64 / lanes_per_row(a.H)) * GU_RPW;
@@ -392,7 +552,7 @@ hipError_t launch_moe_decode(const MoeArgs& a, int stage, hipStream_t s) {
     }
     if (stage == QMOE_STAGE_ALL || stage == QMOE_STAGE_DOWN) {
         dim3 grid((unsigned)((a.H + DN_ROWS - 1) / DN_ROWS), (unsigned)a.T);
-        k_dec_down<<<grid, 256, 0, s>>>(a);
+        k_dec_down<false><<<grid, 256, 0, s>>>(a);
     }
     return hipGetLastError();
 }

@@ -908,22 +908,30 @@ __device__ void token_topk(const MoeArgs& a, int t, int ksplit, int* sel, float*
     keys.select(a.E, a.K, sel, sw);
 }
 
-// LoRA-B term of one output row from 16 rank entries held as two uint4 (entries r < rank
-// count), z from LDS.
-__device__ __forceinline__ float bdot16(const uint4 (&v)[2], const float* z, int rank) {
-    float d = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        if (8 * i < rank) {
-            const uint32_t w4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                d = fmaf(half_lo(w4[j]), z[8 * i + 2 * j], d);
-                d = fmaf(half_hi(w4[j]), z[8 * i + 2 * j + 1], d);
-            }
-        }
+// Wave 0 of k_pf_token for a given routing (the caller's selection): lane k < K takes
+// expert k of the token's routing (clamped) and its logit (split-K partials plus the bias);
+// the weights are the softmax over the K, with the operations and order of given_softmax
+// (maximum and sum taken lane by lane in selection order).  Lanes 0 .. K-1 leave the experts
+// and weights in sel / sw.
+template <int KP>
+__device__ void token_given(const MoeArgs& a, int t, int ksplit, int* sel, float* sw) {
+    const int lane = threadIdx.x & 63, K = a.K;
+    const int e = clamp_expert(a.route[(long)t * K + min(lane, K - 1)], a.E);
+    Parts<KP> p;
+    p.load(a.logits + (long)t * a.Ep + e, (long)a.T * a.Ep, ksplit);
+    float l = p.sum(ksplit);
+    if (a.rbias) l += a.rbias[e];
+    float m = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l), 0));
+    for (int i = 1; i < K; ++i)
+        m = fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l), i)));
+    const float ex = expf(l - m);
+    float total = 0.0f;
+    for (int i = 0; i < K; ++i)
+        total += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ex), i));
+    if (lane < K) {
+        sel[lane] = e;
+        sw[lane] = ex / total;
     }
-    return d;
 }
 
 // The remaining rank entries 16 .. rank - 1 (rank a multiple of 8) of the same dot.
@@ -979,7 +987,8 @@ __device__ __forceinline__ void pf_token_body(const MoeArgs& a, int ksplit) {
     }
 
     if (wave == 0) {
-        token_topk<PER, KP>(a, t, ksplit, sel, sw);
+        if (a.route) token_given<KP>(a, t, ksplit, sel, sw);
+        else token_topk<PER, KP>(a, t, ksplit, sel, sw);
     } else {
         const int w = wave - 1, u = threadIdx.x - 64;
         Parts<KP> g;   // the shared-gate logit (every lane loads, one stores)

@@ -150,6 +150,29 @@ struct TopkKeys {
     }
 };
 
+// Weights of a given selection (the caller's routing, not the top-K): the softmax over its k
+// logits l[0..k-1] (bias included), relative to their largest and summed in selection order,
+// w[i] = exp(l_i - m) / sum_j exp(l_j - m).  Register form, one thread taking all k; the
+// prefill per-token kernel takes the same operations in the same order across a wave's lanes,
+// so both paths give the same bits for the same logits.
+template <int MAXK>
+__device__ __forceinline__ void given_softmax(int k, const float (&l)[MAXK], float (&w)[MAXK]) {
+    float m = l[0];
+#pragma unroll
+    for (int i = 1; i < MAXK; ++i)
+        if (i < k) m = fmaxf(m, l[i]);
+    float total = 0.0f;
+#pragma unroll
+    for (int i = 0; i < MAXK; ++i)
+        if (i < k) total += expf(l[i] - m);
+#pragma unroll
+    for (int i = 0; i < MAXK; ++i) w[i] = i < k ? expf(l[i] - m) / total : 0.0f;
+}
+
+// Expert e of a given selection clamped into [0, n), so an out-of-range index can never
+// address memory outside the expert stack.
+__device__ __forceinline__ int clamp_expert(int e, int n) { return e < 0 ? 0 : (e >= n ? n - 1 : e); }
+
 // Logits per lane needed for e experts (1, 2, 4, 8 or 16).
 __host__ __device__ inline int topk_per_lane(int e) {
     return e <= 64 ? 1 : e <= 128 ? 2 : e <= 256 ? 4 : e <= 512 ? 8 : 16;

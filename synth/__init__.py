@@ -107,6 +107,14 @@ def uniform_f16(shape, lo: float, hi: float, workload: int, layer: int, role: in
     return g.uniform(lo, hi, size=shape).astype(np.float16)
 
 
+def expert_choices(tokens: int, k: int, n_experts: int, workload: int, layer: int = 0,
+                   index: int = 0) -> np.ndarray:
+    """A routing drawn at random: for each token, k distinct experts of n_experts, int32
+    [tokens x k] (stands in for a routing the caller supplies, e.g. a predicted one)."""
+    g = rng(workload, layer, Role.MISC, 1000 + index)
+    return np.stack([g.choice(n_experts, k, replace=False) for _ in range(tokens)]).astype(np.int32)
+
+
 def adapter_index(tokens: int, tokens_per_adapter: int) -> np.ndarray:
     """Per-token adapter id: token t is served by adapter t // tokens_per_adapter."""
     return (np.arange(tokens, dtype=np.int32) // np.int32(tokens_per_adapter)).astype(np.int32)

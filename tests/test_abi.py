@@ -29,7 +29,7 @@ def test_header_declares_the_four_calls():
 def test_every_declared_function_is_exported():
     lib = ctypes.CDLL(q.LIB_PATH)
     names = declared_functions()
-    assert len(names) == 19
+    assert len(names) == 20
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.EXPORTED)
@@ -258,3 +258,15 @@ def test_noalloc_rejects_what_its_scratch_cannot_hold():
     assert f(ctypes.byref(L), X, 1, None, X, None, None, None) == _lib.QMOE_ERR_INVALID_ARG
     assert f(ctypes.byref(L), X + 2, 1, None, Y, None, None, None) == _lib.QMOE_ERR_MISALIGNED
     assert f(ctypes.byref(layer_c(top_k=0)), X, 1, None, Y, None, None, None) == _lib.QMOE_ERR_INVALID_ARG
+
+
+def test_routed_call_validates_like_the_layer_call():
+    f = q.lib.moe_switchglu_int4_routed
+    L = layer_c()
+    ws1 = q.lib.moe_switchglu_int4_workspace_bytes(ctypes.byref(L), 1)
+    X, Y, R, WS = FAKE, FAKE * 16, FAKE * 32, FAKE * 64
+    assert f(ctypes.byref(L), X, 1, None, None, Y, None, WS, ws1, None) == _lib.QMOE_ERR_INVALID_ARG
+    assert f(ctypes.byref(L), X, 1, None, R + 2, Y, None, WS, ws1, None) == _lib.QMOE_ERR_MISALIGNED
+    assert f(ctypes.byref(L), X, 1, None, R, Y, None, WS, ws1 - 1, None) == _lib.QMOE_ERR_WORKSPACE
+    assert f(ctypes.byref(L), X, 1, None, R, X, None, WS, ws1, None) == _lib.QMOE_ERR_INVALID_ARG
+    assert f(ctypes.byref(layer_c(top_k=0)), X, 1, None, R, Y, None, WS, ws1, None) == _lib.QMOE_ERR_INVALID_ARG
