@@ -303,6 +303,100 @@ def bench_moe_decode(args, q, torch):
     return res, cpu_baseline_moe_decode
 
 
+def cpu_baseline_moe_routed(n_tokens=600, budget_s=20.0):
+    """The oracle on a bounded sample: single-token layer forwards under a given routing
+    (the layer evaluated on the stated selection, as the routed call computes it)."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import synth
+    from layers import Shape, build_layer
+    from oracle import moe
+
+    S = Shape(top_k=4)
+    wl = synth.Workload.MOE_DECODE
+    xs = synth.activations(n_tokens, H, wl, 0, 98)
+    route = synth.expert_choices(n_tokens, 4, E, wl, 0, 98)
+    L = build_layer(wl, 0, S, only_experts=set(route.ravel().tolist()))
+    t0 = time.perf_counter()
+    done = 0
+    for i in range(n_tokens):
+        moe.moe_layer(xs[i:i + 1], L, idx=route[i:i + 1])
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "tokens/s", "cores": _threads(), "kind": "oracle", "host": host_desc(),
+            "sample": f"{done} single-token decodes of one layer under a given top-4 routing (hidden 2048, "
+                      f"256 experts, shared expert, LoRA r16), float64 numpy, {dt:.1f} s"}
+
+
+def bench_moe_decode_routed(args, q, torch):
+    """Decode with the prerouter head's prediction as the route ("double shift"): layer l at
+    token i runs the experts that the head of layer l-1 predicted from token i's input, the
+    routing layer l-1 executed for token i and the one it executed for token i-1.  The routes
+    are predicted (and the executed routings taken) before the timed region; the timed steps
+    are the routed layer calls alone, and the head's own forward is timed on its own."""
+    D, F, TOPK = H, 512, 4
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1235)
+    layers = [make_layer(q, torch, gen) for _ in range(LAYERS)]
+    n_in = D + 2 * E
+    rnd = lambda *sh: (torch.randn(sh, generator=gen, device="cuda") * 0.02).half()
+    heads = [q.PrerouterHead(rnd(E, n_in), rnd(E), rnd(F, n_in), rnd(F), rnd(E, F), rnd(E))
+             for _ in range(LAYERS)]
+    flush = CacheFlush(torch)
+    K, W = args.steps, args.warmup
+    n_tok = K + W
+    xs = torch.randn((n_tok, 1, H), generator=gen, device="cuda").half()
+    ys = torch.empty_like(xs)
+    ws = torch.empty(q.moe_workspace_bytes(layers[0], 1), dtype=torch.uint8, device="cuda")
+    # executed routing of layer l-1 for every token, then the head's prediction for layer l
+    execd = torch.empty((n_tok, 1, TOPK), dtype=torch.int32, device="cuda")
+    for i in range(n_tok):
+        lp = (i - 1) % LAYERS
+        q.MoECall(layers[lp], xs[i], ys[i], ws, idx_out=execd[i])()
+    routes = torch.empty((n_tok, 1, TOPK), dtype=torch.int32, device="cuda")
+    for i in range(n_tok):
+        _, _, pred, _ = q.prerouter_forward(heads[(i - 1) % LAYERS], xs[i], execd[i], execd[max(i - 1, 0)])
+        routes[i].copy_(pred)
+    torch.cuda.synchronize()
+    wts = torch.empty((n_tok, 1, TOPK), dtype=torch.float32, device="cuda")
+
+    def run(lo, hi):
+        def f():
+            for i in range(lo, hi):
+                q.moe_switchglu_int4_routed(layers[i % LAYERS], xs[i], routes[i], ws=ws, out=ys[i], w_out=wts[i])
+        return f
+    if W:
+        graph_of(torch, run(K, K + W)).replay()
+    g_main = graph_of(torch, run(0, K))
+    ms_total = time_graph(torch, g_main, flush=flush)
+    ms_step = ms_total / K
+
+    def heads_run():
+        for i in range(K):
+            q.prerouter_forward(heads[(i - 1) % LAYERS], xs[i], execd[i], execd[max(i - 1, 0)])
+    ms_head = time_graph(torch, graph_of(torch, heads_run), flush=flush) / K
+    row = kernel_row("routed layer call (k_dec_rt_gate_up + k_dec_down<routed>)", "moe_decode_routed/step",
+                     ms_step * 1e3, DEC_STEP_BYTES)
+    res = {
+        "metric": "int4 MoE layer tokens/s (decode, 1 token per step, routed by the prerouter's prediction)",
+        "value": K / (ms_total * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "moe_switchglu_int4_routed decode: 1 token/step, hidden 2048, 256 experts "
+                               "int4 g64, top-4 given by the prerouter head's prediction (synthetic head "
+                               "weights), shared expert + 8-bit gate, LoRA r16 a32, 40 layers rotated, "
+                               "caches flushed before the timed region",
+                   "global_batch": 1, "layers_rotated": LAYERS,
+                   "step_algorithmic_bytes": DEC_STEP_BYTES,
+                   "head_us_per_call": ms_head * 1e3,
+                   "layer_plus_head_us_per_step": (ms_step + ms_head) * 1e3,
+                   "kernels": [row]},
+        "roofline": roofline_of(row),
+    }
+    return res, cpu_baseline_moe_routed
+
+
 def cpu_baseline_moe_prefill(n_tokens=448, budget_s=20.0):
     """The oracle (float64 numpy) on a bounded sample: batches of 16 prefill tokens through
     one seeded layer of the same shapes (every expert the sample reaches is quantized)."""
@@ -760,7 +854,8 @@ def bench_prerouter(args, q, torch):
     return res, cpu_baseline_prerouter
 
 
-WORKLOADS = {"moe_decode": bench_moe_decode, "moe_prefill": bench_moe_prefill,
+WORKLOADS = {"moe_decode": bench_moe_decode, "moe_decode_routed": bench_moe_decode_routed,
+             "moe_prefill": bench_moe_prefill,
              "moe_stack": bench_moe_stack, "supergroup": bench_supergroup,
              "supergroup_a8": lambda args, q, torch: bench_supergroup(args, q, torch, a8=True),
              "gemv": bench_gemv, "prerouter": bench_prerouter}

@@ -123,7 +123,7 @@ __device__ __forceinline__ float bdot16(const uint4 (&v)[2], const float* z, int
 // z[r] = A[r] . v for r < rank (A fp16 [rank][K] row-major, v fp16 [K]), whole block: one
 // 16-lane DPP row per rank row, each lane a K/16 slice (K a multiple of 128), so all loads
 // of the block are in flight together.  Writes z (LDS); the caller synchronises.
-__device__ inline void lora_rows16(const uint16_t* __restrict__ A, int rank,
+__device__ __forceinline__ void lora_rows16(const uint16_t* __restrict__ A, int rank,
                                    const uint16_t* __restrict__ v, int K, float* z) {
     const int lane16 = threadIdx.x & 15, row0 = threadIdx.x >> 4, nrows = NT >> 4;
     const int per = K / 16;                 // inputs per lane (a multiple of 8)

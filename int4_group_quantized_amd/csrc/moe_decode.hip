@@ -299,7 +299,11 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
     // become an indexed scratch access whose wait drains every load in flight).
     // the token's adapter first: the addresses of the LoRA rows wait for it, and loads
     // complete in issue order, so a load issued later would make that wait longer
-    const int ad = adapter_of(a.adapter, t, a.nad);
+    // (one load of the index, clamped per projection: every further load of it would be a
+    // round trip of its own before the rows it addresses)
+    const int araw = a.adapter ? a.adapter[t] : 0;
+    auto clamp_ad = [&](int n) { return araw < 0 ? 0 : (araw >= n ? n - 1 : araw); };
+    const int ad = clamp_ad(a.nad);
     const int n_items = (K + 1) * DN_ROWS;
     const int slots = 4 * rpw;            // lane segments in the block
     const int slot = wave * rpw + seg;
@@ -309,24 +313,30 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
         const int m = min(i * slots + slot, n_items - 1) / DN_ROWS;
         eit[i] = expert_of(min(m, K - 1));
     }
+    // routing weights: published by the gate/up launch, or (ROUTED) the softmax of the router
+    // logits over the given set, whose loads wait for the routing and so are issued with the
+    // expert rows below
     float selw[MAX_DEC_K];
-    if constexpr (ROUTED) {
-        float lg[MAX_DEC_K];
-#pragma unroll
-        for (int r = 0; r < MAX_DEC_K; ++r) {
-            const int e = expert_of(min(r, K - 1));
-            lg[r] = a.logits[(long)t * a.Ep + e];
-            if (a.rbias) lg[r] += a.rbias[e];
-        }
-        given_softmax<MAX_DEC_K>(K, lg, selw);
-    } else {
+    if constexpr (!ROUTED) {
 #pragma unroll
         for (int r = 0; r < MAX_DEC_K; ++r) selw[r] = a.wts[(long)t * K + min(r, K - 1)];
     }
-    const uint16_t* hsrow = ROUTED ? hsc : a.hs + (long)t * Kd;
+    // (ROUTED) lane r < K of wave 0 takes the logit of the token's given expert r; the logit
+    // loads wait for the routing, so they are issued with the expert rows, and the values reach
+    // LDS only after the dot products
+    __shared__ float lgs[MAX_DEC_K];
+    const int my_e = ROUTED ? expert_of(min((int)threadIdx.x, K - 1)) : 0;
+    float my_l = 0.0f;
+    const uint16_t* hsrow = a.hs + (long)t * Kd;
     const uint4* hbase4 = reinterpret_cast<const uint4*>(a.h + (long)t * K * Kd);
     const uint4* hsrow4 = reinterpret_cast<const uint4*>(hsrow);
-    auto rowp = [=](int m) { return m < K ? hbase4 + (long)m * (Kd / 8) : hsrow4; };
+    // (ROUTED: rows below K only, all in global memory: a pointer that may also point into
+    // LDS would turn every load through it into a flat load, after which each wait is a full
+    // drain of the loads in flight)
+    auto rowp = [=](int m) {
+        if constexpr (ROUTED) return hbase4 + (long)min(m, K - 1) * (Kd / 8);
+        else return m < K ? hbase4 + (long)m * (Kd / 8) : hsrow4;
+    };
     StageRegs<4, DN_STAGE> st;
     if (one_pass) st.load(rowp, n_staged, Kd);
     // ROUTED: the raw shared gate/up sums of this thread's h_s outputs and, for ranks of at
@@ -334,11 +344,16 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
     constexpr int HSN = ROUTED ? 2 : 1;    // h_s outputs per thread loaded here (the rest later)
     float gsv[HSN], usv[HSN];
     uint4 bgv[HSN][2], buv[HSN][2];
-    const int adg = ROUTED ? adapter_of(a.adapter, t, a.nag) : 0;
-    const int adu = ROUTED ? adapter_of(a.adapter, t, a.nau) : 0;
+    const int adg = ROUTED ? clamp_ad(a.nag) : 0;
+    const int adu = ROUTED ? clamp_ad(a.nau) : 0;
     const bool bgf = ROUTED && a.Bg && (a.rg & 7) == 0 && a.rg <= 16;
     const bool buf = ROUTED && a.Bu && (a.ru & 7) == 0 && a.ru <= 16;
+    __shared__ float zgu[2][MAX_RANK];   // (ROUTED) the token's LoRA z of the shared gate and up
+    float zval = 0.0f;
     if constexpr (ROUTED) {
+        // lanes of wave 0 load the z's now; they reach LDS after the expert rows are issued
+        const int zi = threadIdx.x & 63;
+        zval = (threadIdx.x < 64 ? (zi < 32 ? a.zg : a.zu) : a.zg)[(long)t * MAX_RANK + (zi & 31)];
 #pragma unroll
         for (int j = 0; j < HSN; ++j) {
             const int n = min((int)threadIdx.x + j * NT, Kd - 1);
@@ -403,28 +418,39 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
         }
     };
     load_items(0);
+    float my_b = 0.0f;   // the bias, added at the end (a branch around its load would wait for it)
+    if constexpr (ROUTED) {
+        my_l = a.logits[(long)t * a.Ep + my_e];
+        my_b = (a.rbias ? a.rbias : a.logits)[my_e];
+    }
     // phase 3: activations to LDS
     if constexpr (ROUTED) {
         // h_s = silu(g_s + LoRA_g) * (u_s + LoRA_u), as the shared gate/up blocks of the
-        // top-K path take it
-        const float* zg = a.zg + (long)t * MAX_RANK;
-        const float* zu = a.zu + (long)t * MAX_RANK;
+        // top-K path take it (ranks up to 32 from LDS; larger ones from memory)
+        if (threadIdx.x < 64) zgu[threadIdx.x >> 5][threadIdx.x & 31] = zval;
+        __syncthreads();
+        // z from LDS (ranks up to 32) or from memory; each pointer stays in one address space
+        // (a pointer that may be either makes its loads flat, and every wait a full drain)
+        auto finish = [&](const float* zg, const float* zu) {
 #pragma unroll
-        for (int j = 0; j < HSN; ++j) {
-            const int n = threadIdx.x + j * NT;
-            if (n < Kd) {
-                float gv = gsv[j], uv = usv[j];
-                if (a.Bg) gv = fmaf(a.lsg, bgf ? bdot16(bgv[j], zg, a.rg) : lora_b_dot(a.Bg, adg, Kd, n, a.rg, zg), gv);
-                if (a.Bu) uv = fmaf(a.lsu, buf ? bdot16(buv[j], zu, a.ru) : lora_b_dot(a.Bu, adu, Kd, n, a.ru, zu), uv);
+            for (int j = 0; j < HSN; ++j) {
+                const int n = threadIdx.x + j * NT;
+                if (n < Kd) {
+                    float gv = gsv[j], uv = usv[j];
+                    if (a.Bg) gv = fmaf(a.lsg, bgf ? bdot16(bgv[j], zg, a.rg) : lora_b_dot(a.Bg, adg, Kd, n, a.rg, zg), gv);
+                    if (a.Bu) uv = fmaf(a.lsu, buf ? bdot16(buv[j], zu, a.ru) : lora_b_dot(a.Bu, adu, Kd, n, a.ru, zu), uv);
+                    hsc[n] = f2h(silu(gv) * uv);
+                }
+            }
+            for (int n = threadIdx.x + HSN * NT; n < Kd; n += NT) {   // inter above 512
+                float gv = a.gs[(long)t * Kd + n], uv = a.us[(long)t * Kd + n];
+                if (a.Bg) gv = fmaf(a.lsg, lora_b_dot(a.Bg, adg, Kd, n, a.rg, zg), gv);
+                if (a.Bu) uv = fmaf(a.lsu, lora_b_dot(a.Bu, adu, Kd, n, a.ru, zu), uv);
                 hsc[n] = f2h(silu(gv) * uv);
             }
-        }
-        for (int n = threadIdx.x + HSN * NT; n < Kd; n += NT) {   // inter above 512
-            float gv = a.gs[(long)t * Kd + n], uv = a.us[(long)t * Kd + n];
-            if (a.Bg) gv = fmaf(a.lsg, lora_b_dot(a.Bg, adg, Kd, n, a.rg, zg), gv);
-            if (a.Bu) uv = fmaf(a.lsu, lora_b_dot(a.Bu, adu, Kd, n, a.ru, zu), uv);
-            hsc[n] = f2h(silu(gv) * uv);
-        }
+        };
+        if (a.rg <= 32 && a.ru <= 32) finish(zgu[0], zgu[1]);
+        else finish(a.zg + (long)t * MAX_RANK, a.zu + (long)t * MAX_RANK);
     }
     if (one_pass) st.commit(n_staged, Kd, hs_l, hsum);
     else stage_rows<4, 4>(rowp, n_staged, Kd, hs_l, hsum);
@@ -455,7 +481,8 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
         acc = seg_sum<16>(acc);
         if (lane16 == 0 && zrow < a.rd) zd[zrow] = acc;
     } else if (a.Ad) {
-        lora_rows16(a.Ad + (long)ad * a.rd * Kd, a.rd, hsrow, Kd, zd);
+        if constexpr (ROUTED) lora_rows16(a.Ad + (long)ad * a.rd * Kd, a.rd, hsc, Kd, zd);
+        else lora_rows16(a.Ad + (long)ad * a.rd * Kd, a.rd, hsrow, Kd, zd);
     }
     for (int base = 0; base < n_items; base += slots * DN_ITEMS) {
         if (base > 0) load_items(base);
@@ -469,7 +496,16 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
             if (sl == 0 && mi[i] >= 0) o_l[mi[i] * DN_ROWS + ri[i]] = v;
         }
     }
+    if (ROUTED && threadIdx.x < K) lgs[threadIdx.x] = a.rbias ? my_l + my_b : my_l;
     __syncthreads();
+    if constexpr (ROUTED) {
+        if (threadIdx.x < DN_ROWS) {
+            float lg[MAX_DEC_K];
+#pragma unroll
+            for (int r = 0; r < MAX_DEC_K; ++r) lg[r] = lgs[min(r, K - 1)];
+            given_softmax<MAX_DEC_K>(K, lg, selw);
+        }
+    }
     if (threadIdx.x < DN_ROWS) {
         const int r = threadIdx.x, n = n0 + r;
         if (n < H) {

@@ -25,7 +25,8 @@ def test_more_than_one_gpu_exits_with_a_message(n):
 def test_workload_names_and_options():
     r = run("--help")
     assert r.returncode == 0
-    for w in ("moe_decode", "moe_prefill", "moe_stack", "supergroup", "supergroup_a8", "gemv", "prerouter"):
+    for w in ("moe_decode", "moe_decode_routed", "moe_prefill", "moe_stack", "supergroup", "supergroup_a8",
+              "gemv", "prerouter"):
         assert w in r.stdout
     for opt in ("--steps", "--warmup", "--batch", "--group", "--params", "--skew", "--tokens"):
         assert opt in r.stdout
