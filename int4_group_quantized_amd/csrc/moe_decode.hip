@@ -293,17 +293,13 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
         else return a.idx[(long)t * K + m];
     };
 
-    // phase 1: the routing decision (published by the gate/up stage), the K + 1 activation
-    // rows and the LoRA A_down slices in flight together.  Each lane loads the expert of its
-    // own first-pass items first (per-lane loads: a per-lane pick from a uniform array would
-    // become an indexed scratch access whose wait drains every load in flight).
-    // the token's adapter first: the addresses of the LoRA rows wait for it, and loads
-    // complete in issue order, so a load issued later would make that wait longer
-    // (one load of the index, clamped per projection: every further load of it would be a
-    // round trip of its own before the rows it addresses)
-    const int araw = a.adapter ? a.adapter[t] : 0;
-    auto clamp_ad = [&](int n) { return araw < 0 ? 0 : (araw >= n ? n - 1 : araw); };
-    const int ad = clamp_ad(a.nad);
+    // phase 1: every load that needs no other load's value, issued before any wait: the
+    // routing (published by the gate/up stage, or given), the adapter index, the K + 1
+    // activation rows, the combine's own inputs.  Each lane loads the expert of its own
+    // first-pass items (per-lane loads: a per-lane pick from a uniform array would become an
+    // indexed scratch access whose wait drains every load in flight).  Loads complete in
+    // issue order, so the routing and the adapter index go first: the waits for them below
+    // then do not wait for the activations.
     const int n_items = (K + 1) * DN_ROWS;
     const int slots = 4 * rpw;            // lane segments in the block
     const int slot = wave * rpw + seg;
@@ -313,20 +309,30 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
         const int m = min(i * slots + slot, n_items - 1) / DN_ROWS;
         eit[i] = expert_of(min(m, K - 1));
     }
-    // routing weights: published by the gate/up launch, or (ROUTED) the softmax of the router
-    // logits over the given set, whose loads wait for the routing and so are issued with the
-    // expert rows below
-    float selw[MAX_DEC_K];
-    if constexpr (!ROUTED) {
-#pragma unroll
-        for (int r = 0; r < MAX_DEC_K; ++r) selw[r] = a.wts[(long)t * K + min(r, K - 1)];
-    }
     // (ROUTED) lane r < K of wave 0 takes the logit of the token's given expert r; the logit
     // loads wait for the routing, so they are issued with the expert rows, and the values reach
     // LDS only after the dot products
     __shared__ float lgs[MAX_DEC_K];
     const int my_e = ROUTED ? expert_of(min((int)threadIdx.x, K - 1)) : 0;
     float my_l = 0.0f;
+    // one load of the adapter index, clamped per projection (every further load of it would be
+    // a round trip of its own before the rows it addresses)
+    // (loaded unconditionally, from a stand-in address without adapters: a load under a branch
+    // is waited for inside the branch)
+    const int araw_l = *(a.adapter ? a.adapter + t : reinterpret_cast<const int32_t*>(a.x));
+    __builtin_amdgcn_sched_barrier(0);   // the routing and the adapter index are issued first
+    int araw = 0;
+    auto clamp_ad = [&](int n) {
+        const int v = a.adapter ? araw : 0;
+        return v < 0 ? 0 : (v >= n ? n - 1 : v);
+    };
+    // routing weights: published by the gate/up launch, or (ROUTED) the softmax of the router
+    // logits over the given set (below)
+    float selw[MAX_DEC_K];
+    if constexpr (!ROUTED) {
+#pragma unroll
+        for (int r = 0; r < MAX_DEC_K; ++r) selw[r] = a.wts[(long)t * K + min(r, K - 1)];
+    }
     const uint16_t* hsrow = a.hs + (long)t * Kd;
     const uint4* hbase4 = reinterpret_cast<const uint4*>(a.h + (long)t * K * Kd);
     const uint4* hsrow4 = reinterpret_cast<const uint4*>(hsrow);
@@ -338,20 +344,16 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
         else return m < K ? hbase4 + (long)m * (Kd / 8) : hsrow4;
     };
     StageRegs<4, DN_STAGE> st;
-    if (one_pass) st.load(rowp, n_staged, Kd);
-    // ROUTED: the raw shared gate/up sums of this thread's h_s outputs and, for ranks of at
-    // most 16 in multiples of 8, their LoRA-B rows, loaded before the expert rows
+    st.load(rowp, n_staged, Kd);   // always (clamped, in bounds): loads under a branch are
+                                   // waited for at its merge; unused unless one_pass
+    // ROUTED: the raw shared gate/up sums of this thread's h_s outputs (their LoRA-B rows need
+    // the adapter index and follow below) and the token's LoRA z's (lanes of wave 0; they reach
+    // LDS after the expert rows are issued)
     constexpr int HSN = ROUTED ? 2 : 1;    // h_s outputs per thread loaded here (the rest later)
     float gsv[HSN], usv[HSN];
-    uint4 bgv[HSN][2], buv[HSN][2];
-    const int adg = ROUTED ? clamp_ad(a.nag) : 0;
-    const int adu = ROUTED ? clamp_ad(a.nau) : 0;
-    const bool bgf = ROUTED && a.Bg && (a.rg & 7) == 0 && a.rg <= 16;
-    const bool buf = ROUTED && a.Bu && (a.ru & 7) == 0 && a.ru <= 16;
     __shared__ float zgu[2][MAX_RANK];   // (ROUTED) the token's LoRA z of the shared gate and up
     float zval = 0.0f;
     if constexpr (ROUTED) {
-        // lanes of wave 0 load the z's now; they reach LDS after the expert rows are issued
         const int zi = threadIdx.x & 63;
         zval = (threadIdx.x < 64 ? (zi < 32 ? a.zg : a.zu) : a.zg)[(long)t * MAX_RANK + (zi & 31)];
 #pragma unroll
@@ -359,6 +361,35 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
             const int n = min((int)threadIdx.x + j * NT, Kd - 1);
             gsv[j] = a.gs[(long)t * Kd + n];
             usv[j] = a.us[(long)t * Kd + n];
+        }
+    }
+    // the combine's own inputs (gate logit, residual x) now, not after the dots
+    float gate_t;
+    uint16_t x_res;
+    {   // every thread loads (rows clamped; only threads < DN_ROWS use them): no branch
+        const int nn = min(n0 + (int)(threadIdx.x % DN_ROWS), H - 1);
+        gate_t = a.gate[t];
+        x_res = a.x[(long)t * H + nn];
+    }
+    // nothing below may be scheduled above this point: what follows waits for the routing or
+    // the adapter index, and a wait placed earlier would hold back the loads above
+    __builtin_amdgcn_sched_barrier(0);
+    // the adapter index is first read here (the compiler would otherwise move it to a scalar
+    // register right after its load, and wait for the load there)
+    araw = araw_l;
+    asm volatile("" : "+v"(araw));
+
+    // phase 1b: the LoRA rows (they need the adapter index)
+    const int ad = clamp_ad(a.nad);
+    uint4 bgv[HSN][2], buv[HSN][2];
+    const int adg = ROUTED ? clamp_ad(a.nag) : 0;
+    const int adu = ROUTED ? clamp_ad(a.nau) : 0;
+    const bool bgf = ROUTED && a.Bg && (a.rg & 7) == 0 && a.rg <= 16;
+    const bool buf = ROUTED && a.Bu && (a.ru & 7) == 0 && a.ru <= 16;
+    if constexpr (ROUTED) {
+#pragma unroll
+        for (int j = 0; j < HSN; ++j) {
+            const int n = min((int)threadIdx.x + j * NT, Kd - 1);
             const uint16_t* gb = bgf ? a.Bg + ((long)adg * Kd + n) * a.rg : a.x;
             const uint16_t* ub = buf ? a.Bu + ((long)adu * Kd + n) * a.ru : a.x;
 #pragma unroll
@@ -372,19 +403,12 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
     const int lane16 = threadIdx.x & 15, zrow = threadIdx.x >> 4;
     const int zper = Kd / 16;
     const bool zfast = a.Ad && a.rd <= 16 && zper <= 8 * ZI;
-    // the combine's own inputs (gate logit, residual x, LoRA-B rows of this block's outputs)
-    // are loaded now, not after the dots: one round trip less at the end
     constexpr int BQ = 2;   // prefetched B rows up to rank 16; larger ranks read B at the end
     uint4 bq[BQ];
-    float gate_t = 0.0f;
-    uint16_t x_res = 0;
     const bool bfast = a.Bd && (a.rd & 7) == 0 && a.rd <= 8 * BQ;
-    {   // every thread loads (rows clamped; only threads < DN_ROWS use them): no branch
-        const int nn = min(n0 + (int)(threadIdx.x % DN_ROWS), H - 1);
-        gate_t = a.gate[t];
-        x_res = a.x[(long)t * H + nn];
-        // loaded unconditionally (stand-in: the token's x row): under a branch the compiler
+    {   // loaded unconditionally (stand-in: the token's x row): under a branch the compiler
         // copies the loaded registers at the merge, and a copy waits for every load in flight
+        const int nn = min(n0 + (int)(threadIdx.x % DN_ROWS), H - 1);
         const uint4* brow = bfast ? reinterpret_cast<const uint4*>(a.Bd + ((long)ad * H + nn) * a.rd)
                                   : reinterpret_cast<const uint4*>(a.x + (long)t * H);
 #pragma unroll
@@ -509,14 +533,21 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
     if (threadIdx.x < DN_ROWS) {
         const int r = threadIdx.x, n = n0 + r;
         if (n < H) {
+            // every LDS read first (a read under a branch would be a round trip of its own)
+            float ov[MAX_DEC_K];
+#pragma unroll
+            for (int k = 0; k < MAX_DEC_K; ++k) ov[k] = o_l[min(k, K - 1) * DN_ROWS + r];
+            float os = o_l[K * DN_ROWS + r];
             float acc = 0.0f;
 #pragma unroll
             for (int k = 0; k < MAX_DEC_K; ++k)
-                if (k < K) acc = fmaf(selw[k], o_l[k * DN_ROWS + r], acc);
-            float os = o_l[K * DN_ROWS + r];
+                if (k < K) acc = fmaf(selw[k], ov[k], acc);
             if (bfast) {
 #pragma unroll
                 for (int i = 0; i < BQ; ++i) hold(bq[i]);
+                float zv[8 * BQ];   // read unconditionally (entries past the rank are not used)
+#pragma unroll
+                for (int j = 0; j < 8 * BQ; ++j) zv[j] = zd[j];
                 float d = 0.0f;
 #pragma unroll
                 for (int i = 0; i < BQ; ++i) {
@@ -524,8 +555,8 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
                         const uint32_t w4[4] = {bq[i].x, bq[i].y, bq[i].z, bq[i].w};
 #pragma unroll
                         for (int u = 0; u < 4; ++u) {
-                            d = fmaf(half_lo(w4[u]), zd[i * 8 + 2 * u], d);
-                            d = fmaf(half_hi(w4[u]), zd[i * 8 + 2 * u + 1], d);
+                            d = fmaf(half_lo(w4[u]), zv[i * 8 + 2 * u], d);
+                            d = fmaf(half_hi(w4[u]), zv[i * 8 + 2 * u + 1], d);
                         }
                     }
                 }

@@ -282,3 +282,42 @@ def test_stages_in_order_equal_the_whole_layer(q, T):
     call(q.STAGE_DOWN)   # a stage re-run alone repeats its work on the same inputs
     torch.cuda.synchronize()
     assert torch.equal(whole.view(torch.int16), y.view(torch.int16))
+
+
+def plant_groups(L, seed):
+    """Every matrix of the layer (router, gate, experts, shared expert) with planted special
+    groups: about one group in eight with scale 0 (the degenerate case: each weight equals
+    the group's bias whatever its code), one in eight with every code at the top level (15,
+    or 255 at 8 bits) and one in eight with every code 0, as an imported checkpoint may hold
+    them."""
+    from oracle import affine
+    rng = np.random.default_rng(seed)
+
+    def plant(qw):
+        packed, scales, biases = qw.packed.copy(), qw.scales.copy(), qw.biases.copy()
+        G = scales.shape[-1]
+        wpg = 64 * qw.bits // 32                       # words per group
+        sel = rng.integers(0, 8, size=scales.shape)
+        scales[sel == 0] = np.float16(0.0)
+        words = packed.reshape(scales.shape + (wpg,))
+        words[sel == 1] = np.uint32(0xFFFFFFFF)
+        words[sel == 2] = np.uint32(0)
+        return affine.QWeight(words.reshape(packed.shape), scales, biases, qw.bits, qw.group)
+
+    fields = {k: plant(getattr(L, k)) for k in ("router", "shared_gate", "exp_gate", "exp_up", "exp_down",
+                                                 "sh_gate", "sh_up", "sh_down")}
+    return moe.MoELayer(**{**L.__dict__, **fields})
+
+
+@pytest.mark.parametrize("T", [2, 7, 64, 300])
+def test_layer_with_degenerate_and_extreme_groups(q, T):
+    """Layer parity with planted scale-0 groups and groups of all-15 / all-0 codes in every
+    matrix, on the decode path (2, 7 tokens) and the token-sorted path (64: 16-pair items;
+    300: 64-pair items with fp16 weights)."""
+    S = Shape(hidden=1024, inter=512, shared_inter=512, n_experts=16, top_k=4, rank=16, n_adapters=2)
+    Lc = plant_groups(build_layer(synth.Workload.TEST, 21, S), 21 + T)
+    x = synth.activations(T, S.hidden, synth.Workload.TEST, 21, T)
+    ad = (np.arange(T) % 2).astype(np.int32)
+    y, idx, w = run_device(q, Lc, S, x, ad)
+    err, rel, n_alt = check_layer(Lc, x, ad, y, idx, w)
+    print(f"planted groups T={T}: max abs {err:.2e} rel L2 {rel:.2e} alternatives {n_alt}", flush=True)
