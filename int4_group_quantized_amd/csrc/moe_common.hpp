@@ -12,7 +12,7 @@ constexpr int MAX_RANK = 64;
 constexpr int MAX_K = 32;
 constexpr int MAX_DEC_T = 32;  // the decode path serves up to this many tokens per call
 constexpr int MAX_DEC_K = 8;   // ... and up to this many experts per token
-constexpr int PF_ITEM = 64;    // most pairs per work item of the token-sorted GEMMs (slots per item)
+constexpr int PF_ITEM = 128;   // most pairs per work item of the token-sorted GEMMs (slots per item)
 constexpr int PF_SORT_MAXSEG = 64;   // most blocks (segments of pairs) of the multi-block sort
 
 struct QW {
@@ -197,8 +197,8 @@ __device__ inline void xside_lora_z(const MoeArgs& a, int j, int zjobs) {
 bool decode_path_fits(const qmoe_moe_layer& L, int T);
 hipError_t launch_moe_decode(const MoeArgs& a, int stage, hipStream_t s);
 // moe_prefill.hip
-int prefill_max_items(int E, int T, int K);
-int prefill_item_size(int E, int T, int K);
+int prefill_max_items(int E, int T, int K, int H, int I);
+int prefill_item_size(int E, int T, int K, int H, int I);
 int prefill_ksplit(int hidden, int T);
 hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s);
 

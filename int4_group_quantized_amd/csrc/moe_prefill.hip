@@ -1427,6 +1427,199 @@ template <int KF>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
 k_pf_combine_many(MoeArgs a) { pf_combine_body<KF, 4>(a); }
 
+// ---------------------------------------------------------------------------- large items
+// Grouped GEMM for work items of up to PB_TOK pairs (experts averaging more than 64 pairs),
+// where the GEMMs are bound by the matrix cores.  v_mfma_f32_32x32x16_f16 (on gfx950 it
+// keeps the matrix pipe about 1.5x busier per instruction than 16x16x32, measured back to
+// back), a block of 4 waves covering PB_ROWS = 128 features (32 per wave) of NMAT matrices
+// against 32 NTT token rows (NTT tiles of 32: the item's tokens rounded up, one body per
+// tile count, so no branch sits between the MFMAs).
+//   A (activations, 32 tokens x 16 inputs): lane l supplies token l % 32 and inputs
+//     8 (l / 32) .. +7 of the k-slice, from an LDS double buffer staged per 128-input step
+//     in the pair order of the nibble unpacking (pf_commit).
+//   B (weights, 16 inputs x 32 features): lane l supplies feature l % 32 and the same
+//     inputs, dequantized in registers to fp16(s q + b) (pf_q4, pf_dequant).  A lane loads 8
+//     consecutive packed words of its feature's 128-input step (the lower 64 inputs for
+//     l < 32, the upper 64 otherwise); v_permlane32_swap of word pairs (2i, 2i + 1) then
+//     leaves lane l < 32 the even words 0, 8, 2, 10, 4, 12, 6, 14 and lane l + 32 the odd
+//     ones 1, 9, 3, 11, ..., i.e. for k-slice s the word 2 s + l / 32 in register 2 s
+//     (s < 4) or 2 (s - 4) + 1 (s >= 4).
+//   Output tile c of matrix m: 16 floats per lane, token 8 (v / 4) + 4 (l / 32) + v % 4,
+//     feature l % 32.
+// Each weight is dequantized once per block and feeds NTT MFMAs per matrix; the activation
+// fragments of a k-slice feed NMAT MFMAs each.  Weights and scales are loaded two steps
+// ahead, the next step's activations one step ahead (staged at the top of the step).
+constexpr int PB_TOK = 128;    // pairs per large work item
+constexpr int PB_ROWS = 128;   // features per block
+
+template <int NTT>
+struct PbSmem {
+    f16 tile[2][32 * NTT * PF_PITCH];
+    int arow[32 * NTT], orow[32 * NTT];
+};
+
+template <int NMAT, int NTT, int NS, int FL, int NTS>
+__device__ __forceinline__ void pb_body(const PfGemm& a, int rb, int ntok, int e, PbSmem<NTS>& sm) {
+    constexpr int K = NS * PF_KS, G = K / 64, WPS = PF_KS / 8, WPR = K / 8;
+    constexpr int NQ = 2 * NTT;   // 16-byte activation units per thread per step
+    constexpr int D = 2;          // weight steps in flight
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 31, hh = lane >> 5;
+    const int n = rb * PB_ROWS + wave * 32 + col;
+    const long row = (long)e * a.N + min(n, a.N - 1);   // rows past N clamped, never stored
+    const uint32_t* wrow[NMAT];
+    const uint32_t* srow[NMAT];
+    const uint32_t* brow[NMAT];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) {
+        wrow[m] = a.p[m] + row * WPR + hh * 8;
+        srow[m] = reinterpret_cast<const uint32_t*>(a.s[m] + row * G);
+        brow[m] = reinterpret_cast<const uint32_t*>(a.b[m] + row * G);
+    }
+    const int sr = threadIdx.x >> 4, sc = threadIdx.x & 15;
+    const uint16_t* xrp[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) xrp[q] = a.act + (long)sm.arow[q * 16 + sr] * K + sc * 8;
+
+    struct Slot {
+        uint32_t w[NMAT][8];
+        uint32_t s[NMAT], b[NMAT];   // the step's two groups as fp16 pairs
+    };
+    Slot ws[D];
+    uint4 xr[NQ];
+    auto load_w = [&](Slot& sl, int ks) {
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) {
+            const uint4* src = reinterpret_cast<const uint4*>(wrow[m] + ks * WPS);
+            const uint4 v0 = src[0], v1 = src[1];
+            sl.w[m][0] = v0.x; sl.w[m][1] = v0.y; sl.w[m][2] = v0.z; sl.w[m][3] = v0.w;
+            sl.w[m][4] = v1.x; sl.w[m][5] = v1.y; sl.w[m][6] = v1.z; sl.w[m][7] = v1.w;
+            sl.s[m] = srow[m][ks];
+            sl.b[m] = brow[m][ks];
+        }
+    };
+    auto load_x = [&](int ks) {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) xr[q] = *reinterpret_cast<const uint4*>(xrp[q] + ks * PF_KS);
+    };
+    auto commit_x = [&](int buf) {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) pf_commit<4>(xr[q], q * 16 + sr, sc, sm.tile[buf]);
+    };
+
+    f32x16 acc[NMAT][NTT];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int c = 0; c < NTT; ++c)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[m][c][v] = 0.0f;
+    uint32_t m1024 = 0x64006400u, m64 = 0x54005400u;   // fp16 1024 and 64 in both halves (pf_q4)
+    asm volatile("" : "+v"(m1024), "+v"(m64));
+
+    load_x(0);
+#pragma unroll
+    for (int d = 0; d < D; ++d) load_w(ws[d], d);
+    commit_x(0);
+    if (NS > 1) load_x(1);
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < NS; ++ks) {
+        Slot& sl = ws[ks % D];
+        uint32_t cw[NMAT][8];
+        f16 sh[NMAT][2], bh[NMAT][2];
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const auto r = __builtin_amdgcn_permlane32_swap(sl.w[m][2 * i], sl.w[m][2 * i + 1], false, false);
+                cw[m][2 * i] = r[0];
+                cw[m][2 * i + 1] = r[1];
+            }
+            const f16x2 s2 = as_h2(sl.s[m]), b2 = as_h2(sl.b[m]);
+            sh[m][0] = s2[0]; sh[m][1] = s2[1];
+            bh[m][0] = b2[0]; bh[m][1] = b2[1];
+        }
+        // the next step's activations into the other buffer (every wave finished reading it
+        // before the barrier that ended the previous step), then the loads two steps ahead
+        // into the registers just consumed
+        if (ks + 1 < NS) commit_x((ks + 1) & 1);
+        if (ks + 2 < NS) load_x(ks + 2);
+        if (ks + D < NS) load_w(sl, ks + D);
+        // k-slices of 16 inputs (two waves per SIMD: each covers the other's LDS and memory
+        // latency)
+        const f16* tb = sm.tile[ks & 1] + col * PF_PITCH + 8 * hh;
+#pragma unroll
+        for (int s16 = 0; s16 < 8; ++s16) {
+            const int g = s16 >> 2, reg = s16 < 4 ? 2 * s16 : 2 * (s16 - 4) + 1;
+            f16x8 bw[NMAT];
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m) bw[m] = pf_dequant(pf_q4(cw[m][reg], m1024, m64), sh[m][g], bh[m][g]);
+#pragma unroll
+            for (int c = 0; c < NTT; ++c) {
+                const f16x8 av = *reinterpret_cast<const f16x8*>(tb + c * 32 * PF_PITCH + 16 * s16);
+#pragma unroll
+                for (int m = 0; m < NMAT; ++m)
+                    acc[m][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bw[m], acc[m][c], 0, 0, 0);
+            }
+        }
+        __syncthreads();
+    }
+    if (n >= a.N) return;
+#pragma unroll
+    for (int c = 0; c < NTT; ++c) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int t = c * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
+            if (t < ntok) {
+                const int orow = sm.orow[t];
+                if constexpr (FL & F_HOUT)
+                    a.hout[(long)orow * a.N + n] = f2h(silu(acc[0][c][v]) * acc[NMAT - 1][c][v]);
+                else
+                    a.hout[(long)orow * a.ostride + n] = f2h(acc[0][c][v]);
+            }
+        }
+    }
+}
+
+// One large work item per (item, row block): its record and pair ids, then the body for the
+// item's tile count.
+template <int NMAT, int NS, int FL>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) k_pf_big(PfGemm a) {
+    __shared__ __align__(16) PbSmem<PB_TOK / 32> sm;
+    int rb, item;
+    pf_block(blockIdx.x, a.nrb, rb, item);
+    const int4 rec = reinterpret_cast<const int4*>(a.wrec)[item];
+    const int pair = threadIdx.x < PB_TOK ? a.wpairs[(long)item * PF_ITEM + threadIdx.x] : 0;
+    if (rec.y == 0) return;   // past the last item
+    const int e = rec.x, ntok = rec.y;
+    if (threadIdx.x < PB_TOK) sm.orow[threadIdx.x] = pair;
+    __syncthreads();
+    if (threadIdx.x < PB_TOK) sm.arow[threadIdx.x] = sm.orow[min((int)threadIdx.x, ntok - 1)] / a.act_div;
+    __syncthreads();
+    switch ((ntok + 31) >> 5) {
+        case 1: pb_body<NMAT, 1, NS, FL>(a, rb, ntok, e, sm); break;
+        case 2: pb_body<NMAT, 2, NS, FL>(a, rb, ntok, e, sm); break;
+        case 3: pb_body<NMAT, 3, NS, FL>(a, rb, ntok, e, sm); break;
+        default: pb_body<NMAT, 4, NS, FL>(a, rb, ntok, e, sm); break;
+    }
+}
+
+// The large-item GEMMs exist for reductions of 512, 1024 and 2048 inputs (4, 8, 16 steps).
+bool big_steps_ok(int k) { return k == 512 || k == 1024 || k == 2048; }
+
+template <int NMAT, int FL>
+hipError_t launch_big(const PfGemm& p, hipStream_t s) {
+    const dim3 grid((unsigned)(p.nrb * p.items));
+    switch (p.K) {
+        case 512: k_pf_big<NMAT, 4, FL><<<grid, 256, 0, s>>>(p); break;
+        case 1024: k_pf_big<NMAT, 8, FL><<<grid, 256, 0, s>>>(p); break;
+        case 2048: k_pf_big<NMAT, 16, FL><<<grid, 256, 0, s>>>(p); break;
+        default: return hipErrorInvalidValue;   // prefill_item_size never selects it then
+    }
+    return hipSuccess;
+}
+
 template <int NMAT, int BITS, int NT, int FL>
 void pf_gemm(const PfGemm& p, hipStream_t s) {
     const dim3 grid((unsigned)(p.nrb * p.items));
@@ -1464,17 +1657,19 @@ PfGemm grouped(const MoeArgs& a, const QW& w0, const QW* w1, int N, int K, const
 
 // Pairs per work item: 16 (one token tile: no activation loads for a second, mostly padding
 // tile) while experts average at most 8 pairs, so that few experts need a second item and a
-// second pass over their weights; 32 up to an average of 32; else 64 (four tiles: each
-// weight step feeds four times the MFMA work, the regime where the GEMMs turn compute-bound).
-int prefill_item_size(int E, int T, int K) {
+// second pass over their weights; 32 up to an average of 32; 64 up to 64 (four tiles: each
+// weight step feeds four times the MFMA work, the regime where the GEMMs turn compute-bound);
+// above that PB_TOK = 128, the large-item GEMMs (hidden and inter up to 2048).
+int prefill_item_size(int E, int T, int K, int H, int I) {
     const long tk = (long)T * K;
+    if (tk > 64l * E && big_steps_ok(H) && big_steps_ok(I)) return PB_TOK;
     return tk <= 8l * E ? 16 : tk <= 32l * E ? 32 : 64;
 }
 
 // Upper bound on the work items of the sort, rounded up to the 8 XCDs of the block order:
 // sum over experts of ceil(count / isz) <= E + T K / isz.
-int prefill_max_items(int E, int T, int K) {
-    const int isz = prefill_item_size(E, T, K);
+int prefill_max_items(int E, int T, int K, int H, int I) {
+    const int isz = prefill_item_size(E, T, K, H, I);
     return (E + (T * K + isz - 1) / isz + 7) / 8 * 8;
 }
 
@@ -1484,7 +1679,7 @@ static int xs_inputs(int hidden, int T) { return T >= PF_XS_BIG_T ? std::min(hid
 int prefill_ksplit(int hidden, int T) { return hidden / xs_inputs(hidden, T); }
 
 hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s) {
-    const int items = prefill_max_items(a.E, a.T, a.K), isz = prefill_item_size(a.E, a.T, a.K);
+    const int items = prefill_max_items(a.E, a.T, a.K, a.H, a.I), isz = prefill_item_size(a.E, a.T, a.K, a.H, a.I);
     const int tgroups = (a.T + PF_TOK - 1) / PF_TOK;
     const int ksplit = prefill_ksplit(a.H, a.T);
     const bool all = stage == QMOE_STAGE_ALL;
@@ -1527,11 +1722,35 @@ hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s) {
     if (all || stage == QMOE_STAGE_GATE_UP) {
         PfGemm p = grouped(a, a.eg, &a.eu, a.I, a.H, a.x, a.K, items);
         p.hout = a.h;
-        if (isz == 16) pf_gemm<2, 4, 1, F_GROUPED | F_HOUT>(p, s);
+        if (isz == PB_TOK) {
+            p.nrb = (a.I + PB_ROWS - 1) / PB_ROWS;
+            const hipError_t e = launch_big<2, F_HOUT>(p, s);
+            if (e != hipSuccess) return e;
+        } else if (isz == 16) pf_gemm<2, 4, 1, F_GROUPED | F_HOUT>(p, s);
         else if (isz == 32) pf_gemm<2, 4, 2, F_GROUPED | F_HOUT>(p, s);
         else pf_gemm<2, 4, 4, F_GROUPED | F_HOUT>(p, s);
     }
-    if (all || stage == QMOE_STAGE_DOWN) {
+    if ((all || stage == QMOE_STAGE_DOWN) && isz == PB_TOK) {
+        // large items: the grouped down on the large-item GEMM, then the shared expert's dense
+        // down over 64-token groups (resident activations at inner size 512)
+        PfGemm p = grouped(a, a.ed, nullptr, a.H, a.I, a.h, 1, items);
+        p.hout = a.o;
+        p.nrb = (a.H + PB_ROWS - 1) / PB_ROWS;
+        const hipError_t e = launch_big<1, F_O16>(p, s);
+        if (e != hipSuccess) return e;
+        if (a.SI == 512) {
+            PfGemm q = gemm_args(a.shd, nullptr, a.H, a.SI, a.hs, a.H, (a.T + 63) / 64);
+            q.T = a.T;
+            q.out0 = a.os;
+            q.nrb = (a.H + PF_ROWS * PF_RES_RBG - 1) / (PF_ROWS * PF_RES_RBG);
+            k_pf_down_res<4, 4, PF_RES_RBG><<<(unsigned)(q.nrb * q.items), 256, 0, s>>>(q, q, 0);
+        } else {
+            PfGemm q = gemm_args(a.shd, nullptr, a.H, a.SI, a.hs, a.H, (a.T + 31) / 32);
+            q.T = a.T;
+            q.out0 = a.os;
+            pf_gemm<1, 4, 2, 0>(q, s);
+        }
+    } else if (all || stage == QMOE_STAGE_DOWN) {
         PfGemm p = grouped(a, a.ed, nullptr, a.H, a.I, a.h, 1, items);
         p.hout = a.o;   // fp16 down outputs of the (token, k) pairs
         PfGemm q = gemm_args(a.shd, nullptr, a.H, a.SI, a.hs, a.H, (a.T + 31) / 32);   // 32-token groups
@@ -1573,6 +1792,8 @@ hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s) {
             else pf_gemm<1, 4, 4, F_GROUPED | F_O16>(p, s);
             pf_gemm<1, 4, 2, 0>(q, s);
         }
+    }
+    if (all || stage == QMOE_STAGE_DOWN) {
         // blocks of 16 (few tokens) or 8 (many) tokens x 128 features
         if (a.T < PF_MANY_T) {
             k_pf_combine<<<(unsigned)((a.T + 15) / 16 * (a.H / 128)), 256, 0, s>>>(a);
