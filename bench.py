@@ -481,19 +481,24 @@ def bench_moe_prefill(args, q, torch):
     step_bytes = (MAT_BYTES_8BIT(E, H) + MAT_BYTES_8BIT(1, H) + used * 3 * MAT_BYTES_4BIT(I, H)
                   + 3 * MAT_BYTES_4BIT(SI, H) + 3 * RANK * (H + SI) * 2 + 2 * T * H * 2)
     step_flops = 2 * T * (E * H + H + 3 * SI * H + 4 * 3 * I * H)
-    key = f"moe_prefill{'' if T == 512 else f'_{T}'}{'_skew' if args.skew else ''}/k_pf_gemm"
+    # the gate/up kernel: the large-item GEMM once experts average more than 64 pairs
+    big = pairs > 64 * E
+    gu_kernel = "k_pf_big" if big else "k_pf_gemm"
+    gu_name = (f"{gu_kernel} grouped gate/up ({'128-pair items, 32x32x16 MFMA' if big else 'small items'}; "
+               "silu*up epilogue)")
+    key = f"moe_prefill_{T}{'_skew' if args.skew else ''}/{gu_kernel}"
     ctr = counter_entry(key) or {}
     counted = {k: ctr[k] for k in ("traffic_bytes_per_launch", "mfma_flops_per_launch",
                                    "mfma_busy_frac") if k in ctr}
     if sweep:
-        roofline = {"kernel": "k_pf_gemm grouped gate/up (silu*up epilogue)",
+        roofline = {"kernel": gu_name,
                     "bound": "mfma", "achieved": tflops, "peak": FP16_MFMA_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": tflops / FP16_MFMA_PEAK_TFLOPS,
                     "traffic": ctr.get("traffic_bytes_per_launch"),
                     "flops_per_launch": gu_flops, "us_per_launch": us,
                     "hbm_gbps": achieved, "hbm_frac": achieved / HBM_PEAK_GBS, "counters": counted}
     else:
-        roofline = {"kernel": "k_pf_gemm grouped gate/up (silu*up epilogue)",
+        roofline = {"kernel": gu_name,
                     "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                     "traffic": ctr.get("traffic_bytes_per_launch"),
@@ -694,7 +699,9 @@ def bench_supergroup(args, q, torch, a8=False):
                       "tflops": flops / (us * 1e-6) / 1e12},
            "roofline": {"kernel": f"{name}_gemv" if B <= 8 else f"{name}_mfma", "bound": "hbm",
                         "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                        "frac": ach / HBM_PEAK_GBS, "traffic": None, "bytes_per_launch": bytes_,
+                        "frac": ach / HBM_PEAK_GBS,
+                        "traffic": measured_traffic(f"supergroup{'_a8' if a8 else ''}_b{B}/{name}"),
+                        "bytes_per_launch": bytes_,
                         "us_per_launch": us, "mfma_tflops": flops / (us * 1e-6) / 1e12,
                         "mfma_frac": flops / (us * 1e-6) / 1e12 / mfma_peak}}
     return res, (lambda: cpu_baseline_supergroup(B, a8=a8))
@@ -796,7 +803,8 @@ def bench_gemv(args, q, torch):
            "config": {"workload": f"qlinear_int4 x[1x2048] W[512x2048] {fmt}, 2048 weight copies rotated"},
            "roofline": {"kernel": f"k_qgemv_fast<4,{G},{'bf16' if bf else 'f16'}>", "bound": "hbm", "achieved": ach,
                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
-                        "traffic": None, "bytes_per_launch": bytes_, "us_per_launch": ms / K * 1e3}}
+                        "traffic": measured_traffic(f"gemv_g{G}{'_bf16' if bf else ''}/k_qgemv_fast"),
+                        "bytes_per_launch": bytes_, "us_per_launch": ms / K * 1e3}}
     return res, (lambda: cpu_baseline_gemv(G, bf))
 
 
@@ -849,8 +857,8 @@ def bench_prerouter(args, q, torch):
                                   f"{HEADS} heads rotated"},
            "roofline": {"kernel": "whole call (k_pr_fc1, k_pr_fc2, k_router_topk)", "bound": "hbm",
                         "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                        "frac": ach / HBM_PEAK_GBS, "traffic": None, "bytes_per_launch": bytes_,
-                        "us_per_launch": us}}
+                        "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic("prerouter/call"),
+                        "bytes_per_launch": bytes_, "us_per_launch": us}}
     return res, cpu_baseline_prerouter
 
 
