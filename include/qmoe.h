@@ -84,7 +84,11 @@ extern "C" {
  * parameters (QMOE_PARAM_BF16), the format of the bit-exact port page's QAT checkpoint
  * ([R3] "4-bit group quantization": 32 weights per group, scale and bias in bf16), whose
  * packed words and parameters are used as given, without requantization.  The MoE layer
- * takes group 64, fp16.  param_dtype 0 (the zero-initialised default) is fp16.
+ * takes them for its routed expert stacks (exp_gate, exp_up, exp_down: one format for all
+ * three, hidden and inter each 512, 1024 or 2048; such a layer runs the token-sorted path at
+ * every token count); its router, shared gate and shared expert are group 64, fp16.  bf16
+ * parameters are converted to fp16 before use, which is exact inside fp16's normal range.
+ * param_dtype 0 (the zero-initialised default) is fp16.
  */
 #define QMOE_PARAM_F16 0
 #define QMOE_PARAM_BF16 1

@@ -41,12 +41,14 @@ int check_qweight(const qmoe_qweight* w, int bits_required, bool dense = false) 
     return QMOE_OK;
 }
 
-int check_shape(const qmoe_qweight& w, int rows, int cols, int n_experts, int bits) {
-    int st = check_qweight(&w, bits);
+int check_shape(const qmoe_qweight& w, int rows, int cols, int n_experts, int bits, bool any_format = false) {
+    int st = check_qweight(&w, bits, any_format);
     if (st) return st;
     if (w.rows != rows || w.cols != cols || w.n_experts != n_experts) return QMOE_ERR_INVALID_ARG;
     return QMOE_OK;
 }
+
+bool steps_staged(int k) { return k == 512 || k == 1024 || k == 2048; }
 
 int check_lora(const qmoe_lora* l, int in_dim, int out_dim) {
     if (!l) return QMOE_OK;
@@ -74,9 +76,17 @@ int check_layer(const qmoe_moe_layer* L) {
     int st;
     if ((st = check_shape(L->router, E, H, 1, 8))) return st;
     if ((st = check_shape(L->shared_gate, 1, H, 1, 8))) return st;
-    if ((st = check_shape(L->exp_gate, I, H, E, 4))) return st;
-    if ((st = check_shape(L->exp_up, I, H, E, 4))) return st;
-    if ((st = check_shape(L->exp_down, H, I, E, 4))) return st;
+    // routed expert stacks: group 64 with fp16 parameters, or (the port page's checkpoint
+    // format) group 32 and/or bf16 parameters, the same for all three, for hidden and inter
+    // of 512, 1024 or 2048
+    if ((st = check_shape(L->exp_gate, I, H, E, 4, true))) return st;
+    if ((st = check_shape(L->exp_up, I, H, E, 4, true))) return st;
+    if ((st = check_shape(L->exp_down, H, I, E, 4, true))) return st;
+    if (L->exp_up.group != L->exp_gate.group || L->exp_down.group != L->exp_gate.group ||
+        L->exp_up.param_dtype != L->exp_gate.param_dtype || L->exp_down.param_dtype != L->exp_gate.param_dtype)
+        return QMOE_ERR_UNSUPPORTED;
+    if ((L->exp_gate.group != 64 || L->exp_gate.param_dtype != QMOE_PARAM_F16) && !(steps_staged(H) && steps_staged(I)))
+        return QMOE_ERR_UNSUPPORTED;
     if ((st = check_shape(L->sh_gate, SI, H, 1, 4))) return st;
     if ((st = check_shape(L->sh_up, SI, H, 1, 4))) return st;
     if ((st = check_shape(L->sh_down, H, SI, 1, 4))) return st;

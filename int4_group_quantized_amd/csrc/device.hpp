@@ -26,6 +26,11 @@ __device__ __forceinline__ uint16_t f2h(float v) { return __builtin_bit_cast(uin
 
 // bf16 bits -> fp32 (exact): the upper half of the fp32 pattern
 __device__ __forceinline__ float bf2f(uint16_t b) { return __builtin_bit_cast(float, (uint32_t)b << 16); }
+// Two bf16 values (low and high half) as two fp16 values, rounded to nearest (exact for bf16
+// values inside fp16's normal range, whose 8 significant bits fit fp16's 11).
+__device__ __forceinline__ uint32_t bf2_to_h2(uint32_t v) {
+    return (uint32_t)f2h(bf2f((uint16_t)(v & 0xFFFFu))) | ((uint32_t)f2h(bf2f((uint16_t)(v >> 16))) << 16);
+}
 
 __device__ __forceinline__ f16x2 as_h2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
 __device__ __forceinline__ uint32_t as_u32(f16x2 h) { return __builtin_bit_cast(uint32_t, h); }

@@ -149,6 +149,8 @@ hipError_t launch_moe(const qmoe_moe_layer& L, int stage, const uint16_t* x, int
     a.idx_out = idx_out;
     a.w_out = w_out;
     a.route = route;
+    a.egroup = L.exp_gate.group;
+    a.ebf = L.exp_gate.param_dtype == QMOE_PARAM_BF16;
     if (decode_path_fits(L, T)) return launch_moe_decode(a, stage, s);
     return launch_moe_prefill(a, stage, s);
 }

@@ -34,6 +34,7 @@ struct MoeArgs {
     float lsg, lsu, lsd;
     const float* rbias;
     const int32_t* route;   // given selection [T][K] (the caller's routing), or null: top-K
+    int egroup, ebf;        // routed experts' group size (64 or 32) and bf16 parameters (1)
     // workspace
     float *logits, *gate, *zg, *zu, *zd, *gs, *us;
     int32_t* idx;
@@ -197,8 +198,8 @@ __device__ inline void xside_lora_z(const MoeArgs& a, int j, int zjobs) {
 bool decode_path_fits(const qmoe_moe_layer& L, int T);
 hipError_t launch_moe_decode(const MoeArgs& a, int stage, hipStream_t s);
 // moe_prefill.hip
-int prefill_max_items(int E, int T, int K, int H, int I);
-int prefill_item_size(int E, int T, int K, int H, int I);
+int prefill_max_items(int E, int T, int K, int H, int I, bool std_experts = true);
+int prefill_item_size(int E, int T, int K, int H, int I, bool std_experts = true);
 int prefill_ksplit(int hidden, int T);
 hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s);
 

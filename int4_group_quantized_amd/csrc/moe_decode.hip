@@ -588,7 +588,9 @@ static int chunks_per_lane(int K) { return (K / 32) / lanes_per_row(K); }
 // pairs on, the token-sorted path (each used expert read once, MFMA) is faster on MI355X
 // (measured at 16 x 8, 8 x 8, 8 x 4 and 4 x 8 pairs), below it its fixed route cost loses.
 bool decode_path_fits(const qmoe_moe_layer& L, int T) {
-    return T * L.top_k < 32 && T <= MAX_DEC_T && L.top_k <= MAX_DEC_K && L.inter == L.shared_inter &&
+    // routed experts in groups of 32 or with bf16 parameters run the token-sorted path
+    const bool std_experts = L.exp_gate.group == 64 && L.exp_gate.param_dtype == QMOE_PARAM_F16;
+    return std_experts && T * L.top_k < 32 && T <= MAX_DEC_T && L.top_k <= MAX_DEC_K && L.inter == L.shared_inter &&
            L.hidden <= 4096 && L.inter <= 2048 && chunks_per_lane(L.hidden) <= 2 &&
            chunks_per_lane(L.inter) <= 1;
 }

@@ -61,6 +61,7 @@ struct PfGemm {
     int act_div;                   // grouped: activation row = pair / act_div (1: pair itself)
     const int32_t *wrec, *wpairs;  // grouped: work items (expert, tokens) and their pair ids
     int nrb, items;                // row blocks, grid items (a multiple of 8)
+    int bf;                        // grouped fp16-weight GEMMs: scales and biases stored as bf16
     float* out0; float* out1;      // fp32 outputs [row][ostride]
     int ostride;
     int ksplit;                    // dense: K split over this many blocks (partial outputs)
@@ -76,16 +77,18 @@ constexpr int F_GROUPED = 1;   // work items of the expert sort (else token grou
 constexpr int F_HOUT = 2;      // fp16 silu(out0) * out1 (else fp32 outputs)
 constexpr int F_O16 = 8;       // fp16 outputs to hout, single matrix (the experts' down outputs)
 constexpr int F_EXTRA = 4;     // one extra feature row from a second matrix (single matrix)
+constexpr int F_G32 = 16;      // groups of 32 inputs (four per step; grouped fp16-weight GEMMs)
 constexpr int PF_RES_RBG = 4;  // row blocks per block of the resident-activation GEMM
 
 // LDS of one GEMM block: the activation tile (double buffer: step ks computes from ks % 2
 // while step ks + 1's tile is staged into the other), and with a compile-time step count NS
-// the block's scales and biases as (s | b << 16) dwords per (row, group), row pitch 2 NS + 4
-// dwords (16 rows read without bank conflicts).
-template <int NT, int NMAT, int NS>
+// the block's scales and biases as (s | b << 16) dwords per (row, group), row pitch GPS NS + 4
+// dwords (16 rows read without bank conflicts; GPS groups per 128-input step: 2, or 4 for
+// groups of 32).
+template <int NT, int NMAT, int NS, int GPS = 2>
 struct PfSmem {
     f16 tile[2][16 * NT * PF_PITCH];
-    uint32_t sb[NMAT][PF_ROWS][NS ? 2 * NS + 4 : 1];
+    uint32_t sb[NMAT][PF_ROWS][NS ? GPS * NS + 4 : 1];   // (s, b) per group; GPS groups a step
     int arow[16 * NT], orow[16 * NT];
 };
 
@@ -160,8 +163,8 @@ struct PfSlot {
 // The block's token rows: for a work item (GROUPED) the expert and its pair ids, padded
 // by repeating the last pair (activation rows of the padding are loaded, their results never
 // stored); for a dense GEMM the token group and split of `item`.  False: nothing to do.
-template <int NT, int FL, int NS, int SM_NMAT, int NTS>
-__device__ __forceinline__ bool pf_setup(const PfGemm& a, int item, PfSmem<NTS, SM_NMAT, NS>& sm,
+template <int NT, int FL, int NS, int SM_NMAT, int NTS, int GPS>
+__device__ __forceinline__ bool pf_setup(const PfGemm& a, int item, PfSmem<NTS, SM_NMAT, NS, GPS>& sm,
                                          int& ntok, int& e, int& split) {
     constexpr bool GROUPED = FL & F_GROUPED;
     constexpr int TOKB = 16 * NT;
@@ -199,19 +202,24 @@ __device__ __forceinline__ bool pf_setup(const PfGemm& a, int item, PfSmem<NTS, 
 // buffer one step before their use.  The weight rows of one block share a base address (the
 // expert's matrix) held in scalar registers; a lane keeps 32-bit offsets, or in the fp16
 // path (registers to spare) its row pointers formed once.
-template <int NMAT, int BITS, int NTE, int FL, int NS, int SM_NMAT, int NTS>
+template <int NMAT, int BITS, int NTE, int FL, int NS, int SM_NMAT, int NTS, int GPS>
 __device__ __forceinline__ void pf_gemm_body(const PfGemm& a, int rb, int ntok, int e, int split,
-                                             PfSmem<NTS, SM_NMAT, NS>& sm) {
+                                             PfSmem<NTS, SM_NMAT, NS, GPS>& sm) {
     static_assert(SM_NMAT >= NMAT, "LDS holds the scales of every matrix");
     static_assert(NTE <= NTS, "LDS holds every tile");
     constexpr bool HOUT = FL & F_HOUT, EXTRA = FL & F_EXTRA;
     // fp16 weights for the grouped 4-bit GEMMs and the dense ones with four token tiles;
     // exact codes for the 8-bit router and for dense GEMMs of fewer tiles
     constexpr bool DQ = BITS == 4 && ((FL & F_GROUPED) || NTE >= 4);
+    // groups of 32: grouped fp16-weight GEMMs with a compile-time step count (parameters
+    // staged in LDS), GPS = 4 groups per step
+    constexpr bool G32 = FL & F_G32;
+    static_assert(!G32 || (DQ && NS > 0 && !(FL & F_EXTRA)), "groups of 32: staged fp16-weight GEMMs");
+    static_assert(GPS == (G32 ? 4 : 2), "LDS sized for the group size");
     const int ntiles = (ntok + 15) >> 4;   // <= NTE
     // NS > 0: the block's step count known at compile time (the loop fully unrolled); the
     // block covers steps kofs .. kofs + nsteps - 1 of the row (split-K for dense GEMMs)
-    const int K = a.K, G = K / 64, nsteps = NS ? NS : K / PF_KS;   // even
+    const int K = a.K, G = K / (G32 ? 32 : 64), nsteps = NS ? NS : K / PF_KS;   // even
     const int kofs = split * nsteps;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane & 15, j = lane >> 4;
@@ -237,12 +245,13 @@ __device__ __forceinline__ void pf_gemm_body(const PfGemm& a, int rb, int ntok, 
     const uint16_t* xs = xrow ? a.xs : sb[0] + goff;
     const uint16_t* xb = xrow ? a.xb : bb_[0] + goff;
     // with NS known: the block's scales and biases into LDS with 16-byte loads, 8 groups a unit
-    uint4 sbr[NMAT][2][NS ? (NS * 16 + 255) / 256 : 1];
+    constexpr int UPR = NS * GPS / 8;                        // units of 8 groups per row
+    constexpr int SBI = NS ? (PF_ROWS * UPR + 255) / 256 : 1;   // units per thread
+    uint4 sbr[NMAT][2][SBI];
     auto load_sb = [&] {
         if constexpr (NS > 0) {
-            constexpr int UPR = NS / 4;   // units of 8 groups per row
 #pragma unroll
-            for (int i = 0; i < (NS * 16 + 255) / 256; ++i) {
+            for (int i = 0; i < SBI; ++i) {
                 const int u = min(i * 256 + (int)threadIdx.x, PF_ROWS * UPR - 1);
                 const int r = u / UPR, c8 = u % UPR, rowg = rb * PF_ROWS + r;
 #pragma unroll
@@ -250,24 +259,31 @@ __device__ __forceinline__ void pf_gemm_body(const PfGemm& a, int rb, int ntok, 
                     const uint16_t* ss = sb[m] + (long)min(rowg, a.N - 1) * G;
                     const uint16_t* bs = bb_[m] + (long)min(rowg, a.N - 1) * G;
                     if (EXTRA && rowg >= a.N) { ss = a.xs; bs = a.xb; }
-                    sbr[m][0][i] = reinterpret_cast<const uint4*>(ss + 2 * kofs)[c8];
-                    sbr[m][1][i] = reinterpret_cast<const uint4*>(bs + 2 * kofs)[c8];
+                    sbr[m][0][i] = reinterpret_cast<const uint4*>(ss + GPS * kofs)[c8];
+                    sbr[m][1][i] = reinterpret_cast<const uint4*>(bs + GPS * kofs)[c8];
                 }
             }
         }
     };
     auto commit_sb = [&] {
         if constexpr (NS > 0) {
-            constexpr int UPR = NS / 4;
 #pragma unroll
-            for (int i = 0; i < (NS * 16 + 255) / 256; ++i) {
+            for (int i = 0; i < SBI; ++i) {
                 const int u = i * 256 + (int)threadIdx.x;
                 if (u < PF_ROWS * UPR) {
                     const int r = u / UPR, c8 = u % UPR;
 #pragma unroll
                     for (int m = 0; m < NMAT; ++m) {
-                        const uint32_t* sv = reinterpret_cast<const uint32_t*>(&sbr[m][0][i]);
-                        const uint32_t* bv = reinterpret_cast<const uint32_t*>(&sbr[m][1][i]);
+                        uint32_t sv[4], bv[4];
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            sv[k] = reinterpret_cast<const uint32_t*>(&sbr[m][0][i])[k];
+                            bv[k] = reinterpret_cast<const uint32_t*>(&sbr[m][1][i])[k];
+                            if constexpr (DQ) {   // bf16 parameters: fp16 pairs (exact in fp16's normal range)
+                                sv[k] = a.bf ? bf2_to_h2(sv[k]) : sv[k];
+                                bv[k] = a.bf ? bf2_to_h2(bv[k]) : bv[k];
+                            }
+                        }
                         uint32_t o[8];
 #pragma unroll
                         for (int k = 0; k < 4; ++k) {
@@ -391,7 +407,13 @@ __device__ __forceinline__ void pf_gemm_body(const PfGemm& a, int rb, int ntok, 
                     cw[m][(2 * h + 1) * WPU + v] = r[1];
                 }
             }
-            if constexpr (NS > 0) {
+            if constexpr (NS > 0 && G32) {
+                // groups of 32: register slot g of lane group j covers group 2 g + (j & 1)
+                const uint4 p = *reinterpret_cast<const uint4*>(&sm.sb[m][wave * 16 + col][4 * ks]);
+                const f16x2 g0 = as_h2((j & 1) ? p.y : p.x), g1 = as_h2((j & 1) ? p.w : p.z);
+                sh[m][0] = g0[0]; bh[m][0] = g0[1];
+                sh[m][1] = g1[0]; bh[m][1] = g1[1];
+            } else if constexpr (NS > 0) {
                 const uint2 p = *reinterpret_cast<const uint2*>(&sm.sb[m][wave * 16 + col][2 * ks]);
                 const f16x2 g0 = as_h2(p.x), g1 = as_h2(p.y);   // (s, b) of the step's groups
                 sh[m][0] = g0[0]; bh[m][0] = g0[1];
@@ -510,20 +532,20 @@ __device__ __forceinline__ void pf_gemm_body(const PfGemm& a, int rb, int ntok, 
 // One block: the token rows of `item` (NT tiles of 16), then the GEMM over them.  LDS is
 // sized for NTS >= NT tiles, so kernels that run GEMMs of two tile counts share one layout.
 // (One body per kernel: with two inlined bodies the register allocation spills.)
-template <int NMAT, int BITS, int NT, int FL, int NS, int SM_NMAT, int NTS = NT>
+template <int NMAT, int BITS, int NT, int FL, int NS, int SM_NMAT, int NTS = NT, int GPS = 2>
 __device__ __forceinline__ void pf_gemm_block(const PfGemm& a, int rb, int item,
-                                              PfSmem<NTS, SM_NMAT, NS>& sm) {
+                                              PfSmem<NTS, SM_NMAT, NS, GPS>& sm) {
     int ntok, e, split;
-    if (!pf_setup<NT, FL, NS, SM_NMAT, NTS>(a, item, sm, ntok, e, split)) return;
-    pf_gemm_body<NMAT, BITS, NT, FL, NS, SM_NMAT, NTS>(a, rb, ntok, e, split, sm);
+    if (!pf_setup<NT, FL, NS, SM_NMAT, NTS, GPS>(a, item, sm, ntok, e, split)) return;
+    pf_gemm_body<NMAT, BITS, NT, FL, NS, SM_NMAT, NTS, GPS>(a, rb, ntok, e, split, sm);
 }
 
 template <int NMAT, int BITS, int NT, int FL, int NS>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) k_pf_gemm(PfGemm a) {
-    __shared__ __align__(16) PfSmem<NT, NMAT, NS> sm;
+    __shared__ __align__(16) PfSmem<NT, NMAT, NS, (FL & F_G32) ? 4 : 2> sm;
     int rb, item;
     pf_block(blockIdx.x, a.nrb, rb, item);
-    pf_gemm_block<NMAT, BITS, NT, FL, NS, NMAT>(a, rb, item, sm);
+    pf_gemm_block<NMAT, BITS, NT, FL, NS, NMAT, NT, (FL & F_G32) ? 4 : 2>(a, rb, item, sm);
 }
 
 // The grouped down GEMM and the shared expert's dense down GEMM in one launch (they are
@@ -1631,6 +1653,24 @@ void pf_gemm(const PfGemm& p, hipStream_t s) {
     }
 }
 
+// The grouped fp16-weight GEMM with its parameters staged in LDS (reductions of 512, 1024 or
+// 2048 inputs), one or four token tiles: the routed experts' GEMMs in groups of 32 or with
+// bf16 parameters.
+template <int NMAT, int FL>
+hipError_t pf_gemm_staged(const PfGemm& p, int nt, hipStream_t s) {
+    const dim3 grid((unsigned)(p.nrb * p.items));
+    switch ((p.K / PF_KS) * 8 + nt) {
+        case 4 * 8 + 1: k_pf_gemm<NMAT, 4, 1, FL, 4><<<grid, 256, 0, s>>>(p); break;
+        case 4 * 8 + 4: k_pf_gemm<NMAT, 4, 4, FL, 4><<<grid, 256, 0, s>>>(p); break;
+        case 8 * 8 + 1: k_pf_gemm<NMAT, 4, 1, FL, 8><<<grid, 256, 0, s>>>(p); break;
+        case 8 * 8 + 4: k_pf_gemm<NMAT, 4, 4, FL, 8><<<grid, 256, 0, s>>>(p); break;
+        case 16 * 8 + 1: k_pf_gemm<NMAT, 4, 1, FL, 16><<<grid, 256, 0, s>>>(p); break;
+        case 16 * 8 + 4: k_pf_gemm<NMAT, 4, 4, FL, 16><<<grid, 256, 0, s>>>(p); break;
+        default: return hipErrorInvalidValue;   // the layer check admits no other shape
+    }
+    return hipSuccess;
+}
+
 // Arguments of one GEMM over `feat` feature rows (N plus an optional extra row) and `items`
 // token groups or work items.
 PfGemm gemm_args(const QW& w0, const QW* w1, int N, int K, const uint16_t* act, int feat,
@@ -1660,16 +1700,18 @@ PfGemm grouped(const MoeArgs& a, const QW& w0, const QW* w1, int N, int K, const
 // second pass over their weights; 32 up to an average of 32; 64 up to 64 (four tiles: each
 // weight step feeds four times the MFMA work, the regime where the GEMMs turn compute-bound);
 // above that PB_TOK = 128, the large-item GEMMs (hidden and inter up to 2048).
-int prefill_item_size(int E, int T, int K, int H, int I) {
+int prefill_item_size(int E, int T, int K, int H, int I, bool std_experts) {
     const long tk = (long)T * K;
+    // experts in groups of 32 or with bf16 parameters: 16 or 64 pairs (one- or four-tile GEMMs)
+    if (!std_experts) return tk <= 8l * E ? 16 : 64;
     if (tk > 64l * E && big_steps_ok(H) && big_steps_ok(I)) return PB_TOK;
     return tk <= 8l * E ? 16 : tk <= 32l * E ? 32 : 64;
 }
 
 // Upper bound on the work items of the sort, rounded up to the 8 XCDs of the block order:
 // sum over experts of ceil(count / isz) <= E + T K / isz.
-int prefill_max_items(int E, int T, int K, int H, int I) {
-    const int isz = prefill_item_size(E, T, K, H, I);
+int prefill_max_items(int E, int T, int K, int H, int I, bool std_experts) {
+    const int isz = prefill_item_size(E, T, K, H, I, std_experts);
     return (E + (T * K + isz - 1) / isz + 7) / 8 * 8;
 }
 
@@ -1679,7 +1721,9 @@ static int xs_inputs(int hidden, int T) { return T >= PF_XS_BIG_T ? std::min(hid
 int prefill_ksplit(int hidden, int T) { return hidden / xs_inputs(hidden, T); }
 
 hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s) {
-    const int items = prefill_max_items(a.E, a.T, a.K, a.H, a.I), isz = prefill_item_size(a.E, a.T, a.K, a.H, a.I);
+    const bool std_experts = a.egroup == 64 && !a.ebf;
+    const int items = prefill_max_items(a.E, a.T, a.K, a.H, a.I, std_experts);
+    const int isz = prefill_item_size(a.E, a.T, a.K, a.H, a.I, std_experts);
     const int tgroups = (a.T + PF_TOK - 1) / PF_TOK;
     const int ksplit = prefill_ksplit(a.H, a.T);
     const bool all = stage == QMOE_STAGE_ALL;
@@ -1719,7 +1763,30 @@ hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s) {
             k_pf_place<<<nseg, 1024, 0, s>>>(a, items, isz, cpb, nseg);
         }
     }
-    if (all || stage == QMOE_STAGE_GATE_UP) {
+    if (!std_experts) {
+        // routed experts in groups of 32 and/or with bf16 parameters: the staged
+        // fp16-weight GEMM for gate/up and down, the shared expert's dense down apart
+        if (all || stage == QMOE_STAGE_GATE_UP) {
+            PfGemm p = grouped(a, a.eg, &a.eu, a.I, a.H, a.x, a.K, items);
+            p.hout = a.h;
+            p.bf = a.ebf;
+            const hipError_t e = a.egroup == 32 ? pf_gemm_staged<2, F_GROUPED | F_HOUT | F_G32>(p, isz / 16, s)
+                                                : pf_gemm_staged<2, F_GROUPED | F_HOUT>(p, isz / 16, s);
+            if (e != hipSuccess) return e;
+        }
+        if (all || stage == QMOE_STAGE_DOWN) {
+            PfGemm p = grouped(a, a.ed, nullptr, a.H, a.I, a.h, 1, items);
+            p.hout = a.o;
+            p.bf = a.ebf;
+            const hipError_t e = a.egroup == 32 ? pf_gemm_staged<1, F_GROUPED | F_O16 | F_G32>(p, isz / 16, s)
+                                                : pf_gemm_staged<1, F_GROUPED | F_O16>(p, isz / 16, s);
+            if (e != hipSuccess) return e;
+            PfGemm q = gemm_args(a.shd, nullptr, a.H, a.SI, a.hs, a.H, (a.T + 31) / 32);
+            q.T = a.T;
+            q.out0 = a.os;
+            pf_gemm<1, 4, 2, 0>(q, s);
+        }
+    } else if (all || stage == QMOE_STAGE_GATE_UP) {
         PfGemm p = grouped(a, a.eg, &a.eu, a.I, a.H, a.x, a.K, items);
         p.hout = a.h;
         if (isz == PB_TOK) {
@@ -1730,7 +1797,9 @@ hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s) {
         else if (isz == 32) pf_gemm<2, 4, 2, F_GROUPED | F_HOUT>(p, s);
         else pf_gemm<2, 4, 4, F_GROUPED | F_HOUT>(p, s);
     }
-    if ((all || stage == QMOE_STAGE_DOWN) && isz == PB_TOK) {
+    if (!std_experts) {
+        // (the down GEMMs above)
+    } else if ((all || stage == QMOE_STAGE_DOWN) && isz == PB_TOK) {
         // large items: the grouped down on the large-item GEMM, then the shared expert's dense
         // down over 64-token groups (resident activations at inner size 512)
         PfGemm p = grouped(a, a.ed, nullptr, a.H, a.I, a.h, 1, items);

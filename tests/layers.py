@@ -36,9 +36,10 @@ class Shape:
 
 
 def _quant(args):
-    wl, layer, role, index, rows, cols, bits = args
+    wl, layer, role, index, rows, cols, bits = args[:7]
+    group, params = args[7:] if len(args) > 7 else (64, "f16")
     w = synth.normal_f32((rows, cols), synth.WEIGHT_SIGMA, wl, layer, role, index)
-    q = affine.quantize(w, bits)
+    q = affine.quantize(w, bits, group, params)
     return q.packed, q.scales, q.biases
 
 
@@ -62,9 +63,9 @@ def quantize_many(jobs):
         return list(ex.map(_quant, jobs, chunksize=4))
 
 
-def stack(parts):
+def stack(parts, group=64, params="f16"):
     return affine.QWeight(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]),
-                          np.stack([p[2] for p in parts]), 4, 64)
+                          np.stack([p[2] for p in parts]), 4, group, params)
 
 
 def one(part, bits):
@@ -72,8 +73,12 @@ def one(part, bits):
 
 
 def build_layer(wl: int, layer: int, S: Shape, with_lora: bool = True, skew: bool = False,
-                only_experts: Optional[Iterable[int]] = None) -> moe.MoELayer:
-    """Oracle-side layer.  ``only_experts=None`` quantizes every expert."""
+                only_experts: Optional[Iterable[int]] = None, expert_group: int = 64,
+                expert_params: str = "f16") -> moe.MoELayer:
+    """Oracle-side layer.  ``only_experts=None`` quantizes every expert.  The routed expert
+    stacks may take group 32 and/or bf16 parameters (then every expert is quantized)."""
+    std = expert_group == 64 and expert_params == "f16"
+    assert std or only_experts is None, "filler experts are group 64, fp16"
     H, I, SI, E = S.hidden, S.inter, S.shared_inter, S.n_experts
     dense = [(wl, layer, R.ROUTER, 0, E, H, 8), (wl, layer, R.SHARED_GATE, 0, 1, H, 8),
              (wl, layer, R.SH_GATE, 0, SI, H, 4), (wl, layer, R.SH_UP, 0, SI, H, 4),
@@ -81,8 +86,9 @@ def build_layer(wl: int, layer: int, S: Shape, with_lora: bool = True, skew: boo
     wanted = set(range(E)) if only_experts is None else set(int(e) for e in only_experts)
     ejobs = []
     for e in sorted(wanted):
-        ejobs += [(wl, layer, R.EXP_GATE, e, I, H, 4), (wl, layer, R.EXP_UP, e, I, H, 4),
-                  (wl, layer, R.EXP_DOWN, e, H, I, 4)]
+        fmt = () if std else (expert_group, expert_params)
+        ejobs += [(wl, layer, R.EXP_GATE, e, I, H, 4) + fmt, (wl, layer, R.EXP_UP, e, I, H, 4) + fmt,
+                  (wl, layer, R.EXP_DOWN, e, H, I, 4) + fmt]
     res = quantize_many(dense + ejobs)
     router, sgate, shg, shu, shd = res[:5]
     got = {}
@@ -109,8 +115,9 @@ def build_layer(wl: int, layer: int, S: Shape, with_lora: bool = True, skew: boo
     if skew:
         bias = np.zeros(E, np.float32)
         bias[:16] = 2.0
-    return moe.MoELayer(router=one(router, 8), shared_gate=one(sgate, 8), exp_gate=stack(gates),
-                        exp_up=stack(ups), exp_down=stack(downs), sh_gate=one(shg, 4),
+    ef = (expert_group, expert_params)
+    return moe.MoELayer(router=one(router, 8), shared_gate=one(sgate, 8), exp_gate=stack(gates, *ef),
+                        exp_up=stack(ups, *ef), exp_down=stack(downs, *ef), sh_gate=one(shg, 4),
                         sh_up=one(shu, 4), sh_down=one(shd, 4), top_k=S.top_k,
                         lora_gate=loras[0], lora_up=loras[1], lora_down=loras[2],
                         router_bias=bias)
@@ -136,7 +143,8 @@ def to_device(L: moe.MoELayer, S: Shape, device="cuda", add_residual=False):
     import int4_group_quantized_amd as q
 
     def qw(w: affine.QWeight):
-        return q.QWeight.from_arrays(w.packed, w.scales, w.biases, w.bits, device)
+        return q.QWeight.from_arrays(w.packed, w.scales, w.biases, w.bits, device, group=w.group,
+                                     param_dtype=q.PARAM_BF16 if w.param_dtype == "bf16" else 0)
 
     def lo(l):
         if l is None:

@@ -270,3 +270,27 @@ def test_routed_call_validates_like_the_layer_call():
     assert f(ctypes.byref(L), X, 1, None, R, Y, None, WS, ws1 - 1, None) == _lib.QMOE_ERR_WORKSPACE
     assert f(ctypes.byref(L), X, 1, None, R, X, None, WS, ws1, None) == _lib.QMOE_ERR_INVALID_ARG
     assert f(ctypes.byref(layer_c(top_k=0)), X, 1, None, R, Y, None, WS, ws1, None) == _lib.QMOE_ERR_INVALID_ARG
+
+
+def test_moe_takes_the_port_format_for_its_routed_experts():
+    """Routed expert stacks may be group 32 and/or bf16 parameters (one format for all three,
+    hidden and inter 512, 1024 or 2048); the router, shared gate and shared expert may not."""
+    ws = q.lib.moe_switchglu_int4_workspace_bytes
+    H, I, E = 2048, 512, 256
+    for group, pdt in ((32, 1), (32, 0), (64, 1)):
+        L = layer_c(exp_gate=qw(I, H, 4, E, group=group, param_dtype=pdt),
+                    exp_up=qw(I, H, 4, E, group=group, param_dtype=pdt),
+                    exp_down=qw(H, I, 4, E, group=group, param_dtype=pdt))
+        assert ws(ctypes.byref(L), 1) > 0, (group, pdt)
+    mixed = layer_c(exp_gate=qw(I, H, 4, E, group=32, param_dtype=1), exp_up=qw(I, H, 4, E, group=32, param_dtype=1),
+                    exp_down=qw(H, I, 4, E, group=32, param_dtype=0))
+    wide = layer_c(hidden=1536, router=qw(E, 1536, 8), shared_gate=qw(1, 1536, 8),
+                   exp_gate=qw(I, 1536, 4, E, group=32), exp_up=qw(I, 1536, 4, E, group=32),
+                   exp_down=qw(1536, I, 4, E, group=32), sh_gate=qw(512, 1536), sh_up=qw(512, 1536),
+                   sh_down=qw(1536, 512))
+    std_wide = layer_c(hidden=1536, router=qw(E, 1536, 8), shared_gate=qw(1, 1536, 8),
+                       exp_gate=qw(I, 1536, 4, E), exp_up=qw(I, 1536, 4, E), exp_down=qw(1536, I, 4, E),
+                       sh_gate=qw(512, 1536), sh_up=qw(512, 1536), sh_down=qw(1536, 512))
+    assert ws(ctypes.byref(std_wide), 1) > 0
+    for bad in (mixed, wide, layer_c(router=qw(E, H, 8, group=32)), layer_c(sh_down=qw(H, 512, param_dtype=1))):
+        assert ws(ctypes.byref(bad), 1) == 0
