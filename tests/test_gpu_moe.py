@@ -321,3 +321,46 @@ def test_layer_with_degenerate_and_extreme_groups(q, T):
     y, idx, w = run_device(q, Lc, S, x, ad)
     err, rel, n_alt = check_layer(Lc, x, ad, y, idx, w)
     print(f"planted groups T={T}: max abs {err:.2e} rel L2 {rel:.2e} alternatives {n_alt}", flush=True)
+
+
+MANY_R = Shape(hidden=1536, inter=512, shared_inter=512, n_experts=16, top_k=6, rank=24, n_adapters=3)
+
+
+def test_many_tokens_combine_with_residual_adapters_and_wide_rank(q):
+    """The many-token combine (from 1024 tokens): residual stacking, three adapters changing
+    every few tokens (its LoRA-B rows reloaded when the adapter changes), LoRA rank 24 (a
+    third chunk of 8 ranks past the 16 kept in registers), top-6 (experts past the fourth),
+    and hidden 1536 (a 1024-feature block whose second half is past the features)."""
+    T = 1100
+    Lc = build_layer(synth.Workload.TEST, 47, MANY_R)
+    x = synth.activations(T, MANY_R.hidden, synth.Workload.TEST, 47, T)
+    ad = ((np.arange(T) // 5) % 3).astype(np.int32)
+    y, idx, w = run_device(q, Lc, MANY_R, x, ad, residual=True)
+    err, rel, n_alt = check_layer(Lc, x, ad, y, idx, w, residual=True)
+    print(f"many-token combine: max abs {err:.2e} rel L2 {rel:.2e} alternatives {n_alt}", flush=True)
+
+
+@pytest.mark.parametrize("K", [1, 2])
+def test_layer_exact_router_tie_goes_to_lower_expert(q, K):
+    """Router rows 3 and 5 identical (same words, scales and biases) and both favoured by the
+    router bias: every token's logits tie exactly between them.  With top-1 the tie sits at
+    the selection boundary and expert 3 must win; with top-2 both are selected, 3 first.
+    Exact index equality is required here (no near-tie allowance)."""
+    S = Shape(hidden=512, inter=512, shared_inter=512, n_experts=8, top_k=K, rank=8, n_adapters=1)
+    Lc = build_layer(synth.Workload.TEST, 48, S)
+    for arr in (Lc.router.packed, Lc.router.scales, Lc.router.biases):
+        arr[5] = arr[3]
+    bias = np.zeros(S.n_experts, np.float32)
+    bias[[3, 5]] = 4.0
+    Lc.router_bias = bias
+    T = 24
+    x = synth.activations(T, S.hidden, synth.Workload.TEST, 48, T)
+    y, idx, w = run_device(q, Lc, S, x)
+    ref = moe.moe_layer(x, Lc, None)
+    expect = np.array([[3] if K == 1 else [3, 5]] * T, np.int32)
+    assert np.array_equal(ref["idx"], expect)
+    assert np.array_equal(idx, expect)
+    if K == 2:
+        np.testing.assert_allclose(w, 0.5, rtol=0, atol=1e-7)
+    from layers import assert_close
+    assert_close(y, ref["y64"], what="tied router")
