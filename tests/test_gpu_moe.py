@@ -181,12 +181,26 @@ def test_decode_one_token_full_shape(q):
     8-bit gate, LoRA rank 16 alpha 32 on the shared projections."""
     S = Shape(top_k=4)
     wl = synth.Workload.MOE_DECODE
-    for i in range(3):
-        x = synth.activations(1, S.hidden, wl, 0, i)
-        Lc = build_layer(wl, 0, S, only_experts=routed_experts(x, wl, 0, S))
-        y, idx, w = run_device(q, Lc, S, x)
-        err, rel, _ = check_layer(Lc, x, None, y, idx, w)
-        print(f"decode token {i}: max abs {err:.2e} rel L2 {rel:.2e}", flush=True)
+    for layer in range(2):
+        for i in range(4):
+            x = synth.activations(1, S.hidden, wl, layer, i)
+            Lc = build_layer(wl, layer, S, only_experts=routed_experts(x, wl, layer, S))
+            y, idx, w = run_device(q, Lc, S, x)
+            err, rel, _ = check_layer(Lc, x, None, y, idx, w)
+            print(f"decode layer {layer} token {i}: max abs {err:.2e} rel L2 {rel:.2e}", flush=True)
+
+
+def test_decode_seven_tokens_full_shape_with_adapters(q):
+    """Seven tokens in one decode call (28 routed pairs, the largest batch of the decode
+    path at top-4) at the full shape, four LoRA adapter sets chosen per token."""
+    S = Shape(top_k=4, n_adapters=4)
+    wl = synth.Workload.MOE_DECODE
+    x = synth.activations(7, S.hidden, wl, 2, 0)
+    Lc = build_layer(wl, 2, S, only_experts=routed_experts(x, wl, 2, S))
+    ad = np.array([0, 1, 2, 3, 3, 1, 0], np.int32)
+    y, idx, w = run_device(q, Lc, S, x, ad)
+    err, rel, n_alt = check_layer(Lc, x, ad, y, idx, w)
+    print(f"decode 7 tokens: max abs {err:.2e} rel L2 {rel:.2e} alternatives {n_alt}", flush=True)
 
 
 @pytest.fixture(scope="module")
