@@ -129,6 +129,40 @@ def graph_of(torch, fn):
     return g
 
 
+def chunked_graphs(torch, step, n, chunk):
+    """Graphs that together run exactly n repetitions of `step` (which must do the same work
+    each time): one of `chunk` steps with its replay count, and one of the remainder.  Keeps
+    every graph at a bounded node count (a 40-layer step is 240 launches)."""
+    full, rem = divmod(n, chunk)
+    parts = []
+    if full:
+        parts.append((graph_of(torch, lambda: [step() for _ in range(chunk)]), full))
+    if rem:
+        parts.append((graph_of(torch, lambda: [step() for _ in range(rem)]), 1))
+    return parts
+
+
+def replay_chunks(parts):
+    for g, reps in parts:
+        for _ in range(reps):
+            g.replay()
+
+
+def time_chunks(torch, parts, flush=None):
+    """ms of one pass over `parts` (every graph replayed its count, in order), HIP events on
+    the stream they run on; with `flush`, the caches are flushed first, outside the span."""
+    st = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    if flush is not None:
+        flush()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(st)
+    replay_chunks(parts)
+    b.record(st)
+    b.synchronize()
+    return a.elapsed_time(b)
+
+
 def time_graph(torch, g, reps=1, flush=None):
     """Average ms of one replay: HIP events on the stream the graph runs on.  With `flush`,
     the caches are flushed before each replay, outside the timed span."""
@@ -578,11 +612,12 @@ def bench_moe_stack(args, q, torch):
             c()
     acts[0].copy_(x0)
     flush = CacheFlush(torch)
+    # graphs of at most 25 steps (6,000 launches), replayed to make exactly W, then K steps
+    CH = 25
     if W:
-        gw = graph_of(torch, lambda: [step() for _ in range(W)])
-        gw.replay()
-    g = graph_of(torch, lambda: [step() for _ in range(K)])
-    ms = time_graph(torch, g, flush=flush)
+        replay_chunks(chunked_graphs(torch, step, W, CH))
+    parts = chunked_graphs(torch, step, K, CH)
+    ms = time_chunks(torch, parts, flush=flush)
     ms_step = ms / K
 
     # dominant kernel: gate/up of one layer over routed workspaces (one per layer)

@@ -283,7 +283,7 @@ int moe_switchglu_int4_routed(const qmoe_moe_layer* L, const uint16_t* x, int32_
  * holds QMOE_NOALLOC_SCRATCH_BYTES per device and is kept from the first call on a device
  * until the process ends; a call whose workspace (moe_switchglu_int4_workspace_bytes of the
  * layer at t tokens) exceeds it fails with QMOE_ERR_WORKSPACE before anything is enqueued
- * (hidden 2048, 256 experts, top-4: up to 512 tokens).  The call allocates and frees
+ * (hidden 2048, 256 experts, top-4: up to 609 tokens).  The call allocates and frees
  * nothing.  All calls on one device share that device's scratch, which keeps the last
  * call's contents (nothing in it needs to start at zero): calls that overlap in time on one
  * device (two streams, two host threads) race, and the caller must serialise them.
