@@ -199,6 +199,116 @@ __global__ void __launch_bounds__(256) k_dec_gate_up(MoeArgs a) {
     }
 }
 
+// One block of the shared expert for a given routing: rows bx * rows_per_block .. of the
+// shared gate and up for token t, their LoRA deltas and h_s = silu(g) * u, stored for the
+// down launch (which then reads h_s as in the top-K path).  The LoRA z's of the token are
+// taken in every such block (the x side, which runs in the same launch, cannot hand them
+// over): wave w the ranks 8 w .. 8 w + 7 of the gate's then the up's, each as the x side's
+// LoRA z jobs take it (a lane's inputs lane * 8 + 512 i, then the wave sum).
+__device__ void rt_shared_block(const MoeArgs& a, int t, int bx, f16x2* xs, float* xsum, float (*zs)[MAX_RANK]) {
+    const int H = a.H, SI = a.SI;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lpr = lanes_per_row(H), rpw = 64 / lpr, seg = lane / lpr, sl = lane % lpr;
+    const int n = bx * (4 * rpw) + wave * rpw + seg;
+    const bool ok = n < SI;
+    const int nn = ok ? n : 0;
+    // phase 1: the adapter index (first: the LoRA rows wait for it), x, the rows of the shared
+    // gate and up, and this lane's x chunks for the z's (loaded unconditionally: a stand-in
+    // address without adapters)
+    const int araw_l = *(a.adapter ? a.adapter + t : reinterpret_cast<const int32_t*>(a.x));
+    __builtin_amdgcn_sched_barrier(0);
+    const uint4* xt = reinterpret_cast<const uint4*>(a.x + (long)t * H);
+    StageRegs<4, 2> st;
+    st.load([=](int) { return xt; }, 1, H);
+    RowRegs<4, 2> rg, ru;
+    rg.load(a.shg.p, a.shg.s, a.shg.b, H, nn, lpr, sl, ok);
+    ru.load(a.shu.p, a.shu.s, a.shu.b, H, nn, lpr, sl, ok);
+    constexpr int ZI = 4;   // 512-input chunks per pass: hidden 2048 in one pass
+    uint4 xz[ZI];
+#pragma unroll
+    for (int i = 0; i < ZI; ++i) xz[i] = xt[min(lane * 8 + 512 * i, H - 8) / 8];
+    __builtin_amdgcn_sched_barrier(0);
+    int araw = araw_l;
+    asm volatile("" : "+v"(araw));
+    auto clamp_ad = [&](int na) { const int v = a.adapter ? araw : 0; return v < 0 ? 0 : (v >= na ? na - 1 : v); };
+    const int adg = clamp_ad(a.nag), adu = clamp_ad(a.nau);
+    const int rgk = a.Ag ? a.rg : 0, ruk = a.Au ? a.ru : 0, nz = rgk + ruk;
+    // phase 2: the LoRA rows (they need the adapter index): the B rows of this lane's output
+    // (ranks up to 16, a multiple of 8) and the A rows of this wave's ranks
+    const bool bgf = a.Bg && (a.rg & 7) == 0 && a.rg <= 16;
+    const bool buf = a.Bu && (a.ru & 7) == 0 && a.ru <= 16;
+    uint4 bgv[2], buv[2];
+    {
+        const uint16_t* gb = bgf ? a.Bg + ((long)adg * SI + nn) * a.rg : a.x;
+        const uint16_t* ub = buf ? a.Bu + ((long)adu * SI + nn) * a.ru : a.x;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            bgv[i] = *reinterpret_cast<const uint4*>(gb + (bgf ? min(8 * i, a.rg - 8) : 0));
+            buv[i] = *reinterpret_cast<const uint4*>(ub + (buf ? min(8 * i, a.ru - 8) : 0));
+        }
+    }
+    st.commit(1, H, xs, xsum);
+    for (int j0 = wave * 8; j0 < nz; j0 += 32) {   // passes of 32 ranks (one for ranks <= 16)
+        uint4 av[8][ZI];
+        auto arow = [&](int j) {   // rank row j of the concatenated gate and up ranks (clamped)
+            const int jj = min(j, nz - 1);
+            return jj < rgk ? a.Ag + ((long)adg * a.rg + jj) * H : a.Au + ((long)adu * a.ru + (jj - rgk)) * H;
+        };
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+#pragma unroll
+            for (int i = 0; i < ZI; ++i) av[r][i] = *reinterpret_cast<const uint4*>(arow(j0 + r) + min(lane * 8 + 512 * i, H - 8));
+        float acc[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            acc[r] = 0.0f;
+#pragma unroll
+            for (int i = 0; i < ZI; ++i) {
+                if (lane * 8 + 512 * i < H) {
+                    const f16x2* ah = reinterpret_cast<const f16x2*>(&av[r][i]);
+                    const f16x2* xh = reinterpret_cast<const f16x2*>(&xz[i]);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) acc[r] = __builtin_amdgcn_fdot2(ah[q], xh[q], acc[r], false);
+                }
+            }
+        }
+        for (int c0 = ZI * 512; c0 < H; c0 += ZI * 512) {   // hidden above 2048: further chunks
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+#pragma unroll
+                for (int i = 0; i < ZI; ++i) {
+                    const int k = c0 + lane * 8 + 512 * i;
+                    if (k < H) {
+                        const uint4 av2 = *reinterpret_cast<const uint4*>(arow(j0 + r) + k);
+                        const uint4 xv2 = xt[k / 8];
+                        const f16x2* ah = reinterpret_cast<const f16x2*>(&av2);
+                        const f16x2* xh = reinterpret_cast<const f16x2*>(&xv2);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) acc[r] = __builtin_amdgcn_fdot2(ah[q], xh[q], acc[r], false);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const float v = seg_sum<64>(acc[r]);
+            const int j = j0 + r;
+            if (lane == 0 && j < nz) zs[j < rgk ? 0 : 1][j < rgk ? j : j - rgk] = v;
+        }
+    }
+    __syncthreads();
+    float ag[MT], au[MT];
+    ag[0] = au[0] = 0.0f;
+    rg.dot(H, lpr, sl, xs, xsum, 1, ag);
+    ru.dot(H, lpr, sl, xs, xsum, 1, au);
+    float gv = segment_sum(ag[0], lpr), uv = segment_sum(au[0], lpr);
+    if (sl == 0 && ok) {
+        if (a.Bg) gv = fmaf(a.lsg, bgf ? bdot16(bgv, zs[0], a.rg) : lora_b_dot(a.Bg, adg, SI, n, a.rg, zs[0]), gv);
+        if (a.Bu) uv = fmaf(a.lsu, buf ? bdot16(buv, zs[1], a.ru) : lora_b_dot(a.Bu, adu, SI, n, a.ru, zs[1]), uv);
+        a.hs[(long)t * SI + n] = f2h(silu(gv) * uv);
+    }
+}
+
 // The x side and the routed gate/up of a GIVEN routing in one launch (the caller's selection,
 // e.g. the prerouter head's prediction, which is then the route itself: "Edge0 project
 // review", highlight 1).  Blocks below nx are x-side blocks; every other block is one
@@ -206,12 +316,18 @@ __global__ void __launch_bounds__(256) k_dec_gate_up(MoeArgs a) {
 // entry and issues that expert's gate and up rows at once, so no block waits for another
 // and the router's logits are needed only by the down launch (the routing weights).  The
 // shared expert's h_s, which needs the x side's LoRA z's, is finished by the down launch.
-__global__ void __launch_bounds__(256) k_dec_rt_gate_up(MoeArgs a, int nx) {
+__global__ void __launch_bounds__(256) k_dec_rt_gate_up(MoeArgs a, int nx, int ns) {
     __shared__ __align__(16) f16x2 xs[8192];
     __shared__ float xsum[MT * 128];
-    if ((int)blockIdx.x < nx) {
+    if ((int)blockIdx.x < nx) {   // the router and shared-gate rows of the x side
         QMOE_XSIDE_ARGS();
         xside_block(a, blockIdx.x, xs, xsum);
+        return;
+    }
+    if ((int)blockIdx.x < nx + ns) {   // the shared expert, row block b % nrb of token b / nrb
+        __shared__ float zs[2][MAX_RANK];
+        const int b = blockIdx.x - nx, nrbs = ns / a.T;
+        rt_shared_block(a, b / nrbs, b % nrbs, xs, xsum, zs);
         return;
     }
     QMOE_SGPR_USE4(a.route, a.x, a.eg.p, a.eg.s);
@@ -222,7 +338,7 @@ __global__ void __launch_bounds__(256) k_dec_rt_gate_up(MoeArgs a, int nx) {
     const int lpr = lanes_per_row(H), rpw = 64 / lpr, seg = lane / lpr, sl = lane % lpr;
     const int rows_per_block = 4 * rpw * GU_RPW;
     const int nrb = (I + rows_per_block - 1) / rows_per_block;
-    const int b = blockIdx.x - nx;
+    const int b = blockIdx.x - nx - ns;
     const int pair = b / nrb, bx = b % nrb;
     const int t = pair / a.K;
     const int e = clamp_expert(a.route[pair], a.E);
@@ -258,18 +374,17 @@ constexpr int DN_ROWS = 8;     // output rows per block
 constexpr int DN_ITEMS = 4;    // (matrix, row) items per lane segment per pass
 constexpr int DN_STAGE = 3;    // 16-byte staging loads per thread: (K + 1) * inter / 8 <= 768
 
-// ROUTED: the routing is the caller's (a.route): the experts come from it, the weights are
-// the softmax of the router logits over it, and h_s is finished here from the x side's raw
-// shared gate/up sums and LoRA z's (k_dec_rt_gate_up leaves them), not loaded.
+// ROUTED: the routing is the caller's (a.route): the experts come from it and the weights are
+// the softmax of the router logits over it (h_s comes from the shared blocks of
+// k_dec_rt_gate_up, as from the gate/up launch otherwise).
 template <bool ROUTED>
 __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
     // staged activations: the token's K routed h rows and h_s (as matrix K), pair layout
     __shared__ __align__(16) f16x2 hs_l[(MAX_DEC_K + 1) * 1024];   // inter <= 2048
-    __shared__ __align__(16) uint16_t hsc[ROUTED ? 2048 : 8];      // h_s in input order (ROUTED)
     if constexpr (ROUTED) {
-        QMOE_SGPR_USE4(a.route, a.logits, a.h, a.gs);
-        QMOE_SGPR_USE4(a.us, a.zg, a.zu, a.Bg);
-        QMOE_SGPR_USE4(a.Bu, a.E, a.Ep, a.rbias);
+        QMOE_SGPR_USE4(a.route, a.logits, a.h, a.hs);
+        QMOE_SGPR_USE2(a.E, a.Ep);
+        QMOE_SGPR_USE2(a.rbias, a.w_out);
     } else {
         QMOE_SGPR_USE4(a.idx, a.wts, a.h, a.hs);
     }
@@ -285,7 +400,7 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
     const int t = blockIdx.y;
     const int n0 = blockIdx.x * DN_ROWS;
     const int lpr = lanes_per_row(Kd), rpw = 64 / lpr, seg = lane / lpr, sl = lane % lpr;
-    const int n_staged = ROUTED ? K : K + 1;   // rows staged from memory
+    const int n_staged = K + 1;   // rows staged from memory: the K routed h rows and h_s
     const bool one_pass = n_staged * (Kd / 8) <= 256 * DN_STAGE;
     // expert of routing entry m (< K) of token t
     auto expert_of = [&](int m) {
@@ -336,33 +451,10 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
     const uint16_t* hsrow = a.hs + (long)t * Kd;
     const uint4* hbase4 = reinterpret_cast<const uint4*>(a.h + (long)t * K * Kd);
     const uint4* hsrow4 = reinterpret_cast<const uint4*>(hsrow);
-    // (ROUTED: rows below K only, all in global memory: a pointer that may also point into
-    // LDS would turn every load through it into a flat load, after which each wait is a full
-    // drain of the loads in flight)
-    auto rowp = [=](int m) {
-        if constexpr (ROUTED) return hbase4 + (long)min(m, K - 1) * (Kd / 8);
-        else return m < K ? hbase4 + (long)m * (Kd / 8) : hsrow4;
-    };
+    auto rowp = [=](int m) { return m < K ? hbase4 + (long)m * (Kd / 8) : hsrow4; };
     StageRegs<4, DN_STAGE> st;
     st.load(rowp, n_staged, Kd);   // always (clamped, in bounds): loads under a branch are
                                    // waited for at its merge; unused unless one_pass
-    // ROUTED: the raw shared gate/up sums of this thread's h_s outputs (their LoRA-B rows need
-    // the adapter index and follow below) and the token's LoRA z's (lanes of wave 0; they reach
-    // LDS after the expert rows are issued)
-    constexpr int HSN = ROUTED ? 2 : 1;    // h_s outputs per thread loaded here (the rest later)
-    float gsv[HSN], usv[HSN];
-    __shared__ float zgu[2][MAX_RANK];   // (ROUTED) the token's LoRA z of the shared gate and up
-    float zval = 0.0f;
-    if constexpr (ROUTED) {
-        const int zi = threadIdx.x & 63;
-        zval = (threadIdx.x < 64 ? (zi < 32 ? a.zg : a.zu) : a.zg)[(long)t * MAX_RANK + (zi & 31)];
-#pragma unroll
-        for (int j = 0; j < HSN; ++j) {
-            const int n = min((int)threadIdx.x + j * NT, Kd - 1);
-            gsv[j] = a.gs[(long)t * Kd + n];
-            usv[j] = a.us[(long)t * Kd + n];
-        }
-    }
     // the combine's own inputs (gate logit, residual x) now, not after the dots
     float gate_t;
     uint16_t x_res;
@@ -381,24 +473,6 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
 
     // phase 1b: the LoRA rows (they need the adapter index)
     const int ad = clamp_ad(a.nad);
-    uint4 bgv[HSN][2], buv[HSN][2];
-    const int adg = ROUTED ? clamp_ad(a.nag) : 0;
-    const int adu = ROUTED ? clamp_ad(a.nau) : 0;
-    const bool bgf = ROUTED && a.Bg && (a.rg & 7) == 0 && a.rg <= 16;
-    const bool buf = ROUTED && a.Bu && (a.ru & 7) == 0 && a.ru <= 16;
-    if constexpr (ROUTED) {
-#pragma unroll
-        for (int j = 0; j < HSN; ++j) {
-            const int n = min((int)threadIdx.x + j * NT, Kd - 1);
-            const uint16_t* gb = bgf ? a.Bg + ((long)adg * Kd + n) * a.rg : a.x;
-            const uint16_t* ub = buf ? a.Bu + ((long)adu * Kd + n) * a.ru : a.x;
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                bgv[j][i] = *reinterpret_cast<const uint4*>(gb + (bgf ? min(8 * i, a.rg - 8) : 0));
-                buv[j][i] = *reinterpret_cast<const uint4*>(ub + (buf ? min(8 * i, a.ru - 8) : 0));
-            }
-        }
-    }
     constexpr int ZI = 4;                      // A_down slice: Kd/16 <= 32 inputs per lane
     const int lane16 = threadIdx.x & 15, zrow = threadIdx.x >> 4;
     const int zper = Kd / 16;
@@ -448,43 +522,8 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
         my_b = (a.rbias ? a.rbias : a.logits)[my_e];
     }
     // phase 3: activations to LDS
-    if constexpr (ROUTED) {
-        // h_s = silu(g_s + LoRA_g) * (u_s + LoRA_u), as the shared gate/up blocks of the
-        // top-K path take it (ranks up to 32 from LDS; larger ones from memory)
-        if (threadIdx.x < 64) zgu[threadIdx.x >> 5][threadIdx.x & 31] = zval;
-        __syncthreads();
-        // z from LDS (ranks up to 32) or from memory; each pointer stays in one address space
-        // (a pointer that may be either makes its loads flat, and every wait a full drain)
-        auto finish = [&](const float* zg, const float* zu) {
-#pragma unroll
-            for (int j = 0; j < HSN; ++j) {
-                const int n = threadIdx.x + j * NT;
-                if (n < Kd) {
-                    float gv = gsv[j], uv = usv[j];
-                    if (a.Bg) gv = fmaf(a.lsg, bgf ? bdot16(bgv[j], zg, a.rg) : lora_b_dot(a.Bg, adg, Kd, n, a.rg, zg), gv);
-                    if (a.Bu) uv = fmaf(a.lsu, buf ? bdot16(buv[j], zu, a.ru) : lora_b_dot(a.Bu, adu, Kd, n, a.ru, zu), uv);
-                    hsc[n] = f2h(silu(gv) * uv);
-                }
-            }
-            for (int n = threadIdx.x + HSN * NT; n < Kd; n += NT) {   // inter above 512
-                float gv = a.gs[(long)t * Kd + n], uv = a.us[(long)t * Kd + n];
-                if (a.Bg) gv = fmaf(a.lsg, lora_b_dot(a.Bg, adg, Kd, n, a.rg, zg), gv);
-                if (a.Bu) uv = fmaf(a.lsu, lora_b_dot(a.Bu, adu, Kd, n, a.ru, zu), uv);
-                hsc[n] = f2h(silu(gv) * uv);
-            }
-        };
-        if (a.rg <= 32 && a.ru <= 32) finish(zgu[0], zgu[1]);
-        else finish(a.zg + (long)t * MAX_RANK, a.zu + (long)t * MAX_RANK);
-    }
     if (one_pass) st.commit(n_staged, Kd, hs_l, hsum);
     else stage_rows<4, 4>(rowp, n_staged, Kd, hs_l, hsum);
-    if constexpr (ROUTED) {
-        __syncthreads();
-        // h_s as staged row K (Kd / 8 <= NT units: one per thread)
-        const int u = threadIdx.x;
-        const uint4 raw = reinterpret_cast<const uint4*>(hsc)[min(u, Kd / 8 - 1)];
-        commit_unit<4>(raw, K * (Kd / 8) + u, u < Kd / 8, hs_l, hsum);
-    }
     __syncthreads();
     // z_down = A_down[ad] . h_s[t], from the staged h_s in the pair order of A's registers
     if (zfast) {
@@ -505,8 +544,7 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
         acc = seg_sum<16>(acc);
         if (lane16 == 0 && zrow < a.rd) zd[zrow] = acc;
     } else if (a.Ad) {
-        if constexpr (ROUTED) lora_rows16(a.Ad + (long)ad * a.rd * Kd, a.rd, hsc, Kd, zd);
-        else lora_rows16(a.Ad + (long)ad * a.rd * Kd, a.rd, hsrow, Kd, zd);
+        lora_rows16(a.Ad + (long)ad * a.rd * Kd, a.rd, hsrow, Kd, zd);
     }
     for (int base = 0; base < n_items; base += slots * DN_ITEMS) {
         if (base > 0) load_items(base);
@@ -600,7 +638,12 @@ hipError_t launch_moe_decode(const MoeArgs& a, int stage, hipStream_t s) {
     if (a.route) {   // the caller's routing: two launches
         const int rpb = 4 * (64 / lanes_per_row(a.H)) * GU_RPW;
         const int nrb = (a.I + rpb - 1) / rpb;
-        k_dec_rt_gate_up<<<(unsigned)(nx + nrb * a.T * a.K), 256, 0, s>>>(a, nx);
+        // x side: the router and shared-gate rows only (the shared expert's gate/up and LoRA
+        // z's run in the shared blocks, which finish h_s)
+        const XsideGrid g = xside_grid(a.T, a.H, a.E, a.SI, 0);
+        const int nxr = g.nb_router + g.nb_gate;
+        const int ns = a.T * ((a.SI + rpb - 1) / rpb);
+        k_dec_rt_gate_up<<<(unsigned)(nxr + ns + nrb * a.T * a.K), 256, 0, s>>>(a, nxr, ns);
         dim3 grid((unsigned)((a.H + DN_ROWS - 1) / DN_ROWS), (unsigned)a.T);
         k_dec_down<true><<<grid, 256, 0, s>>>(a);
         return hipGetLastError();
