@@ -248,6 +248,14 @@ __device__ void rt_shared_block(const MoeArgs& a, int t, int bx, f16x2* xs, floa
         }
     }
     st.commit(1, H, xs, xsum);
+    __syncthreads();
+    // the rows' dot products first: the A rows (one round trip later than the weights) arrive
+    // meanwhile
+    float ag[MT], au[MT];
+    ag[0] = au[0] = 0.0f;
+    rg.dot(H, lpr, sl, xs, xsum, 1, ag);
+    ru.dot(H, lpr, sl, xs, xsum, 1, au);
+    float gv = segment_sum(ag[0], lpr), uv = segment_sum(au[0], lpr);
     for (int j0 = wave * 8; j0 < nz; j0 += 32) {   // passes of 32 ranks (one for ranks <= 16)
         uint4 av[8][ZI];
         auto arow = [&](int j) {   // rank row j of the concatenated gate and up ranks (clamped)
@@ -297,11 +305,6 @@ __device__ void rt_shared_block(const MoeArgs& a, int t, int bx, f16x2* xs, floa
         }
     }
     __syncthreads();
-    float ag[MT], au[MT];
-    ag[0] = au[0] = 0.0f;
-    rg.dot(H, lpr, sl, xs, xsum, 1, ag);
-    ru.dot(H, lpr, sl, xs, xsum, 1, au);
-    float gv = segment_sum(ag[0], lpr), uv = segment_sum(au[0], lpr);
     if (sl == 0 && ok) {
         if (a.Bg) gv = fmaf(a.lsg, bgf ? bdot16(bgv, zs[0], a.rg) : lora_b_dot(a.Bg, adg, SI, n, a.rg, zs[0]), gv);
         if (a.Bu) uv = fmaf(a.lsu, buf ? bdot16(buv, zs[1], a.ru) : lora_b_dot(a.Bu, adu, SI, n, a.ru, zs[1]), uv);
