@@ -50,6 +50,7 @@ constexpr int PF_XS_K = 512;          // inputs per block of the split-K x-side 
 constexpr int PF_XS_K_BIG = 2048;     // the same from PF_XS_BIG_T tokens up (enough blocks unsplit)
 constexpr int PF_XS_BIG_T = 2048;
 constexpr int PF_MANY_T = 1024;       // from this many tokens the per-token kernels favour occupancy
+constexpr int PF_IB_TK = 256;         // up to this many pairs the GEMM blocks form their work items
 
 struct PfGemm {
     const uint32_t* p[2];
@@ -60,6 +61,8 @@ struct PfGemm {
     int T;                         // dense: token count
     int act_div;                   // grouped: activation row = pair / act_div (1: pair itself)
     const int32_t *wrec, *wpairs;  // grouped: work items (expert, tokens) and their pair ids
+    const int32_t* ridx;           // grouped, few pairs: the pairs' experts; items formed in the block
+    int rtk, risz, rE;             // ... from rtk pairs, isz pairs per item, rE experts
     int nrb, items;                // row blocks, grid items (a multiple of 8)
     int bf;                        // grouped fp16-weight GEMMs: scales and biases stored as bf16
     float* out0; float* out1;      // fp32 outputs [row][ostride]
@@ -152,6 +155,63 @@ __device__ __forceinline__ void pf_block(int id, int nrb, int& rb, int& item) {
     item = (q / nrb) * 8 + xcd;
 }
 
+// Inclusive prefix sum over the wave.
+__device__ __forceinline__ int wave_scan(int v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(v, off);
+        if (lane >= off) v += t;
+    }
+    return v;
+}
+
+// Work item `item` of the expert sort formed inside the block from the pairs' experts, for few
+// pairs (rtk <= 256, rE <= 256, 256 threads) instead of read from the sort's records: the same
+// items (experts ascending, an expert's pairs in pair order, chunks of risz) and so the same
+// results, without the sort's launch.  Thread tid holds pair tid; the experts' pair counts
+// are taken with LDS atomics, their item counts' prefix by a block scan, and the item's pairs
+// are the pairs of its expert of rank j risz .. j risz + risz - 1 (ballots).  `lds`: 272 ints.
+// Returns false past the last item; else the expert, the pair count and, after the caller's
+// barrier, the pair ids in orow[0 .. ntok) (the block's TOKB slots, TOKB = risz by the host's
+// choice of kernel; bounded by it regardless).  Every thread of the block calls it.
+template <int TOKB>
+__device__ __forceinline__ bool item_in_block(const PfGemm& a, int item, int* lds, int* orow, int& e, int& ntok) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int* cnt = lds;          // [256] pairs per expert
+    int* misc = lds + 256;   // [0, 4): waves' item sums; [4, 7): the item's expert, chunk, count; [8, 12): ballots
+    const int ex = tid < a.rtk ? a.ridx[tid] : -1;
+    cnt[tid] = 0;
+    if (tid == 0) misc[4] = -1;
+    __syncthreads();
+    if (ex >= 0) atomicAdd(&cnt[ex], 1);
+    __syncthreads();
+    const int c = tid < a.rE ? cnt[tid] : 0;
+    const int nw = (c + a.risz - 1) / a.risz;
+    const int inc = wave_scan(nw);
+    if (lane == 63) misc[wave] = inc;
+    __syncthreads();
+    int wex = inc - nw;
+    for (int w = 0; w < wave; ++w) wex += misc[w];
+    if (item >= wex && item < wex + nw) {
+        misc[4] = tid;
+        misc[5] = item - wex;
+        misc[6] = c;
+    }
+    __syncthreads();
+    e = misc[4];
+    if (e < 0) return false;
+    const int j = misc[5];
+    ntok = min(min(a.risz, TOKB), misc[6] - j * a.risz);
+    const uint64_t m = __ballot(ex == e);
+    if (lane == 0) misc[8 + wave] = (int)__popcll(m);
+    __syncthreads();
+    int rank = (int)__popcll(m & ((1ull << lane) - 1)) - j * a.risz;
+    for (int w = 0; w < wave; ++w) rank += misc[8 + w];
+    if (ex == e && rank >= 0 && rank < ntok) orow[rank] = tid;
+    return true;
+}
+
 // The packed words, scales and biases of one 128-input step for this lane's feature row.
 template <int NMAT, int BITS>
 struct PfSlot {
@@ -172,6 +232,13 @@ __device__ __forceinline__ bool pf_setup(const PfGemm& a, int item, PfSmem<NTS, 
     split = 0;
     if constexpr (GROUPED) {
         static_assert(!GROUPED || TOKB <= PF_ITEM, "one work item per block");
+        if (a.ridx) {   // (the tile is free until the GEMM stages its first step)
+            if (!item_in_block<TOKB>(a, item, reinterpret_cast<int*>(sm.tile), sm.orow, e, ntok)) return false;
+            __syncthreads();
+            if (threadIdx.x < TOKB) sm.arow[threadIdx.x] = sm.orow[min((int)threadIdx.x, ntok - 1)] / a.act_div;
+            __syncthreads();
+            return true;
+        }
         // the record and the pair ids in one round trip (both indexed by the item alone)
         const int4 rec = reinterpret_cast<const int4*>(a.wrec)[item];
         const int pair = threadIdx.x < TOKB ? a.wpairs[(long)item * PF_ITEM + threadIdx.x] : 0;
@@ -590,12 +657,16 @@ __device__ __forceinline__ void pf_res_block(const PfGemm& a, int rbg, int item,
         constexpr int TOKB = 16 * NT;
         e = 0; split = 0;
         if constexpr (FL & F_GROUPED) {
-            const int4 rec = reinterpret_cast<const int4*>(a.wrec)[item];
-            const int pair = threadIdx.x < TOKB ? a.wpairs[(long)item * PF_ITEM + threadIdx.x] : 0;
-            if (rec.y == 0) return;
-            e = rec.x;
-            ntok = rec.y;
-            if (threadIdx.x < TOKB) sm.orow[threadIdx.x] = pair;
+            if (a.ridx) {
+                if (!item_in_block<TOKB>(a, item, reinterpret_cast<int*>(sm.tile), sm.orow, e, ntok)) return;
+            } else {
+                const int4 rec = reinterpret_cast<const int4*>(a.wrec)[item];
+                const int pair = threadIdx.x < TOKB ? a.wpairs[(long)item * PF_ITEM + threadIdx.x] : 0;
+                if (rec.y == 0) return;
+                e = rec.x;
+                ntok = rec.y;
+                if (threadIdx.x < TOKB) sm.orow[threadIdx.x] = pair;
+            }
             __syncthreads();
             if (threadIdx.x < TOKB) sm.arow[threadIdx.x] = sm.orow[min((int)threadIdx.x, ntok - 1)] / a.act_div;
         } else {
@@ -1149,17 +1220,6 @@ void launch_token(const MoeArgs& a, int ksplit, int kp, size_t tsm, hipStream_t 
     }
 }
 
-// Inclusive prefix sum over the wave.
-__device__ __forceinline__ int wave_scan(int v) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int t = __shfl_up(v, off);
-        if (lane >= off) v += t;
-    }
-    return v;
-}
-
 // Exclusive prefix sum over a block of 1024 threads; the total goes to *total.
 __device__ int block_scan_excl(int v, int* wsum, int* total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1685,11 +1745,18 @@ PfGemm gemm_args(const QW& w0, const QW* w1, int N, int K, const uint16_t* act, 
     return p;
 }
 
+// ib_isz > 0: items formed in the block (item_in_block) with that many pairs per item.
 PfGemm grouped(const MoeArgs& a, const QW& w0, const QW* w1, int N, int K, const uint16_t* act,
-               int act_div, int items) {
+               int act_div, int items, int ib_isz) {
     PfGemm p = gemm_args(w0, w1, N, K, act, N, items);
     p.act_div = act_div;
     p.wrec = a.wrec; p.wpairs = a.wpairs;
+    if (ib_isz > 0) {
+        p.ridx = a.idx;
+        p.rtk = a.T * a.K;
+        p.risz = ib_isz;
+        p.rE = a.E;
+    }
     return p;
 }
 
@@ -1727,6 +1794,8 @@ hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s) {
     const int tgroups = (a.T + PF_TOK - 1) / PF_TOK;
     const int ksplit = prefill_ksplit(a.H, a.T);
     const bool all = stage == QMOE_STAGE_ALL;
+    // few pairs: no sort launch, each grouped GEMM block forms its work item (item_in_block)
+    const int ib = (long)a.T * a.K <= PF_IB_TK && a.E <= 256 && isz <= 64 ? isz : 0;
     if (all || stage == QMOE_STAGE_ROUTE) {
         // x side: split-K blocks of PF_XS_K inputs write partial sums, k_pf_token adds them
         XsideArgs xa{};
@@ -1755,7 +1824,9 @@ hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s) {
         if (a.E <= 256) launch_token<4>(a, ksplit, kp, tsm, s);
         else launch_token<16>(a, ksplit, kp, tsm, s);
         const int TK = a.T * a.K;
-        if (TK <= 2048) {
+        if (ib > 0) {
+            // (few pairs: the GEMM blocks form their items themselves)
+        } else if (TK <= 2048) {
             k_pf_sort<<<1, 1024, 0, s>>>(a, items, isz);
         } else {
             const int cpb = sort_chunks_per_block(TK), nseg = (TK + cpb * 1024 - 1) / (cpb * 1024);
@@ -1767,7 +1838,7 @@ hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s) {
         // routed experts in groups of 32 and/or with bf16 parameters: the staged
         // fp16-weight GEMM for gate/up and down, the shared expert's dense down apart
         if (all || stage == QMOE_STAGE_GATE_UP) {
-            PfGemm p = grouped(a, a.eg, &a.eu, a.I, a.H, a.x, a.K, items);
+            PfGemm p = grouped(a, a.eg, &a.eu, a.I, a.H, a.x, a.K, items, ib);
             p.hout = a.h;
             p.bf = a.ebf;
             const hipError_t e = a.egroup == 32 ? pf_gemm_staged<2, F_GROUPED | F_HOUT | F_G32>(p, isz / 16, s)
@@ -1775,7 +1846,7 @@ hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s) {
             if (e != hipSuccess) return e;
         }
         if (all || stage == QMOE_STAGE_DOWN) {
-            PfGemm p = grouped(a, a.ed, nullptr, a.H, a.I, a.h, 1, items);
+            PfGemm p = grouped(a, a.ed, nullptr, a.H, a.I, a.h, 1, items, ib);
             p.hout = a.o;
             p.bf = a.ebf;
             const hipError_t e = a.egroup == 32 ? pf_gemm_staged<1, F_GROUPED | F_O16 | F_G32>(p, isz / 16, s)
@@ -1787,7 +1858,7 @@ hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s) {
             pf_gemm<1, 4, 2, 0>(q, s);
         }
     } else if (all || stage == QMOE_STAGE_GATE_UP) {
-        PfGemm p = grouped(a, a.eg, &a.eu, a.I, a.H, a.x, a.K, items);
+        PfGemm p = grouped(a, a.eg, &a.eu, a.I, a.H, a.x, a.K, items, ib);
         p.hout = a.h;
         if (isz == PB_TOK) {
             p.nrb = (a.I + PB_ROWS - 1) / PB_ROWS;
@@ -1802,7 +1873,7 @@ hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s) {
     } else if ((all || stage == QMOE_STAGE_DOWN) && isz == PB_TOK) {
         // large items: the grouped down on the large-item GEMM, then the shared expert's dense
         // down over 64-token groups (resident activations at inner size 512)
-        PfGemm p = grouped(a, a.ed, nullptr, a.H, a.I, a.h, 1, items);
+        PfGemm p = grouped(a, a.ed, nullptr, a.H, a.I, a.h, 1, items, ib);
         p.hout = a.o;
         p.nrb = (a.H + PB_ROWS - 1) / PB_ROWS;
         const hipError_t e = launch_big<1, F_O16>(p, s);
@@ -1820,7 +1891,7 @@ hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s) {
             pf_gemm<1, 4, 2, 0>(q, s);
         }
     } else if (all || stage == QMOE_STAGE_DOWN) {
-        PfGemm p = grouped(a, a.ed, nullptr, a.H, a.I, a.h, 1, items);
+        PfGemm p = grouped(a, a.ed, nullptr, a.H, a.I, a.h, 1, items, ib);
         p.hout = a.o;   // fp16 down outputs of the (token, k) pairs
         PfGemm q = gemm_args(a.shd, nullptr, a.H, a.SI, a.hs, a.H, (a.T + 31) / 32);   // 32-token groups
         q.T = a.T;
