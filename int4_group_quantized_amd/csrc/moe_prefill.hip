@@ -81,7 +81,7 @@ constexpr int F_HOUT = 2;      // fp16 silu(out0) * out1 (else fp32 outputs)
 constexpr int F_O16 = 8;       // fp16 outputs to hout, single matrix (the experts' down outputs)
 constexpr int F_EXTRA = 4;     // one extra feature row from a second matrix (single matrix)
 constexpr int F_G32 = 16;      // groups of 32 inputs (four per step; grouped fp16-weight GEMMs)
-constexpr int PF_RES_RBG = 4;  // row blocks per block of the resident-activation GEMM
+constexpr int PF_RES_RBG = 2;  // row blocks per block of the resident-activation GEMM
 
 // LDS of one GEMM block: the activation tile (double buffer: step ks computes from ks % 2
 // while step ks + 1's tile is staged into the other), and with a compile-time step count NS

@@ -120,6 +120,26 @@ def test_prefill_wide_inter_many_items(q):
     check_layer(Lc, x, ad, y, idx, w)
 
 
+# Few pairs (at most 256, at most 256 experts): the grouped GEMM blocks form their work items
+# themselves.  37 experts (grid items past the last item), 256 pairs (the limit) over 64
+# experts, and experts split over two 64-pair items.
+@pytest.mark.parametrize("T,S,seed", [
+    (16, Shape(hidden=1024, inter=512, shared_inter=512, n_experts=37, top_k=4, rank=16, n_adapters=2), 20),
+    (32, Shape(hidden=512, inter=512, shared_inter=512, n_experts=64, top_k=8, rank=8, n_adapters=2), 21),
+    (128, Shape(hidden=512, inter=512, shared_inter=512, n_experts=4, top_k=2, rank=8, n_adapters=2), 20),
+], ids=["37-experts", "256-pairs", "two-items"])
+def test_prefill_items_formed_in_block(q, T, S, seed):
+    print(f"items in block T={T} E={S.n_experts} K={S.top_k}", flush=True)
+    assert T * S.top_k <= 256
+    Lc = build_layer(synth.Workload.TEST, seed, S)
+    x = synth.activations(T, S.hidden, synth.Workload.TEST, seed)
+    ad = (np.arange(T) % 2).astype(np.int32)
+    y, idx, w = run_device(q, Lc, S, x, ad)
+    if T == 128:
+        assert np.bincount(idx.ravel(), minlength=S.n_experts).max() > 64
+    check_layer(Lc, x, ad, y, idx, w)
+
+
 @pytest.mark.parametrize("T", [64, 100, 200])
 def test_prefill_inter_1024(q, T):
     """Routed and shared inner size 1024: 16-pair work items at 64 and 100 tokens (the down
