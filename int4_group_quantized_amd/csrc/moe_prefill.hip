@@ -82,6 +82,8 @@ constexpr int F_O16 = 8;       // fp16 outputs to hout, single matrix (the exper
 constexpr int F_EXTRA = 4;     // one extra feature row from a second matrix (single matrix)
 constexpr int F_G32 = 16;      // groups of 32 inputs (four per step; grouped fp16-weight GEMMs)
 constexpr int PF_RES_RBG = 2;  // row blocks per block of the resident-activation GEMM
+constexpr int PF_RES_RBG64 = 4;   // ... for the dense shared down over 64-token groups (its 64 KB
+                                  // activation staging per block favours fewer, longer blocks)
 
 // LDS of one GEMM block: the activation tile (double buffer: step ks computes from ks % 2
 // while step ks + 1's tile is staged into the other), and with a compile-time step count NS
@@ -1882,8 +1884,8 @@ hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s) {
             PfGemm q = gemm_args(a.shd, nullptr, a.H, a.SI, a.hs, a.H, (a.T + 63) / 64);
             q.T = a.T;
             q.out0 = a.os;
-            q.nrb = (a.H + PF_ROWS * PF_RES_RBG - 1) / (PF_ROWS * PF_RES_RBG);
-            k_pf_down_res<4, 4, PF_RES_RBG><<<(unsigned)(q.nrb * q.items), 256, 0, s>>>(q, q, 0);
+            q.nrb = (a.H + PF_ROWS * PF_RES_RBG64 - 1) / (PF_ROWS * PF_RES_RBG64);
+            k_pf_down_res<4, 4, PF_RES_RBG64><<<(unsigned)(q.nrb * q.items), 256, 0, s>>>(q, q, 0);
         } else {
             PfGemm q = gemm_args(a.shd, nullptr, a.H, a.SI, a.hs, a.H, (a.T + 31) / 32);
             q.T = a.T;
