@@ -173,10 +173,12 @@ __device__ __forceinline__ int wave_scan(int v) {
 // items (experts ascending, an expert's pairs in pair order, chunks of risz) and so the same
 // results, without the sort's launch.  Thread tid holds pair tid; the experts' pair counts
 // are taken with LDS atomics, their item counts' prefix by a block scan, and the item's pairs
-// are the pairs of its expert of rank j risz .. j risz + risz - 1 (ballots).  `lds`: 272 ints.
+// are the pairs of its expert of rank j risz .. j risz + risz - 1 (ballots).  `lds`: IIB_LDS_INTS ints.
 // Returns false past the last item; else the expert, the pair count and, after the caller's
 // barrier, the pair ids in orow[0 .. ntok) (the block's TOKB slots, TOKB = risz by the host's
-// choice of kernel; bounded by it regardless).  Every thread of the block calls it.
+// choice of kernel; bounded by it regardless).  Every thread of the block calls it; the
+// block has 256 threads (one per expert and per pair).
+constexpr int IIB_LDS_INTS = 272;
 template <int TOKB>
 __device__ __forceinline__ bool item_in_block(const PfGemm& a, int item, int* lds, int* orow, int& e, int& ntok) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -235,6 +237,7 @@ __device__ __forceinline__ bool pf_setup(const PfGemm& a, int item, PfSmem<NTS, 
     if constexpr (GROUPED) {
         static_assert(!GROUPED || TOKB <= PF_ITEM, "one work item per block");
         if (a.ridx) {   // (the tile is free until the GEMM stages its first step)
+            static_assert(sizeof(sm.tile) >= IIB_LDS_INTS * sizeof(int), "LDS for item_in_block");
             if (!item_in_block<TOKB>(a, item, reinterpret_cast<int*>(sm.tile), sm.orow, e, ntok)) return false;
             __syncthreads();
             if (threadIdx.x < TOKB) sm.arow[threadIdx.x] = sm.orow[min((int)threadIdx.x, ntok - 1)] / a.act_div;
@@ -660,6 +663,7 @@ __device__ __forceinline__ void pf_res_block(const PfGemm& a, int rbg, int item,
         e = 0; split = 0;
         if constexpr (FL & F_GROUPED) {
             if (a.ridx) {
+                static_assert(sizeof(sm.tile) >= IIB_LDS_INTS * sizeof(int), "LDS for item_in_block");
                 if (!item_in_block<TOKB>(a, item, reinterpret_cast<int*>(sm.tile), sm.orow, e, ntok)) return;
             } else {
                 const int4 rec = reinterpret_cast<const int4*>(a.wrec)[item];
