@@ -202,5 +202,8 @@ int prefill_max_items(int E, int T, int K, int H, int I, bool std_experts = true
 int prefill_item_size(int E, int T, int K, int H, int I, bool std_experts = true);
 int prefill_ksplit(int hidden, int T);
 hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s);
+// moe_down_fs.hip: the down projections and the combine in one launch (few routed pairs)
+bool down_fs_fits(const MoeArgs& a);
+hipError_t launch_down_fs(const MoeArgs& a, hipStream_t s);
 
 }  // namespace qmoe

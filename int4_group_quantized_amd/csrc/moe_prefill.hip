@@ -1802,6 +1802,7 @@ hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s) {
     const bool all = stage == QMOE_STAGE_ALL;
     // few pairs: no sort launch, each grouped GEMM block forms its work item (item_in_block)
     const int ib = (long)a.T * a.K <= PF_IB_TK && a.E <= 256 && isz <= 64 ? isz : 0;
+    const bool fused_down = ib > 0 && std_experts && down_fs_fits(a);
     if (all || stage == QMOE_STAGE_ROUTE) {
         // x side: split-K blocks of PF_XS_K inputs write partial sums, k_pf_token adds them
         XsideArgs xa{};
@@ -1896,6 +1897,10 @@ hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s) {
             q.out0 = a.os;
             pf_gemm<1, 4, 2, 0>(q, s);
         }
+    } else if ((all || stage == QMOE_STAGE_DOWN) && fused_down) {
+        // few pairs: every down projection and the combine in one feature-sliced launch
+        const hipError_t e = launch_down_fs(a, s);
+        if (e != hipSuccess) return e;
     } else if (all || stage == QMOE_STAGE_DOWN) {
         PfGemm p = grouped(a, a.ed, nullptr, a.H, a.I, a.h, 1, items, ib);
         p.hout = a.o;   // fp16 down outputs of the (token, k) pairs
@@ -1939,7 +1944,7 @@ hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s) {
             pf_gemm<1, 4, 2, 0>(q, s);
         }
     }
-    if (all || stage == QMOE_STAGE_DOWN) {
+    if ((all || stage == QMOE_STAGE_DOWN) && !fused_down) {
         // blocks of 16 (few tokens) or 8 (many) tokens x 128 features
         if (a.T < PF_MANY_T) {
             k_pf_combine<<<(unsigned)((a.T + 15) / 16 * (a.H / 128)), 256, 0, s>>>(a);
