@@ -12,6 +12,8 @@ constexpr int MAX_RANK = 64;
 constexpr int MAX_K = 32;
 constexpr int MAX_DEC_T = 32;  // the decode path serves up to this many tokens per call
 constexpr int MAX_DEC_K = 8;   // ... and up to this many experts per token
+constexpr int DEC_ZP_BLOCKS = 32;   // decode: shared-expert row blocks of 64 per token (inter <= 2048)
+constexpr int DEC_ZP_RANK = 16;     // ... each holding its share of z_down for LoRA ranks up to 16
 constexpr int PF_ITEM = 128;   // most pairs per work item of the token-sorted GEMMs (slots per item)
 constexpr int PF_SORT_MAXSEG = 64;   // most blocks (segments of pairs) of the multi-block sort
 

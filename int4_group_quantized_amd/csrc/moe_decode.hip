@@ -14,12 +14,14 @@
 //                wave reads token t's logits and takes the selection up to round k (the
 //                same deterministic selection in every block), so it issues the gate and up
 //                rows of expert idx[t][k] before x is staged and the block synchronises;
-//                then h = silu(g) * u is stored (fp16).  Shared blocks add the LoRA
-//                up-projections and store h_s.
-//   D3 down    : one block per (row block, token).  It reads the token's published routing,
-//                stages the token's K expert activations h and h_s, computes the shared
-//                expert's LoRA z_down, streams the K + 1 down matrices' rows, and combines
-//                y = sum_k w_k o_k + sigmoid(gate) (o_s + LoRA) (+ residual) in-block.
+//                then h = silu(g) * u is stored (fp16).  Shared blocks (one wave per 64
+//                rows of a token) add the LoRA up-projections, store h_s and, for LoRA ranks
+//                up to 16, their rows' share of the down LoRA's z_down = A_down h_s.
+//   D3 down    : one block per (row block, token).  It reads the token's published routing
+//                and sums the z_down shares (or takes A_down h_s itself), stages the token's
+//                K expert activations h and h_s, streams the K + 1 down matrices' rows, and
+//                combines y = sum_k w_k o_k + sigmoid(gate) (o_s + LoRA) (+ residual)
+//                in-block.
 #include <algorithm>
 
 #include "gemv_core.hpp"
@@ -124,6 +126,66 @@ int xside_blocks(const MoeArgs& a) {
 
 constexpr int GU_RPW = 1;  // gate/up row pairs per wave
 
+// 64 rows n = 64 rb + lane of token t's shared expert after the x side, one wave:
+//   h_s[n] = fp16( silu(gs + (alpha/r) B_g z_g) * (us + (alpha/r) B_u z_u) )   (to memory)
+// and, for LoRA ranks up to DEC_ZP_RANK, these rows' share of the down LoRA's z_d:
+//   zp[t][rb][r] = sum over the 64 rows of A_d[a_t][r][n] h_s[n]   (fixed order)
+// which the down launch adds over rb in order, instead of every down block taking A_d . h_s
+// from the whole of A_d.  Every load is issued before any arithmetic (the A_d column loads
+// are unconditional, from a stand-in row without them).  `lds`: 64 x 16 floats.
+__device__ __forceinline__ void dec_shared_rows(const MoeArgs& a, int t, int rb, float* lds) {
+    const int lane = threadIdx.x & 63, SI = a.SI, n = rb * 64 + lane;
+    const int ad = adapter_of(a.adapter, t, a.nad);
+    const bool zpart = a.Ad && a.rd <= DEC_ZP_RANK;
+    float gv = a.gs[(long)t * SI + n];
+    float uv = a.us[(long)t * SI + n];
+    uint16_t ac[DEC_ZP_RANK];
+#pragma unroll
+    for (int r = 0; r < DEC_ZP_RANK; ++r)
+        ac[r] = zpart ? a.Ad[((long)ad * a.rd + min(r, a.rd - 1)) * SI + n] : a.x[(long)t * a.H + lane];
+    // the B rows of both projections (ranks up to 16 in registers, loaded unconditionally from
+    // a stand-in row without them: a load under a branch is waited for at the branch's end,
+    // which would put the second projection's rows a round trip behind the first's)
+    const int ag = adapter_of(a.adapter, t, a.nag), au = adapter_of(a.adapter, t, a.nau);
+    const bool gfast = a.Bg && (a.rg & 7) == 0 && a.rg <= 16, ufast = a.Bu && (a.ru & 7) == 0 && a.ru <= 16;
+    const uint4* xst = reinterpret_cast<const uint4*>(a.x + (long)t * a.H);
+    const uint4* bgp = gfast ? reinterpret_cast<const uint4*>(a.Bg + ((long)ag * SI + n) * a.rg) : xst;
+    const uint4* bup = ufast ? reinterpret_cast<const uint4*>(a.Bu + ((long)au * SI + n) * a.ru) : xst;
+    uint4 bg[2], bu[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        bg[i] = bgp[gfast ? min(i, a.rg / 8 - 1) : 0];
+        bu[i] = bup[ufast ? min(i, a.ru / 8 - 1) : 0];
+    }
+    const float* zg = a.zg + t * MAX_RANK;
+    const float* zu = a.zu + t * MAX_RANK;
+    if (gfast) gv = fmaf(a.lsg, bdot16(bg, zg, a.rg), gv);
+    else if (a.Bg) gv = fmaf(a.lsg, lora_b_dot(a.Bg, ag, SI, n, a.rg, zg), gv);
+    if (ufast) uv = fmaf(a.lsu, bdot16(bu, zu, a.ru), uv);
+    else if (a.Bu) uv = fmaf(a.lsu, lora_b_dot(a.Bu, au, SI, n, a.ru, zu), uv);
+    const uint16_t hv = f2h(silu(gv) * uv);
+    a.hs[(long)t * SI + n] = hv;
+    if (zpart) {
+        const float hf = h2f(hv);
+        // the 16 sums over the wave's lanes through LDS (one wave: LDS accesses complete in
+        // order, so only the compiler needs a fence): lane l adds rank l % 16 over lanes
+        // 16 (l / 16) .. + 15, then the four partial sums meet in a fixed order
+        float4* pl = reinterpret_cast<float4*>(lds + lane * DEC_ZP_RANK);
+#pragma unroll
+        for (int i = 0; i < DEC_ZP_RANK / 4; ++i)
+            pl[i] = make_float4(h2f(ac[4 * i]) * hf, h2f(ac[4 * i + 1]) * hf, h2f(ac[4 * i + 2]) * hf,
+                                h2f(ac[4 * i + 3]) * hf);
+        asm volatile("" ::: "memory");
+        const int r = lane & 15, g = lane >> 4;
+        float zs = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) zs += lds[(16 * g + i) * DEC_ZP_RANK + r];
+        zs += __shfl_xor(zs, 16, 64);
+        zs += __shfl_xor(zs, 32, 64);
+        if (lane < DEC_ZP_RANK && lane < a.rd) a.zd[((long)t * DEC_ZP_BLOCKS + rb) * DEC_ZP_RANK + lane] = zs;
+    }
+}
+
 template <int PER>
 __global__ void __launch_bounds__(256) k_dec_gate_up(MoeArgs a) {
     __shared__ __align__(16) f16x2 xs[2048];   // one token, hidden <= 4096
@@ -140,17 +202,10 @@ __global__ void __launch_bounds__(256) k_dec_gate_up(MoeArgs a) {
     const int lpr = lanes_per_row(H), rpw = 64 / lpr, seg = lane / lpr, sl = lane % lpr;
     const int rows_per_block = 4 * rpw * GU_RPW;
 
-    if (pair == TK) {  // shared expert: LoRA up-projections, silu(g) * u
-        const int n0 = blockIdx.x * rows_per_block;
-        for (int it = threadIdx.x; it < rows_per_block * a.T; it += NT) {
-            const int n = n0 + it % rows_per_block, t = it / rows_per_block;
-            if (n >= a.SI) continue;
-            float gv = a.gs[(long)t * a.SI + n];
-            float uv = a.us[(long)t * a.SI + n];
-            if (a.Bg) gv = fmaf(a.lsg, lora_b_dot(a.Bg, adapter_of(a.adapter, t, a.nag), a.SI, n, a.rg, a.zg + t * MAX_RANK), gv);
-            if (a.Bu) uv = fmaf(a.lsu, lora_b_dot(a.Bu, adapter_of(a.adapter, t, a.nau), a.SI, n, a.ru, a.zu + t * MAX_RANK), uv);
-            a.hs[(long)t * a.SI + n] = f2h(silu(gv) * uv);
-        }
+    if (pair == TK) {  // shared expert: wave 0 of block b finishes rows 64 (b % nbs) .. of token b / nbs
+        const int nbs = a.SI / 64;
+        if (blockIdx.x < (unsigned)(a.T * nbs) && wave == 0)
+            dec_shared_rows(a, blockIdx.x / nbs, blockIdx.x % nbs, reinterpret_cast<float*>(xs));
         return;
     }
     if (blockIdx.x * rows_per_block >= I) return;
@@ -380,7 +435,9 @@ constexpr int DN_STAGE = 3;    // 16-byte staging loads per thread: (K + 1) * in
 // ROUTED: the routing is the caller's (a.route): the experts come from it and the weights are
 // the softmax of the router logits over it (h_s comes from the shared blocks of
 // k_dec_rt_gate_up, as from the gate/up launch otherwise).
-template <bool ROUTED>
+// ZP: the down LoRA's z_d is the sum of the gate/up launch's per-64-row shares (top-K path,
+// rank <= DEC_ZP_RANK); otherwise every block takes A_d . h_s itself.
+template <bool ROUTED, bool ZP>
 __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
     // staged activations: the token's K routed h rows and h_s (as matrix K), pair layout
     __shared__ __align__(16) f16x2 hs_l[(MAX_DEC_K + 1) * 1024];   // inter <= 2048
@@ -458,6 +515,17 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
     StageRegs<4, DN_STAGE> st;
     st.load(rowp, n_staged, Kd);   // always (clamped, in bounds): loads under a branch are
                                    // waited for at its merge; unused unless one_pass
+    // (ZP) z_d shares: thread i < 16 nbs holds share i / 16 of rank row i % 16
+    __shared__ float zpl[DEC_ZP_BLOCKS * DEC_ZP_RANK];
+    const int nbs = Kd / 64;
+    float zpv[2];
+    if constexpr (ZP) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int i = (int)threadIdx.x + NT * j;
+            zpv[j] = a.zd[((long)t * DEC_ZP_BLOCKS + min(i / DEC_ZP_RANK, nbs - 1)) * DEC_ZP_RANK + i % DEC_ZP_RANK];
+        }
+    }
     // the combine's own inputs (gate logit, residual x) now, not after the dots
     float gate_t;
     uint16_t x_res;
@@ -479,7 +547,7 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
     constexpr int ZI = 4;                      // A_down slice: Kd/16 <= 32 inputs per lane
     const int lane16 = threadIdx.x & 15, zrow = threadIdx.x >> 4;
     const int zper = Kd / 16;
-    const bool zfast = a.Ad && a.rd <= 16 && zper <= 8 * ZI;
+    const bool zfast = !ZP && a.Ad && a.rd <= 16 && zper <= 8 * ZI;
     constexpr int BQ = 2;   // prefetched B rows up to rank 16; larger ranks read B at the end
     uint4 bq[BQ];
     const bool bfast = a.Bd && (a.rd & 7) == 0 && a.rd <= 8 * BQ;
@@ -492,7 +560,7 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
         for (int i = 0; i < BQ; ++i) bq[i] = brow[bfast ? min(i, a.rd / 8 - 1) : 0];
     }
     uint4 av[ZI];
-    {   // unconditional as well (stand-in: the token's x row)
+    if constexpr (!ZP) {   // unconditional as well (stand-in: the token's x row)
         const uint16_t* arow = zfast ? a.Ad + ((long)ad * a.rd + min(zrow, a.rd - 1)) * Kd + lane16 * zper
                                      : a.x + (long)t * H;
 #pragma unroll
@@ -527,6 +595,13 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
     // phase 3: activations to LDS
     if (one_pass) st.commit(n_staged, Kd, hs_l, hsum);
     else stage_rows<4, 4>(rowp, n_staged, Kd, hs_l, hsum);
+    if constexpr (ZP) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int i = (int)threadIdx.x + NT * j;
+            if (i < nbs * DEC_ZP_RANK) zpl[i] = zpv[j];
+        }
+    }
     __syncthreads();
     // z_down = A_down[ad] . h_s[t], from the staged h_s in the pair order of A's registers
     if (zfast) {
@@ -546,6 +621,12 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
         }
         acc = seg_sum<16>(acc);
         if (lane16 == 0 && zrow < a.rd) zd[zrow] = acc;
+    } else if (ZP) {
+        if (threadIdx.x < DEC_ZP_RANK) {   // the shares in row-block order
+            float z = 0.0f;
+            for (int b = 0; b < nbs; ++b) z += zpl[b * DEC_ZP_RANK + threadIdx.x];
+            zd[threadIdx.x] = z;
+        }
     } else if (a.Ad) {
         lora_rows16(a.Ad + (long)ad * a.rd * Kd, a.rd, hsrow, Kd, zd);
     }
@@ -648,7 +729,7 @@ hipError_t launch_moe_decode(const MoeArgs& a, int stage, hipStream_t s) {
         const int ns = a.T * ((a.SI + rpb - 1) / rpb);
         k_dec_rt_gate_up<<<(unsigned)(nxr + ns + nrb * a.T * a.K), 256, 0, s>>>(a, nxr, ns);
         dim3 grid((unsigned)((a.H + DN_ROWS - 1) / DN_ROWS), (unsigned)a.T);
-        k_dec_down<true><<<grid, 256, 0, s>>>(a);
+        k_dec_down<true, false><<<grid, 256, 0, s>>>(a);
         return hipGetLastError();
     }
     if (stage == QMOE_STAGE_ALL || stage == QMOE_STAGE_ROUTE)
@@ -656,7 +737,8 @@ hipError_t launch_moe_decode(const MoeArgs& a, int stage, hipStream_t s) {
     const int per = topk_per_lane(a.E);
     if (stage == QMOE_STAGE_ALL || stage == QMOE_STAGE_GATE_UP) {
         const int rpb = 4 * (64 / lanes_per_row(a.H)) * GU_RPW;
-        dim3 grid((unsigned)((std::max(a.I, a.SI) + rpb - 1) / rpb), (unsigned)(a.T * a.K + 1));
+        // x: the routed row blocks, and for the shared slot (y = T K) SI / 64 blocks per token
+        dim3 grid((unsigned)std::max((a.I + rpb - 1) / rpb, a.T * (a.SI / 64)), (unsigned)(a.T * a.K + 1));
         switch (per) {
             case 1: k_dec_gate_up<1><<<grid, 256, 0, s>>>(a); break;
             case 2: k_dec_gate_up<2><<<grid, 256, 0, s>>>(a); break;
@@ -667,7 +749,8 @@ hipError_t launch_moe_decode(const MoeArgs& a, int stage, hipStream_t s) {
     }
     if (stage == QMOE_STAGE_ALL || stage == QMOE_STAGE_DOWN) {
         dim3 grid((unsigned)((a.H + DN_ROWS - 1) / DN_ROWS), (unsigned)a.T);
-        k_dec_down<false><<<grid, 256, 0, s>>>(a);
+        if (a.Ad && a.rd <= DEC_ZP_RANK) k_dec_down<false, true><<<grid, 256, 0, s>>>(a);
+        else k_dec_down<false, false><<<grid, 256, 0, s>>>(a);
     }
     return hipGetLastError();
 }

@@ -357,6 +357,26 @@ def test_layer_with_degenerate_and_extreme_groups(q, T):
     print(f"planted groups T={T}: max abs {err:.2e} rel L2 {rel:.2e} alternatives {n_alt}", flush=True)
 
 
+@pytest.mark.parametrize("S,T", [
+    # rank 24: the down launch takes A_d . h_s itself
+    (Shape(hidden=1024, inter=512, shared_inter=512, n_experts=16, top_k=4, rank=24, n_adapters=3), 3),
+    # inter 2048: 32 shares of 64 rows per token, rank 8 (half of the 16 share slots)
+    (Shape(hidden=512, inter=2048, shared_inter=2048, n_experts=8, top_k=2, rank=8, n_adapters=2), 5),
+    # one token, rank 16, three adapters: the gate/up launch's per-row-block shares of z_down
+    (Shape(hidden=2048, inter=512, shared_inter=512, n_experts=64, top_k=4, rank=16, n_adapters=3), 1),
+])
+def test_decode_path_down_lora(q, S, T):
+    """Decode path (fewer than 32 routed pairs): the down LoRA's z_down = A_d h_s either summed
+    from the gate/up launch's per-64-row shares (ranks up to 16) or taken by the down blocks
+    themselves (larger ranks), against the oracle; the adapter changes from token to token."""
+    Lc = build_layer(synth.Workload.TEST, 49, S)
+    x = synth.activations(T, S.hidden, synth.Workload.TEST, 49, T)
+    ad = ((np.arange(T) + 1) % S.n_adapters).astype(np.int32)
+    y, idx, w = run_device(q, Lc, S, x, ad)
+    err, rel, n_alt = check_layer(Lc, x, ad, y, idx, w)
+    print(f"decode down LoRA rank {S.rank} inter {S.inter} T={T}: max abs {err:.2e} rel L2 {rel:.2e}", flush=True)
+
+
 MANY_R = Shape(hidden=1536, inter=512, shared_inter=512, n_experts=16, top_k=6, rank=24, n_adapters=3)
 
 
