@@ -566,6 +566,28 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
 #pragma unroll
         for (int i = 0; i < ZI; ++i) av[i] = *reinterpret_cast<const uint4*>(arow + (zfast ? min(i * 8, zper - 8) : 0));
     }
+    // the LoRA-B term of the block's output row threadIdx.x (< DN_ROWS): B_d row . z_d (LDS)
+    auto bz_dot = [&]() {
+#pragma unroll
+        for (int i = 0; i < BQ; ++i) hold(bq[i]);
+        float zv[8 * BQ];   // read unconditionally (entries past the rank are not used)
+#pragma unroll
+        for (int j = 0; j < 8 * BQ; ++j) zv[j] = zd[j];
+        float d = 0.0f;
+#pragma unroll
+        for (int i = 0; i < BQ; ++i) {
+            if (i < a.rd / 8) {
+                const uint32_t w4[4] = {bq[i].x, bq[i].y, bq[i].z, bq[i].w};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    d = fmaf(half_lo(w4[u]), zv[i * 8 + 2 * u], d);
+                    d = fmaf(half_hi(w4[u]), zv[i * 8 + 2 * u + 1], d);
+                }
+            }
+        }
+        return d;
+    };
+    float lora_pre = 0.0f, sig_pre = 0.0f;   // (ZP) taken before the dot products
     // phase 2: the K + 1 down rows' loads (they need only the routing)
     RowRegs<4, 1> rr[DN_ITEMS];
     int mi[DN_ITEMS], ri[DN_ITEMS];
@@ -627,6 +649,14 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
             for (int b = 0; b < nbs; ++b) z += zpl[b * DEC_ZP_RANK + threadIdx.x];
             zd[threadIdx.x] = z;
         }
+        // the combine's LoRA term and gate now, while the weight rows are in flight (wave 0
+        // wrote zd and reads it back: the LDS accesses of one wave complete in order, so only
+        // the compiler needs a fence)
+        asm volatile("" ::: "memory");
+        if (threadIdx.x < DN_ROWS) {
+            if (bfast) lora_pre = bz_dot();
+            sig_pre = sigmoid(gate_t);
+        }
     } else if (a.Ad) {
         lora_rows16(a.Ad + (long)ad * a.rd * Kd, a.rd, hsrow, Kd, zd);
     }
@@ -665,28 +695,11 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
             for (int k = 0; k < MAX_DEC_K; ++k)
                 if (k < K) acc = fmaf(selw[k], ov[k], acc);
             if (bfast) {
-#pragma unroll
-                for (int i = 0; i < BQ; ++i) hold(bq[i]);
-                float zv[8 * BQ];   // read unconditionally (entries past the rank are not used)
-#pragma unroll
-                for (int j = 0; j < 8 * BQ; ++j) zv[j] = zd[j];
-                float d = 0.0f;
-#pragma unroll
-                for (int i = 0; i < BQ; ++i) {
-                    if (i < a.rd / 8) {
-                        const uint32_t w4[4] = {bq[i].x, bq[i].y, bq[i].z, bq[i].w};
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) {
-                            d = fmaf(half_lo(w4[u]), zv[i * 8 + 2 * u], d);
-                            d = fmaf(half_hi(w4[u]), zv[i * 8 + 2 * u + 1], d);
-                        }
-                    }
-                }
-                os = fmaf(a.lsd, d, os);
+                os = fmaf(a.lsd, ZP ? lora_pre : bz_dot(), os);
             } else if (a.Bd) {
                 os = fmaf(a.lsd, lora_b_dot(a.Bd, ad, H, n, a.rd, zd), os);
             }
-            acc = fmaf(sigmoid(gate_t), os, acc);
+            acc = fmaf(ZP ? sig_pre : sigmoid(gate_t), os, acc);
             uint16_t outv = f2h(acc);
             if (a.add_residual) outv = f2h(h2f(x_res) + h2f(outv));
             a.y[(long)t * H + n] = outv;
