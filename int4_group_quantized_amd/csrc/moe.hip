@@ -49,8 +49,8 @@ Layout layout_of(const qmoe_moe_layer& L, int T) {
     // LoRA z of gate and up: partial sums per 256 inputs (prefill), the first slice for decode
     l.zg = take((size_t)(L.hidden / 256) * T * MAX_RANK * 4);
     l.zu = take((size_t)(L.hidden / 256) * T * MAX_RANK * 4);
-    // z_down (prefill), or the decode path's per-row-block shares of it
-    l.zd = take((size_t)T * std::max(MAX_RANK, DEC_ZP_BLOCKS * DEC_ZP_RANK) * 4);
+    // z_down (prefill), or the decode path's per-row-block shares of it (at most MAX_DEC_T tokens)
+    l.zd = take((size_t)std::max(T * MAX_RANK, std::min(T, MAX_DEC_T) * DEC_ZP_BLOCKS * DEC_ZP_RANK) * 4);
     l.gs = take(ks * T * L.shared_inter * 4);
     l.us = take(ks * T * L.shared_inter * 4);
     l.idx = take(TK * 4);

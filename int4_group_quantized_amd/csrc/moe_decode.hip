@@ -429,7 +429,7 @@ __global__ void __launch_bounds__(256) k_dec_rt_gate_up(MoeArgs a, int nx, int n
 // ------------------------------------------------------------------------------ D3 down
 
 constexpr int DN_ROWS = 8;     // output rows per block
-constexpr int DN_ITEMS = 4;    // (matrix, row) items per lane segment per pass
+constexpr int DN_ITEMS = 4;    // routed (expert, row) items per lane segment per pass (at most)
 constexpr int DN_STAGE = 3;    // 16-byte staging loads per thread: (K + 1) * inter / 8 <= 768
 
 // ROUTED: the routing is the caller's (a.route): the experts come from it and the weights are
@@ -437,7 +437,8 @@ constexpr int DN_STAGE = 3;    // 16-byte staging loads per thread: (K + 1) * in
 // k_dec_rt_gate_up, as from the gate/up launch otherwise).
 // ZP: the down LoRA's z_d is the sum of the gate/up launch's per-64-row shares (top-K path,
 // rank <= DEC_ZP_RANK); otherwise every block takes A_d . h_s itself.
-template <bool ROUTED, bool ZP>
+// NI: routed items per lane segment per pass (2 when K DN_ROWS fits twice the segments).
+template <bool ROUTED, bool ZP, int NI>
 __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
     // staged activations: the token's K routed h rows and h_s (as matrix K), pair layout
     __shared__ __align__(16) f16x2 hs_l[(MAX_DEC_K + 1) * 1024];   // inter <= 2048
@@ -469,18 +470,18 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
     };
 
     // phase 1: every load that needs no other load's value, issued before any wait: the
-    // routing (published by the gate/up stage, or given), the adapter index, the K + 1
-    // activation rows, the combine's own inputs.  Each lane loads the expert of its own
-    // first-pass items (per-lane loads: a per-lane pick from a uniform array would become an
-    // indexed scratch access whose wait drains every load in flight).  Loads complete in
-    // issue order, so the routing and the adapter index go first: the waits for them below
-    // then do not wait for the activations.
-    const int n_items = (K + 1) * DN_ROWS;
+    // routing (published by the gate/up stage, or given), the adapter index, the shared
+    // expert's down rows, the K + 1 activation rows, the combine's own inputs.  Each lane
+    // loads the expert of its own first-pass items (per-lane loads: a per-lane pick from a
+    // uniform array would become an indexed scratch access whose wait drains every load in
+    // flight).  Loads complete in issue order, so the routing and the adapter index go first:
+    // the waits for them below then do not wait for the rest.
+    const int n_items = K * DN_ROWS;      // routed (expert, row) items
     const int slots = 4 * rpw;            // lane segments in the block
     const int slot = wave * rpw + seg;
-    int eit[DN_ITEMS];
+    int eit[NI];
 #pragma unroll
-    for (int i = 0; i < DN_ITEMS; ++i) {
+    for (int i = 0; i < NI; ++i) {
         const int m = min(i * slots + slot, n_items - 1) / DN_ROWS;
         eit[i] = expert_of(min(m, K - 1));
     }
@@ -496,6 +497,15 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
     // is waited for inside the branch)
     const int araw_l = *(a.adapter ? a.adapter + t : reinterpret_cast<const int32_t*>(a.x));
     __builtin_amdgcn_sched_barrier(0);   // the routing and the adapter index are issued first
+    // the shared expert's rows: slot s takes rows s and s + slots (< DN_ROWS); slots past
+    // them read the block's first row again, unused
+    RowRegs<4, 1> rsh[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int r = slot + j * slots;
+        const bool ok = r < DN_ROWS && n0 + r < H;
+        rsh[j].load(a.shd.p, a.shd.s, a.shd.b, Kd, (long)(ok ? n0 + r : n0), lpr, sl, ok);
+    }
     int araw = 0;
     auto clamp_ad = [&](int n) {
         const int v = a.adapter ? araw : 0;
@@ -589,11 +599,11 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
     };
     float lora_pre = 0.0f, sig_pre = 0.0f;   // (ZP) taken before the dot products
     // phase 2: the K + 1 down rows' loads (they need only the routing)
-    RowRegs<4, 1> rr[DN_ITEMS];
-    int mi[DN_ITEMS], ri[DN_ITEMS];
+    RowRegs<4, 1> rr[NI];
+    int mi[NI], ri[NI];
     auto load_items = [&](int base) {
 #pragma unroll
-        for (int i = 0; i < DN_ITEMS; ++i) {
+        for (int i = 0; i < NI; ++i) {
             const int item = base + i * slots + slot;
             const int ic = min(item, n_items - 1);
             const int m = ic / DN_ROWS, r = ic % DN_ROWS;
@@ -602,13 +612,12 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
             const int e = base == 0 ? eit[i] : expert_of(min(m, K - 1));
             mi[i] = ok ? m : -1;
             ri[i] = r;
-            const bool routed = m < K;
-            rr[i].load(routed ? a.ed.p : a.shd.p, routed ? a.ed.s : a.shd.s,
-                       routed ? a.ed.b : a.shd.b, Kd, routed ? (long)e * H + nn : (long)nn,
-                       lpr, sl, ok);
+            rr[i].load(a.ed.p, a.ed.s, a.ed.b, Kd, (long)e * H + nn, lpr, sl, ok);
         }
     };
     load_items(0);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) rsh[j].hold();   // their first use after the routed rows' issue
     float my_b = 0.0f;   // the bias, added at the end (a branch around its load would wait for it)
     if constexpr (ROUTED) {
         my_l = a.logits[(long)t * a.Ep + my_e];
@@ -660,10 +669,22 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
     } else if (a.Ad) {
         lora_rows16(a.Ad + (long)ad * a.rd * Kd, a.rd, hsrow, Kd, zd);
     }
-    for (int base = 0; base < n_items; base += slots * DN_ITEMS) {
+    // the shared expert's outputs first (its rows were issued before the routing arrived)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int r = slot + j * slots;
+        if (r < DN_ROWS) {   // uniform over each wave (slots of a wave are consecutive)
+            float acc[MT];
+            acc[0] = 0.0f;
+            rsh[j].dot(Kd, lpr, sl, hs_l + K * (Kd / 2), hsum + K * (Kd / 32), 1, acc);
+            const float v = segment_sum(acc[0], lpr);
+            if (sl == 0) o_l[K * DN_ROWS + r] = v;
+        }
+    }
+    for (int base = 0; base < n_items; base += slots * NI) {
         if (base > 0) load_items(base);
 #pragma unroll
-        for (int i = 0; i < DN_ITEMS; ++i) {
+        for (int i = 0; i < NI; ++i) {
             float acc[MT];
             acc[0] = 0.0f;
             const int m = mi[i] < 0 ? 0 : mi[i];
@@ -716,6 +737,13 @@ __global__ void __launch_bounds__(256) k_dec_down(MoeArgs a) {
 
 static int chunks_per_lane(int K) { return (K / 32) / lanes_per_row(K); }
 
+// routed items per lane segment per pass of the down kernel: 2 when the K experts' rows of a
+// block fill at most two passes' worth of segments, else DN_ITEMS
+static int dn_items(const MoeArgs& a) {
+    const int slots = 4 * (64 / lanes_per_row(a.I));
+    return a.K * DN_ROWS <= 2 * slots ? 2 : DN_ITEMS;
+}
+
 // The register and LDS budgets of the decode kernels: hidden rows of at most two 32-input
 // chunks per lane (hidden <= 4096), down rows of one chunk per lane (inter <= 2048, a power
 // of two), equal routed and shared intermediate sizes.
@@ -742,7 +770,8 @@ hipError_t launch_moe_decode(const MoeArgs& a, int stage, hipStream_t s) {
         const int ns = a.T * ((a.SI + rpb - 1) / rpb);
         k_dec_rt_gate_up<<<(unsigned)(nxr + ns + nrb * a.T * a.K), 256, 0, s>>>(a, nxr, ns);
         dim3 grid((unsigned)((a.H + DN_ROWS - 1) / DN_ROWS), (unsigned)a.T);
-        k_dec_down<true, false><<<grid, 256, 0, s>>>(a);
+        if (dn_items(a) == 2) k_dec_down<true, false, 2><<<grid, 256, 0, s>>>(a);
+        else k_dec_down<true, false, DN_ITEMS><<<grid, 256, 0, s>>>(a);
         return hipGetLastError();
     }
     if (stage == QMOE_STAGE_ALL || stage == QMOE_STAGE_ROUTE)
@@ -762,8 +791,14 @@ hipError_t launch_moe_decode(const MoeArgs& a, int stage, hipStream_t s) {
     }
     if (stage == QMOE_STAGE_ALL || stage == QMOE_STAGE_DOWN) {
         dim3 grid((unsigned)((a.H + DN_ROWS - 1) / DN_ROWS), (unsigned)a.T);
-        if (a.Ad && a.rd <= DEC_ZP_RANK) k_dec_down<false, true><<<grid, 256, 0, s>>>(a);
-        else k_dec_down<false, false><<<grid, 256, 0, s>>>(a);
+        const bool zp = a.Ad && a.rd <= DEC_ZP_RANK;
+        if (dn_items(a) == 2) {
+            if (zp) k_dec_down<false, true, 2><<<grid, 256, 0, s>>>(a);
+            else k_dec_down<false, false, 2><<<grid, 256, 0, s>>>(a);
+        } else {
+            if (zp) k_dec_down<false, true, DN_ITEMS><<<grid, 256, 0, s>>>(a);
+            else k_dec_down<false, false, DN_ITEMS><<<grid, 256, 0, s>>>(a);
+        }
     }
     return hipGetLastError();
 }
