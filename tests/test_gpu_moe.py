@@ -364,6 +364,8 @@ def test_layer_with_degenerate_and_extreme_groups(q, T):
     (Shape(hidden=512, inter=2048, shared_inter=2048, n_experts=8, top_k=2, rank=8, n_adapters=2), 5),
     # one token, rank 16, three adapters: the gate/up launch's per-row-block shares of z_down
     (Shape(hidden=2048, inter=512, shared_inter=512, n_experts=64, top_k=4, rank=16, n_adapters=3), 1),
+    # inter 2048, top-4: the routed rows take two passes, activations staged through LDS
+    (Shape(hidden=512, inter=2048, shared_inter=2048, n_experts=8, top_k=4, rank=16, n_adapters=2), 3),
 ])
 def test_decode_path_down_lora(q, S, T):
     """Decode path (fewer than 32 routed pairs): the down LoRA's z_down = A_d h_s either summed
