@@ -1050,6 +1050,7 @@ __device__ __forceinline__ float bdot_tail(const uint16_t* __restrict__ brow, co
 
 constexpr int TOK_HW = 3;   // waves of k_pf_token on the shared expert's h
 constexpr int TOK_NPC = 4;  // h outputs per thread whose loads are issued together (few tokens)
+constexpr int TOK_WIDE_T = 64;   // up to this many tokens: blocks of 8 waves (7 on h_s, 2 outputs each)
 
 // Per-token finish of the x side, one block of 4 waves per token.  Wave 0 sums the token's
 // router-logit partials in registers and runs top-K.  Waves 1-3 sum the shared-gate logit and
@@ -1059,12 +1060,13 @@ constexpr int TOK_NPC = 4;  // h outputs per thread whose loads are issued toget
 // the one barrier:
 // h_s and the selection are written out and z_d = A_down h_s is taken, one wave per four rank
 // rows.  Split-K partials are added in split order, LoRA chunks in chunk order.
-template <int KP, int PER, int NPC>
+template <int KP, int PER, int NPC, int HW>
 __device__ __forceinline__ void pf_token_body(const MoeArgs& a, int ksplit) {
+    constexpr int NTB = 64 * (HW + 1);   // threads per block
     extern __shared__ __align__(16) uint16_t hl[];        // h_s of the token, fp16 [SI]
     __shared__ int sel[MAX_K];
     __shared__ float sw[MAX_K];
-    __shared__ float zw[TOK_HW][2][MAX_RANK];
+    __shared__ float zw[HW][2][MAX_RANK];
     const int t = blockIdx.x, T = a.T, SI = a.SI;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 
@@ -1104,12 +1106,12 @@ __device__ __forceinline__ void pf_token_body(const MoeArgs& a, int ksplit) {
         const int gs = fg ? a.rg : 0, us = fu ? a.ru : 0;
         const int g8 = max(min(a.rg, 16) - 8, 0), u8 = max(min(a.ru, 16) - 8, 0);
         bool first = true;
-        for (int n0 = u; n0 < SI; n0 += NPC * TOK_HW * 64) {
+        for (int n0 = u; n0 < SI; n0 += NPC * HW * 64) {
             Parts<KP> pg[NPC], pu[NPC];
             uint4 bg[NPC][2], bu[NPC][2];
 #pragma unroll
             for (int c = 0; c < NPC; ++c) {
-                const int n = min(n0 + c * TOK_HW * 64, SI - 1);
+                const int n = min(n0 + c * HW * 64, SI - 1);
                 pg[c].load(a.gs + (long)t * SI + n, pgu, ksplit);
                 pu[c].load(a.us + (long)t * SI + n, pgu, ksplit);
 #pragma unroll
@@ -1128,7 +1130,7 @@ __device__ __forceinline__ void pf_token_body(const MoeArgs& a, int ksplit) {
             }
 #pragma unroll
             for (int c = 0; c < NPC; ++c) {
-                const int n = n0 + c * TOK_HW * 64;
+                const int n = n0 + c * HW * 64;
                 if (n < SI) {
                     float gv = pg[c].sum(ksplit), uv = pu[c].sum(ksplit);
                     if (a.Bg) {
@@ -1149,7 +1151,7 @@ __device__ __forceinline__ void pf_token_body(const MoeArgs& a, int ksplit) {
     }
     __syncthreads();
 
-    for (int n = threadIdx.x * 8; n < SI; n += 256 * 8)
+    for (int n = threadIdx.x * 8; n < SI; n += NTB * 8)
         *reinterpret_cast<uint4*>(a.hs + (long)t * SI + n) = *reinterpret_cast<const uint4*>(hl + n);
     if (threadIdx.x < a.K) {
         const long i = (long)t * a.K + threadIdx.x;
@@ -1176,7 +1178,7 @@ __device__ __forceinline__ void pf_token_body(const MoeArgs& a, int ksplit) {
             }
         }
     };
-    for (int r0 = 4 * wave; r0 < rd; r0 += 16) {
+    for (int r0 = 4 * wave; r0 < rd; r0 += 4 * (HW + 1)) {
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
         for (int k0 = 0; k0 < SI; k0 += 1024) {
             if (PRE && r0 == 4 * wave && k0 == 0) {
@@ -1204,18 +1206,31 @@ __device__ __forceinline__ void pf_token_body(const MoeArgs& a, int ksplit) {
 // logits per lane of the top-K (4 up to 256 experts, else 16), fixed per kernel so that one
 // kernel holds one selection.
 template <int KP, int PER>
-__global__ void __launch_bounds__(256) k_pf_token(MoeArgs a, int ksplit) { pf_token_body<KP, PER, TOK_NPC>(a, ksplit); }
+__global__ void __launch_bounds__(256) k_pf_token(MoeArgs a, int ksplit) { pf_token_body<KP, PER, TOK_NPC, TOK_HW>(a, ksplit); }
+
+// Very few tokens (at most TOK_WIDE_T, so that only that many blocks run): eight waves per
+// block, seven of them on h_s with two outputs each, so each thread's chain of loads is
+// shorter.
+template <int KP, int PER>
+__global__ void __launch_bounds__(512) k_pf_token_wide(MoeArgs a, int ksplit) { pf_token_body<KP, PER, 2, 7>(a, ksplit); }
 
 // Many tokens (several rounds of blocks): one h output per thread in flight, so that four waves
 // fit a SIMD and twice the tokens are in flight.
 template <int KP, int PER>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
-k_pf_token_many(MoeArgs a, int ksplit) { pf_token_body<KP, PER, 1>(a, ksplit); }
+k_pf_token_many(MoeArgs a, int ksplit) { pf_token_body<KP, PER, 1, TOK_HW>(a, ksplit); }
 
 // The per-token kernel for T tokens: KP split-K partials, PER logits per lane.
 template <int PER>
 void launch_token(const MoeArgs& a, int ksplit, int kp, size_t tsm, hipStream_t s) {
-    if (a.T < PF_MANY_T) {
+    // (the eight-wave form for up to 256 experts: with 16 logits per lane it would spill)
+    if (PER == 4 && a.T <= TOK_WIDE_T) {
+        if constexpr (PER == 4) {
+            if (kp <= 2) k_pf_token_wide<2, PER><<<a.T, 512, tsm, s>>>(a, ksplit);
+            else if (kp <= 4) k_pf_token_wide<4, PER><<<a.T, 512, tsm, s>>>(a, ksplit);
+            else k_pf_token_wide<8, PER><<<a.T, 512, tsm, s>>>(a, ksplit);
+        }
+    } else if (a.T < PF_MANY_T) {
         if (kp <= 2) k_pf_token<2, PER><<<a.T, 256, tsm, s>>>(a, ksplit);
         else if (kp <= 4) k_pf_token<4, PER><<<a.T, 256, tsm, s>>>(a, ksplit);
         else k_pf_token<8, PER><<<a.T, 256, tsm, s>>>(a, ksplit);
