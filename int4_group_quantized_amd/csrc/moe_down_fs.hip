@@ -30,9 +30,8 @@
 //   3. the first jobs' rows are issued, then the shared expert's outputs are computed (its rows
 //      arrived during step 2); 16-lane segments (lane l owns inputs 32 l .. 32 l + 31 of a
 //      512-input row) take tokens sg, sg + 16, ...;
-//   4. the segments take jobs sg, sg + 16, ..., each with a ring of three job slots: the rows of
-//      job m + 2 and the first pair's activations of job m + 1 are issued before job m is
-//      computed, so two jobs' weights are in flight per segment;
+//   4. the segments take jobs sg, sg + 16, ..., each with two job slots: the rows and the first
+//      pair's activations of job m + 1 are issued before job m is computed;
 //   5. the combine, from registers loaded in step 1.
 #include "gemv_core.hpp"
 #include "launch.hpp"
@@ -266,18 +265,18 @@ __global__ void __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) k
         }
     };
 
-    // ---- phase 3: the routed jobs' first rows in flight, then the shared expert's outputs
-    // (its rows arrived during the grouping).  Each segment keeps a ring of three job slots;
-    // loads complete in issue order, so a job's activations are issued before the rows of the
-    // job after it: waiting for job m leaves the rows of jobs m + 1 and m + 2 in flight.
-    FsSlot<FR> S0, S1, S2;
+    // ---- phase 3: the first routed job's rows and activations in flight, then the shared
+    // expert's outputs (its rows arrived during the grouping).  Each segment keeps two job
+    // slots: while job m is computed, job m + 1's loads are in flight.  A third slot (two jobs
+    // in flight) ran the 16-token stack 2 % slower: with more requests outstanding from every
+    // block, the rows arrived later.
+    FsSlot<FR> S0, S1;
     load_rows(S0, sg);
     {
         const GU4* hp = h_src(sg, 0);
 #pragma unroll
         for (int q = 0; q < 4; ++q) S0.h[q] = ldg(hp + q);
     }
-    load_rows(S1, sg + NSEG);
     __builtin_amdgcn_sched_barrier(0);
     {
         float v[FR];
@@ -293,16 +292,16 @@ __global__ void __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) k
         }
     }
 
-    // ---- phase 4: the routed jobs.  One ring step: issue the first activations of job m + 1
-    // (into `nx1`) and the rows of job m + 2 (into `nx2`), then compute job m from `cur`.
-    auto step = [&](FsSlot<FR>& cur, FsSlot<FR>& nx1, FsSlot<FR>& nx2, int m) {
+    // ---- phase 4: the routed jobs.  One step: issue the first activations and the rows of
+    // job m + 1 (into `nxt`), then compute job m from `cur`.
+    auto step = [&](FsSlot<FR>& cur, FsSlot<FR>& nxt, int m) {
         const int j = sg + NSEG * m;
         {
             const GU4* hp = h_src(j + NSEG, 0);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) nx1.h[q] = ldg(hp + q);
+            for (int q = 0; q < 4; ++q) nxt.h[q] = ldg(hp + q);
         }
-        load_rows(nx2, sg + NSEG * (m + 2));
+        load_rows(nxt, j + NSEG);
         __builtin_amdgcn_sched_barrier(0);   // the loads above are issued before any wait below
         const int cnt = job_cnt(j);
         float v[FR];
@@ -318,13 +317,11 @@ __global__ void __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) k
         }
     };
     int m = 0;
-    for (; m + 3 <= niter; m += 3) {
-        step(S0, S1, S2, m);
-        step(S1, S2, S0, m + 1);
-        step(S2, S0, S1, m + 2);
+    for (; m + 2 <= niter; m += 2) {
+        step(S0, S1, m);
+        step(S1, S0, m + 1);
     }
-    if (m < niter) step(S0, S1, S2, m);   // (niter is the same in every lane of the block)
-    if (m + 1 < niter) step(S1, S2, S0, m + 1);
+    if (m < niter) step(S0, S1, m);   // (niter is the same in every lane of the block)
     __syncthreads();
 
     // ---- phase 5: combine, thread (t, r) for feature n0 + r of token t; the first pass from
