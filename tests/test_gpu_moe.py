@@ -379,6 +379,22 @@ def test_decode_path_down_lora(q, S, T):
     print(f"decode down LoRA rank {S.rank} inter {S.inter} T={T}: max abs {err:.2e} rel L2 {rel:.2e}", flush=True)
 
 
+WIDE_H = Shape(hidden=4096, inter=512, shared_inter=512, n_experts=16, top_k=4, rank=16, n_adapters=2)
+
+
+@pytest.mark.parametrize("T", [3, 40, 300])
+def test_largest_hidden(q, T):
+    """Hidden 4096, the largest the layer accepts: two 32-input chunks per lane in the decode
+    GEMVs (3 tokens), eight split-K partials per value in the per-token kernels (40 tokens: the
+    eight-wave form and the feature-sliced down; 300 tokens: the four-wave form, sorted items)."""
+    Lc = build_layer(synth.Workload.TEST, 50, WIDE_H)
+    x = synth.activations(T, WIDE_H.hidden, synth.Workload.TEST, 50, T)
+    ad = (np.arange(T) % 2).astype(np.int32)
+    y, idx, w = run_device(q, Lc, WIDE_H, x, ad)
+    err, rel, n_alt = check_layer(Lc, x, ad, y, idx, w)
+    print(f"hidden 4096 T={T}: max abs {err:.2e} rel L2 {rel:.2e} alternatives {n_alt}", flush=True)
+
+
 MANY_R = Shape(hidden=1536, inter=512, shared_inter=512, n_experts=16, top_k=6, rank=24, n_adapters=3)
 
 
