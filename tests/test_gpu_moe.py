@@ -395,6 +395,24 @@ def test_largest_hidden(q, T):
     print(f"hidden 4096 T={T}: max abs {err:.2e} rel L2 {rel:.2e} alternatives {n_alt}", flush=True)
 
 
+@pytest.mark.parametrize("E,K,T", [
+    (260, 4, 5),      # decode path, 8 logits per lane, expert count not a multiple of 64
+    (1024, 8, 3),     # decode path at the most experts the layer accepts (16 logits per lane)
+    (260, 16, 4),     # token-sorted path (past 256 experts: the sort launch), top-16
+    (1024, 32, 9),    # the largest expert count and top-K the layer accepts
+])
+def test_many_experts_and_large_top_k(q, E, K, T):
+    """Expert counts past 256 and top-K past 8 on both paths, against the oracle (indices
+    equal up to near-ties, weights and outputs within the tolerance)."""
+    S = Shape(hidden=512, inter=512, shared_inter=512, n_experts=E, top_k=K, rank=8, n_adapters=2)
+    Lc = build_layer(synth.Workload.TEST, 51, S)
+    x = synth.activations(T, S.hidden, synth.Workload.TEST, 51, T)
+    ad = (np.arange(T) % 2).astype(np.int32)
+    y, idx, w = run_device(q, Lc, S, x, ad)
+    err, rel, n_alt = check_layer(Lc, x, ad, y, idx, w)
+    print(f"E={E} K={K} T={T}: max abs {err:.2e} rel L2 {rel:.2e} alternatives {n_alt}", flush=True)
+
+
 MANY_R = Shape(hidden=1536, inter=512, shared_inter=512, n_experts=16, top_k=6, rank=24, n_adapters=3)
 
 
