@@ -413,6 +413,22 @@ def test_many_experts_and_large_top_k(q, E, K, T):
     print(f"E={E} K={K} T={T}: max abs {err:.2e} rel L2 {rel:.2e} alternatives {n_alt}", flush=True)
 
 
+DEEPEST = Shape(hidden=512, inter=4096, shared_inter=2048, n_experts=8, top_k=2, rank=16, n_adapters=2)
+
+
+@pytest.mark.parametrize("T", [5, 70])
+def test_largest_inter(q, T):
+    """Routed inner size 4096 (the largest the layer accepts) with a shared expert of 2048: the
+    token-sorted path at any token count (the decode path needs equal inner sizes of at most
+    2048), down GEMMs over 4096 inputs, the per-token kernel's h_s loop over 2048 outputs."""
+    Lc = build_layer(synth.Workload.TEST, 52, DEEPEST)
+    x = synth.activations(T, DEEPEST.hidden, synth.Workload.TEST, 52, T)
+    ad = (np.arange(T) % 2).astype(np.int32)
+    y, idx, w = run_device(q, Lc, DEEPEST, x, ad)
+    err, rel, n_alt = check_layer(Lc, x, ad, y, idx, w)
+    print(f"inter 4096 T={T}: max abs {err:.2e} rel L2 {rel:.2e} alternatives {n_alt}", flush=True)
+
+
 MANY_R = Shape(hidden=1536, inter=512, shared_inter=512, n_experts=16, top_k=6, rank=24, n_adapters=3)
 
 
