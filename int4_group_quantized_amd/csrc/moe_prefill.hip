@@ -935,19 +935,21 @@ __host__ __device__ inline int lora_z_jobs(int T, int H, int rank, int nad) {
 // x side of the layer in one launch: the router rows plus the shared-gate row (8-bit), the
 // shared expert's gate and up (int4), all as split-K partial sums, then the LoRA z's of the
 // shared gate and up as partial sums over 256-input chunks (one wave per lora_z_chunk job).
-template <int NS>
+// NT: token tiles of 16 per block (4; 1 for at most 16 tokens, which would otherwise pad
+// three of the four tiles).
+template <int NS, int NT>
 __global__ void __launch_bounds__(256) k_pf_xside(XsideArgs xa, MoeArgs a) {
     __shared__ __align__(16) PfSmem<4, 2, NS> sm;
     const int b = blockIdx.x;
     int rb, item;
     if (b < xa.nb_router) {
         pf_block(b, xa.router.nrb, rb, item);
-        pf_gemm_block<1, 8, 4, F_EXTRA, NS, 2>(xa.router, rb, item, sm);
+        pf_gemm_block<1, 8, NT, F_EXTRA, NS, 2>(xa.router, rb, item, sm);
         return;
     }
     if (b < xa.nb_router + xa.nb_shared) {
         pf_block(b - xa.nb_router, xa.shared.nrb, rb, item);
-        pf_gemm_block<2, 4, 4, 0, NS, 2>(xa.shared, rb, item, sm);
+        pf_gemm_block<2, 4, NT, 0, NS, 2>(xa.shared, rb, item, sm);
         return;
     }
     const int jb = (b - xa.nb_router - xa.nb_shared) * 4 + (threadIdx.x >> 6);
@@ -1821,12 +1823,15 @@ hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s) {
     if (all || stage == QMOE_STAGE_ROUTE) {
         // x side: split-K blocks of PF_XS_K inputs write partial sums, k_pf_token adds them
         XsideArgs xa{};
-        xa.router = gemm_args(a.router, nullptr, a.E, a.H, a.x, a.E + 1, tgroups * ksplit);
+        // token groups of 64 (four tiles), or one tile of 16 for at most 16 tokens
+        const bool x1 = a.T <= 16;
+        const int xgroups = x1 ? 1 : tgroups;
+        xa.router = gemm_args(a.router, nullptr, a.E, a.H, a.x, a.E + 1, xgroups * ksplit);
         xa.router.T = a.T;
         xa.router.ksplit = ksplit;
         xa.router.out0 = a.logits; xa.router.ostride = a.Ep; xa.router.pstride = (long)a.T * a.Ep;
         xa.router.xp = a.sgate.p; xa.router.xs = a.sgate.s; xa.router.xb = a.sgate.b; xa.router.xout = a.gate;
-        xa.shared = gemm_args(a.shg, &a.shu, a.SI, a.H, a.x, a.SI, tgroups * ksplit);
+        xa.shared = gemm_args(a.shg, &a.shu, a.SI, a.H, a.x, a.SI, xgroups * ksplit);
         xa.shared.T = a.T;
         xa.shared.ksplit = ksplit;
         xa.shared.out0 = a.gs; xa.shared.out1 = a.us; xa.shared.pstride = (long)a.T * a.SI;
@@ -1835,9 +1840,12 @@ hipError_t launch_moe_prefill(const MoeArgs& a, int stage, hipStream_t s) {
         xa.zjobs = (a.Ag ? lora_z_jobs(a.T, a.H, a.rg, a.nag) : 0) + (a.Au ? lora_z_jobs(a.T, a.H, a.ru, a.nau) : 0);
         const unsigned xgrid = (unsigned)(xa.nb_router + xa.nb_shared + (xa.zjobs + 3) / 4);
         switch (xs_inputs(a.H, a.T) / PF_KS) {
-            case 4: k_pf_xside<4><<<xgrid, 256, 0, s>>>(xa, a); break;
-            case 8: k_pf_xside<8><<<xgrid, 256, 0, s>>>(xa, a); break;
-            default: k_pf_xside<16><<<xgrid, 256, 0, s>>>(xa, a); break;
+            case 4:
+                if (x1) k_pf_xside<4, 1><<<xgrid, 256, 0, s>>>(xa, a);
+                else k_pf_xside<4, 4><<<xgrid, 256, 0, s>>>(xa, a);
+                break;
+            case 8: k_pf_xside<8, 4><<<xgrid, 256, 0, s>>>(xa, a); break;
+            default: k_pf_xside<16, 4><<<xgrid, 256, 0, s>>>(xa, a); break;
         }
         const size_t tsm = (size_t)a.SI * 2;   // hidden <= 4096: at most 8 splits
         // KP covers the split-K partials (<= hidden / 512) and half the LoRA z chunks
