@@ -1052,7 +1052,7 @@ __device__ __forceinline__ float bdot_tail(const uint16_t* __restrict__ brow, co
 
 constexpr int TOK_HW = 3;   // waves of k_pf_token on the shared expert's h
 constexpr int TOK_NPC = 4;  // h outputs per thread whose loads are issued together (few tokens)
-constexpr int TOK_WIDE_T = 64;   // up to this many tokens: blocks of 8 waves (7 on h_s, 2 outputs each)
+constexpr int TOK_WIDE_T = 256;  // up to this many tokens: blocks of 8 waves (7 on h_s, 2 outputs each)
 
 // Per-token finish of the x side, one block of 4 waves per token.  Wave 0 sums the token's
 // router-logit partials in registers and runs top-K.  Waves 1-3 sum the shared-gate logit and
@@ -1210,9 +1210,9 @@ __device__ __forceinline__ void pf_token_body(const MoeArgs& a, int ksplit) {
 template <int KP, int PER>
 __global__ void __launch_bounds__(256) k_pf_token(MoeArgs a, int ksplit) { pf_token_body<KP, PER, TOK_NPC, TOK_HW>(a, ksplit); }
 
-// Very few tokens (at most TOK_WIDE_T, so that only that many blocks run): eight waves per
-// block, seven of them on h_s with two outputs each, so each thread's chain of loads is
-// shorter.
+// Few tokens (at most TOK_WIDE_T: all blocks resident at once): eight waves per block, seven
+// of them on h_s with two outputs each, so each thread's chain of loads is shorter (measured
+// faster at 16 and 256 tokens, slower at 512, where the blocks no longer all fit at once).
 template <int KP, int PER>
 __global__ void __launch_bounds__(512) k_pf_token_wide(MoeArgs a, int ksplit) { pf_token_body<KP, PER, 2, 7>(a, ksplit); }
 
